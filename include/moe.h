@@ -1,0 +1,213 @@
+/*
+ * moe.h: C ABI of a single Mixture-of-Experts layer on one MI355X (gfx950) GPU.
+ *
+ * The layer computes y = sum_k g_k E_k(x): an fp32 router picks k experts per
+ * token and renormalised gates g; token copies are dispatched into an
+ * expert-contiguous ring buffer; every expert applies a SwiGLU FFN
+ * E(x) = W_down (silu(W_gate x) * (W_up x)); the results are combined with the
+ * gates in a fixed order.  Sources of each step:
+ *
+ *   routing of tokens to experts ........ dzen.guru page, section "Что именно тормозило
+ *                                          обучение MoE-моделей?"
+ *   fixed ring buffer, no dropped tokens,
+ *   reverse traversal in the backward ... dzen.guru page, ring-buffer paragraph of
+ *                                          "Три решения, которые дали результат"
+ *   one deterministic result; BF16 and
+ *   MXFP8 ................................ dzen.guru page, megakernel paragraph of the same
+ *                                          section; @cursor_ai tweet on the khabar-ai page
+ *   no CPU in the loop .................. @rohanpaul_ai tweet on the khabar-ai page
+ *   output-parallel two-kernel decode ... toolnavs.com warp-decode page, sections "Cursor a
+ *                                          réécrit le décodage de MoE" and "1.84x plus de
+ *                                          vitesse…"
+ * The pages give no formulas; the router (softmax over all experts, top-k,
+ * renormalise), the SwiGLU expert and the MXFP8 encoding (E4M3 elements, one
+ * E8M0 scale per 32 elements along the reduction dimension, RNE) are those of
+ * the layer's workload definition.
+ *
+ * Conventions for every call
+ *   - Every tensor pointer is a DEVICE pointer; `shape` is a HOST pointer.
+ *   - Row-major, nn.Linear layout: W_gate, W_up [E, f, d]; W_down [E, d, f];
+ *     W_r [E, d] fp32; b_r [E] fp32 (may be NULL).
+ *   - "act" tensors are fp32 when shape->dtype == MOE_F32, otherwise bf16
+ *     (raw 16-bit patterns).  With MOE_MXFP8 the router and the tokens x stay
+ *     bf16; ring_x, H and the expert weights are E4M3 codes (uint8) with one
+ *     E8M0 scale byte per 32 elements along the reduction dimension.
+ *   - The caller owns every buffer.  The library allocates nothing, keeps no
+ *     pointer after return, and only enqueues work on `stream`: there is no
+ *     host synchronisation and no device-to-host copy inside any call.
+ *   - Outputs are fully overwritten; read-only inputs are never written.
+ *   - Results are bitwise reproducible run to run (fixed reduction orders,
+ *     no floating-point atomics).
+ *   - Errors: arguments are validated on the host from `shape` before any
+ *     launch.  A launch failure returns MOE_ERR_HIP.  No exception crosses
+ *     the ABI.  Calls that share a workspace must not overlap in time.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,       /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,      /* non-positive size, k > E, MX length not a multiple of 32, ... */
+  MOE_ERR_CAPACITY = 3,   /* ring capacity below tokens * top_k: tokens would be dropped */
+  MOE_ERR_WORKSPACE = 4,  /* workspace smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = 5,        /* a HIP launch or runtime call failed */
+  MOE_ERR_DTYPE = 6       /* unknown dtype, or a dtype the call does not support */
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 };
+
+enum moe_op {
+  MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_EXPERT_FFN = 2,
+  MOE_OP_COMBINE = 3, MOE_OP_DECODE = 4, MOE_OP_BACKWARD = 5
+};
+
+/* Shape of one layer call (host struct). */
+typedef struct moe_shape {
+  int64_t tokens;      /* T: tokens of this call (decode: batch B) */
+  int64_t capacity;    /* C: ring rows; must be >= tokens * top_k */
+  int32_t hidden;      /* d */
+  int32_t experts;     /* E */
+  int32_t top_k;       /* k, 1 <= k <= E */
+  int32_t ffn;         /* f: expert intermediate size */
+  int32_t shared_ffn;  /* fs: always-on shared expert width (decode only), 0 = none */
+  int32_t dtype;       /* enum moe_dtype */
+} moe_shape;
+
+/*
+ * moe_route: the router (dzen.guru, "Что именно тормозило…": each layer routes
+ * tokens to experts).  In fp32, with x widened exactly from bf16:
+ *   l[t,e] = sum_i x[t,i] W_r[e,i] (+ b_r[e]);  p = softmax_e(l);
+ *   S_t = the k largest l (ties to the lower id);  g[t,j] = p[S_tj] / sum_S p.
+ * In:  x [T,d] act (bf16 for MOE_MXFP8), w_router [E,d] f32, b_router [E] f32 or NULL.
+ * Out: topk_idx [T,k] int32, ascending expert id per token; topk_gate [T,k] f32;
+ *      expert_count [E] int32 = copies routed to each expert.
+ * workspace: moe_workspace_bytes(shape, MOE_OP_ROUTE) bytes (router logits).
+ */
+int moe_route(const moe_shape* shape, const void* x, const float* w_router,
+              const float* b_router, int32_t* topk_idx, float* topk_gate,
+              int32_t* expert_count, void* workspace, size_t workspace_bytes,
+              hipStream_t stream);
+
+/*
+ * moe_dispatch: deterministic counting sort of the T*k token copies into the
+ * fixed ring buffer (dzen.guru, ring-buffer paragraph: fixed size, nothing
+ * dropped, no size computed on the CPU).  Copy c = t*k + j goes to
+ *   slot = (ring_head + rank(c)) mod C,
+ * where rank orders copies by (expert, token): segments are expert-contiguous
+ * and hold their tokens in ascending order.
+ * In:  x [T,d] act (bf16 for MOE_MXFP8), topk_idx [T,k], ring_head in [0, C).
+ * Out: ring_x [C,d] act (MOE_MXFP8: E4M3 codes, each row MX-quantised along d)
+ *        — only the T*k used slots are written;
+ *      ring_x_scale [C, d/32] E8M0 bytes (MOE_MXFP8 only, else NULL);
+ *      expert_offset [E+1] int32, segment starts relative to the head (offset[E] = T*k);
+ *      copy_slot [T,k] int32 absolute slot of each copy;
+ *      slot_copy [C] int32 copy id t*k+j held by each used slot (other slots untouched).
+ * workspace: moe_workspace_bytes(shape, MOE_OP_DISPATCH) bytes.
+ */
+int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
+                 int64_t ring_head, void* ring_x, uint8_t* ring_x_scale,
+                 int32_t* expert_offset, int32_t* copy_slot, int32_t* slot_copy,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_ffn: every expert's SwiGLU FFN over its own ring segment, as two
+ * grouped GEMMs (the expert-centric scheme the warp-decode page contrasts with;
+ * MXFP8 expert kernels per the @rohanpaul_ai tweet on the khabar-ai page):
+ *   [A|U] = X_e [W_gate[e]; W_up[e]]^T,  H = silu(A) * U,  Y_e = H W_down[e]^T.
+ * H is bf16 (fp32 for MOE_F32; MX along f for MOE_MXFP8) and lives in the workspace.
+ * In:  ring_x (+ ring_x_scale), expert_offset, ring_head; w_gate, w_up [E,f,d] and
+ *      w_down [E,d,f] act, or E4M3 codes with w_gate_scale/w_up_scale [E,f,d/32]
+ *      and w_down_scale [E,d,f/32] for MOE_MXFP8 (NULL otherwise).
+ * Out: ring_y [C,d] (bf16; fp32 for MOE_F32) at the segment slots;
+ *      saved_au [C,2f] bf16 (A then U per slot) when not NULL — the backward's input
+ *      (MOE_BF16 only; must be NULL otherwise).
+ * workspace: moe_workspace_bytes(shape, MOE_OP_EXPERT_FFN) bytes.
+ */
+int moe_expert_ffn(const moe_shape* shape, const void* ring_x, const uint8_t* ring_x_scale,
+                   const int32_t* expert_offset, int64_t ring_head,
+                   const void* w_gate, const void* w_up, const void* w_down,
+                   const uint8_t* w_gate_scale, const uint8_t* w_up_scale,
+                   const uint8_t* w_down_scale, void* ring_y, void* saved_au,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_combine: y[t] = sum_j g[t,j] ring_y[copy_slot[t,j]], j in ascending expert
+ * order, fp32 accumulation, one final rounding (deterministic gather; dzen.guru,
+ * megakernel paragraph).
+ * In: ring_y [C,d], copy_slot [T,k], topk_gate [T,k].  Out: y [T,d] (bf16; f32 for MOE_F32).
+ */
+int moe_combine(const moe_shape* shape, const void* ring_y, const int32_t* copy_slot,
+                const float* topk_gate, void* y, hipStream_t stream);
+
+/*
+ * moe_decode: small-batch decode parallelised over outputs, in two kernels and
+ * with no permuted buffer (toolnavs.com warp-decode page, "1.84x plus de vitesse…").
+ * Kernel 1: router and shared-expert gate/up, a grid barrier, then each
+ * wavefront streams rows of W_gate/W_up of the experts the batch selected and
+ * writes h = silu(a) * u in fp32, token-major.  Kernel 2: each wavefront owns a
+ * group of output rows, streams W_down rows of every selected expert and of the
+ * shared expert, and writes y = sum_j g_j (W_down h_j) + W_s_down h_s in bf16.
+ * In:  x [B,d] bf16 (B = shape->tokens <= 64), w_router, b_router (or NULL),
+ *      w_gate/w_up/w_down bf16, shared ws_gate/ws_up [fs,d], ws_down [d,fs] bf16
+ *      or NULL when shape->shared_ffn == 0.
+ * Out: y [B,d] bf16, topk_idx [B,k], topk_gate [B,k].
+ * workspace: moe_workspace_bytes(shape, MOE_OP_DECODE) bytes.  MOE_BF16 only.
+ */
+int moe_decode(const moe_shape* shape, const void* x, const float* w_router,
+               const float* b_router, const void* w_gate, const void* w_up,
+               const void* w_down, const void* ws_gate, const void* ws_up,
+               const void* ws_down, void* y, int32_t* topk_idx, float* topk_gate,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_backward: gradients of L = sum_t <dy_t, y_t> with the routing S held
+ * fixed; the ring is traversed in reverse (dzen.guru, ring-buffer paragraph):
+ * experts E-1 -> 0, and every weight gradient sums its segment's rows from the
+ * last slot to the first.  Per copy (t,j) of expert e with gate g:
+ *   dh = W_down[e]^T dy_t,  dg = <dh, h>,  da = g dh u s (1 + a (1 - s)),
+ *   du = g dh a s  (s = sigmoid(a)),   dx_t += W_gate[e]^T da + W_up[e]^T du,
+ *   dW_down[e] += g dy_t h^T,  dW_gate[e] += da x_t^T,  dW_up[e] += du x_t^T;
+ *   router: dl_j = g_j (dg_j - sum_i g_i dg_i),  dW_r[e_j] += dl_j x_t,  dx_t += dl_j W_r[e_j].
+ * In:  dy [T,d] bf16; x [T,d] bf16; w_router [E,d]; topk_idx, topk_gate; ring_x,
+ *      expert_offset, copy_slot, slot_copy, ring_head from moe_dispatch; saved_au from
+ *      moe_expert_ffn; w_gate, w_up, w_down bf16.
+ * Out: dx [T,d] bf16; dw_gate, dw_up [E,f,d] bf16; dw_down [E,d,f] bf16 (zero for
+ *      experts with no rows); dw_router [E,d] f32.
+ * workspace: moe_workspace_bytes(shape, MOE_OP_BACKWARD) bytes.  MOE_BF16 only.
+ */
+int moe_backward(const moe_shape* shape, const void* dy, const void* x,
+                 const float* w_router, const int32_t* topk_idx, const float* topk_gate,
+                 const void* ring_x, const int32_t* expert_offset, const int32_t* copy_slot,
+                 const int32_t* slot_copy, int64_t ring_head, const void* saved_au,
+                 const void* w_gate, const void* w_up, const void* w_down,
+                 void* dx, void* dw_gate, void* dw_up, void* dw_down, float* dw_router,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace `op` needs for `shape` (0 if none).  Host only, no GPU call. */
+size_t moe_workspace_bytes(const moe_shape* shape, int op);
+
+/* Static description of a status code. */
+const char* moe_status_string(int status);
+
+/*
+ * moe_quantize_mx: MX-quantise a bf16 matrix [rows, cols] along cols (cols % 32 == 0):
+ * per block of 32, X = floor(log2 amax) - 8 clamped to [-127, 127] (-127 for a zero
+ * block), code = RNE_E4M3(clamp(v / 2^X, +-448)), scale = X + 127.
+ * Out: codes [rows, cols] uint8, scales [rows, cols/32] uint8.  Used for the weights.
+ */
+int moe_quantize_mx(const void* src_bf16, int64_t rows, int64_t cols, uint8_t* codes,
+                    uint8_t* scales, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,209 @@
+"""Python binding of the MI355X MoE layer library (libmoe.so, include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  Functions
+with the C names take torch tensors for every buffer (outputs included);
+``Layer`` allocates those buffers and chains the calls.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Optional
+
+import torch
+
+from ._lib import (DTYPES, MOE_BF16, MOE_F32, MOE_MXFP8, OP_BACKWARD, OP_COMBINE, OP_DECODE,
+                   OP_DISPATCH, OP_EXPERT_FFN, OP_ROUTE, LIB_PATH, MoeError, MoeShape, check, lib)
+
+__all__ = ["make_shape", "workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn",
+           "moe_combine", "moe_decode", "moe_backward", "moe_quantize_mx", "Layer", "MoeError",
+           "LIB_PATH"]
+
+
+def make_shape(T: int, d: int, E: int, k: int, f: int, C: Optional[int] = None, fs: int = 0,
+               dtype: str = "bf16") -> MoeShape:
+    import math
+    if C is None:
+        C = int(math.ceil(1.25 * T * k))
+    return MoeShape(tokens=T, capacity=C, hidden=d, experts=E, top_k=k, ffn=f, shared_ffn=fs,
+                    dtype=DTYPES[dtype] if isinstance(dtype, str) else int(dtype))
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libmoe takes device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("libmoe takes contiguous tensors only")
+    return t.data_ptr()
+
+
+def _s(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def workspace_bytes(shape: MoeShape, op: int) -> int:
+    return int(lib().moe_workspace_bytes(shape, op))
+
+
+def workspace(shape: MoeShape, op: int, device) -> torch.Tensor:
+    """A zero-filled workspace buffer of the size `op` needs (at least 256 bytes)."""
+    return torch.zeros(max(workspace_bytes(shape, op), 256), dtype=torch.uint8, device=device)
+
+
+def moe_route(shape, x, w_router, b_router, topk_idx, topk_gate, expert_count, ws, stream=None):
+    check("moe_route", lib().moe_route(shape, _p(x), _p(w_router), _p(b_router), _p(topk_idx),
+                                       _p(topk_gate), _p(expert_count), _p(ws), ws.numel(),
+                                       _s(stream)))
+
+
+def moe_dispatch(shape, x, topk_idx, ring_head, ring_x, ring_x_scale, expert_offset, copy_slot,
+                 slot_copy, ws, stream=None):
+    check("moe_dispatch", lib().moe_dispatch(shape, _p(x), _p(topk_idx), int(ring_head), _p(ring_x),
+                                             _p(ring_x_scale), _p(expert_offset), _p(copy_slot),
+                                             _p(slot_copy), _p(ws), ws.numel(), _s(stream)))
+
+
+def moe_expert_ffn(shape, ring_x, ring_x_scale, expert_offset, ring_head, w_gate, w_up, w_down,
+                   w_gate_scale, w_up_scale, w_down_scale, ring_y, saved_au, ws, stream=None):
+    check("moe_expert_ffn", lib().moe_expert_ffn(
+        shape, _p(ring_x), _p(ring_x_scale), _p(expert_offset), int(ring_head), _p(w_gate),
+        _p(w_up), _p(w_down), _p(w_gate_scale), _p(w_up_scale), _p(w_down_scale), _p(ring_y),
+        _p(saved_au), _p(ws), ws.numel(), _s(stream)))
+
+
+def moe_combine(shape, ring_y, copy_slot, topk_gate, y, stream=None):
+    check("moe_combine", lib().moe_combine(shape, _p(ring_y), _p(copy_slot), _p(topk_gate), _p(y),
+                                           _s(stream)))
+
+
+def moe_decode(shape, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
+               topk_idx, topk_gate, ws, stream=None):
+    check("moe_decode", lib().moe_decode(shape, _p(x), _p(w_router), _p(b_router), _p(w_gate),
+                                         _p(w_up), _p(w_down), _p(ws_gate), _p(ws_up),
+                                         _p(ws_down), _p(y), _p(topk_idx), _p(topk_gate), _p(ws),
+                                         ws.numel(), _s(stream)))
+
+
+def moe_backward(shape, dy, x, w_router, topk_idx, topk_gate, ring_x, expert_offset, copy_slot,
+                 slot_copy, ring_head, saved_au, w_gate, w_up, w_down, dx, dw_gate, dw_up,
+                 dw_down, dw_router, ws, stream=None):
+    check("moe_backward", lib().moe_backward(
+        shape, _p(dy), _p(x), _p(w_router), _p(topk_idx), _p(topk_gate), _p(ring_x),
+        _p(expert_offset), _p(copy_slot), _p(slot_copy), int(ring_head), _p(saved_au),
+        _p(w_gate), _p(w_up), _p(w_down), _p(dx), _p(dw_gate), _p(dw_up), _p(dw_down),
+        _p(dw_router), _p(ws), ws.numel(), _s(stream)))
+
+
+def moe_quantize_mx(src, codes, scales, stream=None):
+    rows = src.numel() // src.shape[-1]
+    check("moe_quantize_mx", lib().moe_quantize_mx(_p(src), rows, src.shape[-1], _p(codes),
+                                                   _p(scales), _s(stream)))
+
+
+def quantize_mx(src: torch.Tensor, stream=None):
+    """(codes uint8, scales uint8) of a bf16 tensor, MX along its last dimension."""
+    codes = torch.empty(src.shape, dtype=torch.uint8, device=src.device)
+    scales = torch.empty(src.shape[:-1] + (src.shape[-1] // 32,), dtype=torch.uint8,
+                         device=src.device)
+    moe_quantize_mx(src, codes, scales, stream)
+    return codes, scales
+
+
+@dataclass
+class Layer:
+    """Buffers of one layer shape, and the forward / backward / decode as chained C calls.
+
+    Expert weights are passed per call; for MXFP8 pass their MX codes and scales."""
+    shape: MoeShape
+    device: torch.device
+    bufs: Dict[str, torch.Tensor] = field(default_factory=dict)
+
+    @classmethod
+    def create(cls, T, d, E, k, f, C=None, fs=0, dtype="bf16", device="cuda"):
+        return cls(make_shape(T, d, E, k, f, C, fs, dtype), torch.device(device))
+
+    @property
+    def act_dtype(self):
+        return torch.float32 if self.shape.dtype == MOE_F32 else torch.bfloat16
+
+    def _buf(self, name, shape, dtype):
+        b = self.bufs.get(name)
+        if b is None or tuple(b.shape) != tuple(shape) or b.dtype != dtype:
+            b = torch.zeros(shape, dtype=dtype, device=self.device)
+            self.bufs[name] = b
+        return b
+
+    def _ws(self, op):
+        n = max(workspace_bytes(self.shape, op), 256)
+        return self._buf(f"ws{op}", (n,), torch.uint8)
+
+    def route(self, x, w_router, b_router=None):
+        s = self.shape
+        T, k, E = s.tokens, s.top_k, s.experts
+        idx = self._buf("topk_idx", (T, k), torch.int32)
+        gate = self._buf("topk_gate", (T, k), torch.float32)
+        cnt = self._buf("expert_count", (E,), torch.int32)
+        moe_route(s, x, w_router, b_router, idx, gate, cnt, self._ws(OP_ROUTE))
+        return idx, gate, cnt
+
+    def dispatch(self, x, topk_idx, head=0):
+        s = self.shape
+        mx = s.dtype == MOE_MXFP8
+        ring = self._buf("ring_x", (s.capacity, s.hidden), torch.uint8 if mx else self.act_dtype)
+        rsc = self._buf("ring_x_scale", (s.capacity, s.hidden // 32), torch.uint8) if mx else None
+        off = self._buf("expert_offset", (s.experts + 1,), torch.int32)
+        cs = self._buf("copy_slot", (s.tokens, s.top_k), torch.int32)
+        sc = self._buf("slot_copy", (s.capacity,), torch.int32)
+        moe_dispatch(s, x, topk_idx, head, ring, rsc, off, cs, sc, self._ws(OP_DISPATCH))
+        return ring, rsc, off, cs, sc
+
+    def expert_ffn(self, ring_x, ring_x_scale, expert_offset, head, w_gate, w_up, w_down,
+                   scales=(None, None, None), save_au=False):
+        s = self.shape
+        ydt = torch.float32 if s.dtype == MOE_F32 else torch.bfloat16
+        ring_y = self._buf("ring_y", (s.capacity, s.hidden), ydt)
+        au = self._buf("saved_au", (s.capacity, 2 * s.ffn), torch.bfloat16) if save_au else None
+        moe_expert_ffn(s, ring_x, ring_x_scale, expert_offset, head, w_gate, w_up, w_down,
+                       scales[0], scales[1], scales[2], ring_y, au, self._ws(OP_EXPERT_FFN))
+        return ring_y, au
+
+    def combine(self, ring_y, copy_slot, topk_gate):
+        s = self.shape
+        y = self._buf("y", (s.tokens, s.hidden), torch.float32 if s.dtype == MOE_F32 else torch.bfloat16)
+        moe_combine(s, ring_y, copy_slot, topk_gate, y)
+        return y
+
+    def forward(self, x, w_router, b_router, w_gate, w_up, w_down, scales=(None, None, None),
+                head=0, save_au=False):
+        idx, gate, cnt = self.route(x, w_router, b_router)
+        ring, rsc, off, cs, sc = self.dispatch(x, idx, head)
+        ring_y, au = self.expert_ffn(ring, rsc, off, head, w_gate, w_up, w_down, scales, save_au)
+        y = self.combine(ring_y, cs, gate)
+        return y
+
+    def decode(self, x, w_router, b_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None,
+               ws_down=None):
+        s = self.shape
+        y = self._buf("y", (s.tokens, s.hidden), torch.bfloat16)
+        idx = self._buf("topk_idx", (s.tokens, s.top_k), torch.int32)
+        gate = self._buf("topk_gate", (s.tokens, s.top_k), torch.float32)
+        moe_decode(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y, idx,
+                   gate, self._ws(OP_DECODE))
+        return y, idx, gate
+
+    def backward(self, dy, x, w_router, w_gate, w_up, w_down, head=0):
+        """Gradients after a forward(..., save_au=True) with the same buffers."""
+        s = self.shape
+        b = self.bufs
+        dx = self._buf("dx", (s.tokens, s.hidden), torch.bfloat16)
+        dwg = self._buf("dw_gate", (s.experts, s.ffn, s.hidden), torch.bfloat16)
+        dwu = self._buf("dw_up", (s.experts, s.ffn, s.hidden), torch.bfloat16)
+        dwd = self._buf("dw_down", (s.experts, s.hidden, s.ffn), torch.bfloat16)
+        dwr = self._buf("dw_router", (s.experts, s.hidden), torch.float32)
+        moe_backward(s, dy, x, w_router, b["topk_idx"], b["topk_gate"], b["ring_x"],
+                     b["expert_offset"], b["copy_slot"], b["slot_copy"], head, b["saved_au"],
+                     w_gate, w_up, w_down, dx, dwg, dwu, dwd, dwr, self._ws(OP_BACKWARD))
+        return dx, dwg, dwu, dwd, dwr

@@ -1,0 +1,146 @@
+// Shared device helpers for the gfx950 MoE kernels: bf16 bits, ring addressing,
+// wave64 reductions and the MX (E4M3 + E8M0 per 32) encoder.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bf16 bit pattern
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// Low / high bf16 of a packed 32-bit word, widened exactly.
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Ring slot of row i of a segment that starts `off` rows after the head.
+__device__ __forceinline__ int64_t ring_slot(int64_t head, int64_t off, int64_t i, int64_t C) {
+  int64_t s = head + off + i;
+  return s >= C ? s - C : s;
+}
+
+__device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
+__device__ __forceinline__ float sigm(float a) { return 1.0f / (1.0f + expf(-a)); }
+
+// Butterfly reductions over the 64 lanes of a wavefront (fixed order: deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+// Reduction over aligned groups of `G` lanes (G a power of two <= 64).
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = G / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ---------------------------------------------------------------- router row
+// Softmax statistics and top-k of one row of E <= 64*VPL logits held by a
+// wavefront (lane owns entries lane + 64 i).  k rounds of a wave-wide argmax,
+// ties to the lower expert id.  On return lane r < k holds the r-th selected
+// expert (`choice`), its rank in ascending expert order (`rank`) and its
+// renormalised gate p / sum_S p with p = exp(l - max) / sum_e exp(l - max).
+template <int VPL>
+__device__ __forceinline__ void wave_route_row(const float* __restrict__ l, int E, int k,
+                                               int& choice, int& rank, float& gate) {
+  const int lane = threadIdx.x & 63;
+  float v[VPL];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? l[e] : -INFINITY;
+    m = fmaxf(m, v[i]);
+  }
+  m = wave_max(m);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) s += (lane + 64 * i < E) ? expf(v[i] - m) : 0.f;
+  s = wave_sum(s);
+  uint32_t taken = 0;
+  choice = 0;
+  float my_logit = 0.f;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == r) { choice = bi; my_logit = bv; }
+  }
+  const float p = lane < k ? expf(my_logit - m) / s : 0.f;
+  const float ps = wave_sum(p);
+  rank = 0;
+  for (int i = 0; i < k; ++i) rank += (__shfl(choice, i, 64) < choice) ? 1 : 0;
+  gate = p / ps;
+}
+
+// ---------------------------------------------------------------- MX / E4M3
+// Block exponent of the OCP MX rule: X = floor(log2 amax) - 8, clamped to
+// [-127, 127]; a zero (or fp32-subnormal) amax gives -127.  amax >= 0.
+__device__ __forceinline__ int mx_block_exp(float amax) {
+  int ef = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+  if (ef == 0) return -127;
+  int X = ef - 127 - 8;
+  return X < -127 ? -127 : X;
+}
+
+// E4M3 code of v * 2^-X: saturate to +-448, round to nearest even.  The sign
+// is kept also when the magnitude rounds to zero.
+__device__ __forceinline__ uint32_t e4m3_encode(float v, int X) {
+  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  float a = fminf(fabsf(ldexpf(v, -X)), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {                       // below 2^-6: subnormal steps of 2^-9
+    code = (uint32_t)rintf(a * 512.0f);      // 0..8; 8 is the smallest normal, encoded alike
+  } else {
+    int e = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;   // floor(log2 a), -6..8
+    uint32_t q = (uint32_t)rintf(ldexpf(a, 3 - e));              // 8..16
+    code = (uint32_t)((e + 7) * 8) + q - 8u;                     // 16 carries into e+1
+  }
+  return code | sign;
+}
+
+}  // namespace moe

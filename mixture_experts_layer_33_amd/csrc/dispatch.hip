@@ -1,0 +1,172 @@
+// Dispatch: a deterministic counting sort of the T*k token copies into the
+// fixed-capacity ring buffer, expert-contiguous, tokens ascending inside each
+// expert's segment.  The pages' token ring buffer has a fixed size, drops no
+// token and needs no size computed on the CPU (dzen.guru page, ring-buffer
+// paragraph of "Три решения, которые дали результат"); every count and offset
+// here stays on the device.
+//
+//   1. per chunk of 64 tokens (one wavefront): for every expert a 64-bit mask
+//      of the chunk's tokens that chose it (LDS atomicOr), and its popcount;
+//   2. one workgroup scans the chunk counts per expert and the expert totals:
+//      base[chunk][e] = rank of the chunk's first copy of expert e;
+//   3. one workgroup per token: rank = base + popcount(mask below the token),
+//      slot = (head + rank) mod C; the row is read once and written to its k
+//      slots (MX: quantised once, codes and scales written k times).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int DCH = 64;  // tokens per chunk = wavefront width
+
+__global__ __launch_bounds__(64) void dispatch_hist_kernel(const int32_t* __restrict__ idx,
+                                                           int64_t T, int k, int E,
+                                                           unsigned long long* __restrict__ masks,
+                                                           int32_t* __restrict__ hist) {
+  extern __shared__ unsigned long long m[];
+  const int lane = threadIdx.x;
+  const int64_t chunk = blockIdx.x;
+  for (int e = lane; e < E; e += 64) m[e] = 0ull;
+  __syncthreads();
+  const int64_t t = chunk * DCH + lane;
+  if (t < T)
+    for (int j = 0; j < k; ++j) atomicOr(&m[idx[t * k + j]], 1ull << lane);
+  __syncthreads();
+  for (int e = lane; e < E; e += 64) {
+    masks[chunk * E + e] = m[e];
+    hist[chunk * E + e] = __popcll(m[e]);
+  }
+}
+
+// One workgroup of 1024 threads, one expert per thread (E <= 1024).
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ hist, int nch,
+                                                             int E,
+                                                             int32_t* __restrict__ expert_offset) {
+  __shared__ int32_t sc[1024];
+  const int e = threadIdx.x;
+  int32_t run = 0;
+  if (e < E)
+    for (int c = 0; c < nch; ++c) {
+      const int32_t h = hist[(int64_t)c * E + e];
+      hist[(int64_t)c * E + e] = run;
+      run += h;
+    }
+  sc[e] = e < E ? run : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the expert totals
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int32_t v = e >= o ? sc[e - o] : 0;
+    __syncthreads();
+    sc[e] += v;
+    __syncthreads();
+  }
+  const int32_t off = sc[e] - run;  // exclusive
+  if (e < E) {
+    expert_offset[e] = off;
+    for (int c = 0; c < nch; ++c) hist[(int64_t)c * E + e] += off;
+  }
+  if (e == E - 1) expert_offset[E] = sc[e];
+}
+
+__device__ __forceinline__ void copy_slots(const int32_t* __restrict__ idx,
+                                           const unsigned long long* __restrict__ masks,
+                                           const int32_t* __restrict__ base, int64_t t, int k,
+                                           int E, int64_t head, int64_t C,
+                                           int32_t* __restrict__ copy_slot,
+                                           int32_t* __restrict__ slot_copy, int64_t* slots) {
+  const int j = threadIdx.x;
+  if (j < k) {
+    const int64_t chunk = t / DCH;
+    const int lc = (int)(t % DCH);
+    const int e = idx[t * k + j];
+    const unsigned long long mk = masks[chunk * E + e];
+    const int64_t rank = base[chunk * E + e] + __popcll(mk & ((1ull << lc) - 1ull));
+    int64_t s = head + rank;
+    if (s >= C) s -= C;
+    slots[j] = s;
+    copy_slot[t * k + j] = (int32_t)s;
+    slot_copy[s] = (int32_t)(t * k + j);
+  }
+  __syncthreads();
+}
+
+// Plain copy of one token row (row_bytes a multiple of 16) into its k slots.
+__global__ __launch_bounds__(256) void dispatch_copy_kernel(
+    const uint8_t* __restrict__ x, const int32_t* __restrict__ idx,
+    const unsigned long long* __restrict__ masks, const int32_t* __restrict__ base, int k, int E,
+    int64_t head, int64_t C, int64_t row_bytes, uint8_t* __restrict__ ring,
+    int32_t* __restrict__ copy_slot, int32_t* __restrict__ slot_copy) {
+  __shared__ int64_t slots[64];
+  const int64_t t = blockIdx.x;
+  copy_slots(idx, masks, base, t, k, E, head, C, copy_slot, slot_copy, slots);
+  const int64_t nv = row_bytes / 16;
+  const u32x4* src = (const u32x4*)(x + t * row_bytes);
+  for (int64_t v = threadIdx.x; v < nv; v += blockDim.x) {
+    const u32x4 val = src[v];
+    for (int j = 0; j < k; ++j) ((u32x4*)(ring + slots[j] * row_bytes))[v] = val;
+  }
+}
+
+// MX: each 32-element block is held by 4 consecutive lanes (8 bf16 each).
+__global__ __launch_bounds__(256) void dispatch_mx_kernel(
+    const bf16_t* __restrict__ x, const int32_t* __restrict__ idx,
+    const unsigned long long* __restrict__ masks, const int32_t* __restrict__ base, int k, int E,
+    int64_t head, int64_t C, int d, uint8_t* __restrict__ ring, uint8_t* __restrict__ ring_scale,
+    int32_t* __restrict__ copy_slot, int32_t* __restrict__ slot_copy) {
+  __shared__ int64_t slots[64];
+  const int64_t t = blockIdx.x;
+  copy_slots(idx, masks, base, t, k, E, head, C, copy_slot, slot_copy, slots);
+  const int nv = d / 8;
+  const int iters = (nv + 255) / 256;  // uniform trip count: all lanes join the shuffles
+  for (int it = 0; it < iters; ++it) {
+    const int v = it * 256 + threadIdx.x;
+    const bool ok = v < nv;
+    u32x4 w = ok ? ((const u32x4*)(x + t * d))[v] : u32x4{0, 0, 0, 0};
+    float f[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { f[2 * q] = lo_bf(w[q]); f[2 * q + 1] = hi_bf(w[q]); }
+    float am = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(f[q]));
+    am = group_max<4>(am);
+    const int X = mx_block_exp(am);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lo |= e4m3_encode(f[q], X) << (8 * q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hi |= e4m3_encode(f[4 + q], X) << (8 * q);
+    if (ok)
+      for (int j = 0; j < k; ++j) {
+        *(u32x2*)(ring + slots[j] * d + (int64_t)v * 8) = u32x2{lo, hi};
+        if ((v & 3) == 0) ring_scale[slots[j] * (d / 32) + v / 4] = (uint8_t)(X + 127);
+      }
+  }
+}
+
+size_t dispatch_workspace_bytes(int64_t T, int E) {
+  const int64_t nch = (T + DCH - 1) / DCH;
+  return (size_t)nch * E * (sizeof(unsigned long long) + sizeof(int32_t));
+}
+
+hipError_t launch_dispatch(const void* x, int elem_bytes, bool mx, const int32_t* topk_idx,
+                           int64_t T, int d, int E, int k, int64_t head, int64_t C, void* ring_x,
+                           uint8_t* ring_scale, int32_t* expert_offset, int32_t* copy_slot,
+                           int32_t* slot_copy, void* ws, hipStream_t st) {
+  const int64_t nch = (T + DCH - 1) / DCH;
+  unsigned long long* masks = (unsigned long long*)ws;
+  int32_t* base = (int32_t*)(masks + nch * E);
+  dispatch_hist_kernel<<<(unsigned)nch, 64, E * sizeof(unsigned long long), st>>>(
+      topk_idx, T, k, E, masks, base);
+  dispatch_scan_kernel<<<1, 1024, 0, st>>>(base, (int)nch, E, expert_offset);
+  if (mx)
+    dispatch_mx_kernel<<<(unsigned)T, 256, 0, st>>>((const bf16_t*)x, topk_idx, masks, base, k, E,
+                                                    head, C, d, (uint8_t*)ring_x, ring_scale,
+                                                    copy_slot, slot_copy);
+  else
+    dispatch_copy_kernel<<<(unsigned)T, 256, 0, st>>>((const uint8_t*)x, topk_idx, masks, base, k,
+                                                      E, head, C, (int64_t)d * elem_bytes,
+                                                      (uint8_t*)ring_x, copy_slot, slot_copy);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,52 @@
+// MX quantisation of a bf16 matrix along its rows (the weight helper): per
+// block of 32 elements X = floor(log2 amax) - 8 (clamped, -127 for a zero
+// block), codes = RNE E4M3 of v / 2^X saturated to +-448, scale byte X + 127.
+// The MXFP8 format is the one the pages name for the expert kernels (khabar-ai
+// page, @rohanpaul_ai tweet; dzen.guru page, megakernel paragraph); the bits
+// follow the OCP MX v1.0 rule.  4 lanes hold one block (8 bf16 each).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void quantize_mx_kernel(const bf16_t* __restrict__ src,
+                                                          int64_t nvec, uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  // nvec = rows * cols / 8 vectors of 8 bf16; blocks never straddle rows (cols % 32 == 0)
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t rounds = (nvec + stride - 1) / stride;
+  for (int64_t it = 0; it < rounds; ++it) {
+    const int64_t v = it * stride + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const bool ok = v < nvec;
+    const u32x4 w = ok ? ((const u32x4*)src)[v] : u32x4{0, 0, 0, 0};
+    float f[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { f[2 * q] = lo_bf(w[q]); f[2 * q + 1] = hi_bf(w[q]); }
+    float am = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(f[q]));
+    am = group_max<4>(am);
+    const int X = mx_block_exp(am);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lo |= e4m3_encode(f[q], X) << (8 * q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hi |= e4m3_encode(f[4 + q], X) << (8 * q);
+    if (ok) {
+      ((u32x2*)codes)[v] = u32x2{lo, hi};
+      if ((v & 3) == 0) scales[v / 4] = (uint8_t)(X + 127);
+    }
+  }
+}
+
+hipError_t launch_quantize_mx(const void* src, int64_t rows, int64_t cols, uint8_t* codes,
+                              uint8_t* scales, hipStream_t st) {
+  const int64_t nvec = rows * cols / 8;
+  if (nvec == 0) return hipSuccess;
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  quantize_mx_kernel<<<(unsigned)blocks, 256, 0, st>>>((const bf16_t*)src, nvec, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -221,17 +221,22 @@ def forward(x: np.ndarray, w_r: np.ndarray, b: Optional[np.ndarray], k: int,
 def forward_tokens(tokens: Sequence[int], x: np.ndarray, routing: Routing, weights: Weights,
                    mx_path: bool = False,
                    shared: Optional[Tuple[np.ndarray, np.ndarray, np.ndarray]] = None) -> np.ndarray:
-    """y for a few tokens, one by one: y_t = sum_j g_tj E_{S_tj}(x_t) (+ shared)."""
+    """y for a few tokens: y_t = sum_j g_tj E_{S_tj}(x_t) (+ shared), evaluated per token.
+    The experts are visited in ascending id (each token's terms in its j order), so that a
+    lazy weight accessor loads every expert once."""
     tokens = np.asarray(tokens, dtype=np.int64)
+    k = routing.idx.shape[1]
+    xs = x[tokens]
+    xq = mx.fake_quant(xs, axis=1) if mx_path else xs
     y = np.zeros((tokens.size, x.shape[1]))
-    for i, t in enumerate(tokens):
-        xt = x[t:t + 1]
-        xq = mx.fake_quant(xt, axis=1) if mx_path else xt
-        for j in range(routing.idx.shape[1]):
-            e = int(routing.idx[t, j])
-            y[i] += routing.gate[t, j] * swiglu(xq, *weights(e), h_mx=mx_path)[0]
-        if shared is not None:
-            y[i] += swiglu(xt, *shared)[0]
+    for e in np.unique(routing.idx[tokens]):
+        wg, wu, wd = weights(int(e))
+        for i, t in enumerate(tokens):
+            for j in range(k):
+                if routing.idx[t, j] == e:
+                    y[i] += routing.gate[t, j] * swiglu(xq[i:i + 1], wg, wu, wd, h_mx=mx_path)[0]
+    if shared is not None:
+        y += swiglu(xs, *shared)
     return y
 
 
