@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
     if (kt + 1 < KT) gload(kt + 1);
     const uint8_t* as = As + cur * BM * KBYTES;
     const uint8_t* bs = Bs + cur * BN * KBYTES;
-    if (!MX) {
+    if constexpr (!MX) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {           // 4 x 16 K per stage
         const int c = kk * 2 + lg;
@@ -240,17 +240,21 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
     } else {
       const uint32_t* asc = Asc + cur * BM;
       const uint32_t* bsc = Bsc + cur * BN;
+      // Operand layout of the 32x32x64 E4M3 MFMA: of a lane's 32 bytes, bytes
+      // 0-15 belong to the first 32-element scale block of the 64-wide K step and
+      // bytes 16-31 to the second; lane group g (= lane / 32) holds elements
+      // [16g, 16g + 16) of each block and supplies the scale of block g.
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {           // 2 x 64 K per stage
-        const int c0 = kk * 4 + lg * 2;          // this lane's 32-byte block = chunks c0, c0+1
+        const int ca = kk * 4 + lg, cb = kk * 4 + 2 + lg;   // 16-byte chunks of this lane
         const int blk = kk * 2 + lg;             // its scale byte inside the row's dword
         i32x8 af[FM], bfr[FN];
         int sa[FM], sb[FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const int r = wm * WTM + i * 32 + lr;
-          const u32x4 lo = *(const u32x4*)(as + swz(r, c0));
-          const u32x4 hi = *(const u32x4*)(as + swz(r, c0 + 1));
+          const u32x4 lo = *(const u32x4*)(as + swz(r, ca));
+          const u32x4 hi = *(const u32x4*)(as + swz(r, cb));
           af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
           sa[i] = (int)((asc[r] >> (8 * blk)) & 0xffu);
@@ -258,8 +262,8 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int r = brow(j) + lr;
-          const u32x4 lo = *(const u32x4*)(bs + swz(r, c0));
-          const u32x4 hi = *(const u32x4*)(bs + swz(r, c0 + 1));
+          const u32x4 lo = *(const u32x4*)(bs + swz(r, ca));
+          const u32x4 hi = *(const u32x4*)(bs + swz(r, cb));
           bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
           sb[j] = (int)((bsc[r] >> (8 * blk)) & 0xffu);
