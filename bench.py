@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X MoE layer on one GPU.
+
+A step is one forward of the layer at 2,048 pre-routing tokens per GPU
+(dzen.guru page, "Что показали замеры?": 2,048 tokens before routing on each
+GPU) with DeepSeek-V3-like expert shapes: d = 7168, E = 256, top-8, f = 2048,
+bf16, ring capacity 1.25 x the copies.  The step runs the whole forward path:
+router, counting-sort dispatch into the ring, gate/up + SwiGLU grouped GEMM,
+down grouped GEMM, gate-weighted combine.  Inputs are synthetic and resident
+in HBM before timing starts.
+
+Prints ONE JSON line.  `roofline` is for the dominant kernel (the gate/up +
+SwiGLU grouped GEMM), from HIP events recorded around it on the launch stream
+in every timed step.  `cpu_baseline` times the fp64 oracle on the host on a
+bounded sample of the same workload.  `secondary` carries the small-batch
+decode (us/token, HBM fraction), the grouped GEMMs at one GPU's
+expert-parallel share (MFMA fraction), and the MXFP8 forward.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-secondary]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at 2048 tok; decode µs/token; % of MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFS = 2516.6
+FP8_PEAK_TFS = 5033.2
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle expert work in the CPU baseline sample")
+    return ap.parse_args()
+
+
+def progress(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gemm_source_hash() -> str:
+    with open(os.path.join(ROOT, "mixture_experts_layer_33_amd", "csrc", "gemm.hip"), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, per_launch_alg_bytes: float):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = data.get(kernel)
+    if not ent or ent.get("gemm_hip_sha256_16") != gemm_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def fwd_step_timed(layer, inp, events):
+    layer.forward(inp.x, inp.w_router, inp.b_router, inp.w_gate, inp.w_up, inp.w_down,
+                  events=events)
+
+
+def measure_forward(torch, moe, inp, cfg, steps, warmup, scales=(None, None, None), wq=None):
+    """Time `steps` forwards; returns (ms/step, avg GEMM-1 ms, avg GEMM-2 ms, layer)."""
+    layer = moe.Layer.create(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.C, dtype=cfg.dtype)
+    wg, wu, wd = wq if wq is not None else (inp.w_gate, inp.w_up, inp.w_down)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for _ in range(warmup):
+        layer.forward(inp.x, inp.w_router, inp.b_router, wg, wu, wd, scales=scales)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        layer.forward(inp.x, inp.w_router, inp.b_router, wg, wu, wd, scales=scales, events=evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    g1 = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    g2 = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    return ms, g1, g2, layer
+
+
+def expert_bytes(counts, d, f, elem_bytes, scale_bytes_per_elem=0.0):
+    used = int((counts > 0).sum())
+    per = d * f * (elem_bytes + scale_bytes_per_elem)
+    return used, used * 2 * per, used * per
+
+
+def cpu_baseline(inp, cfg, budget_s):
+    """The oracle on the host: router, dispatch and combine over all tokens, the expert
+    FFN on a sample of experts (ascending id) until `budget_s` seconds of expert work;
+    the full-layer time is extrapolated by the sampled share of token copies."""
+    import numpy as np
+    import oracle
+    from gen import bits16
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    x = oracle.from_bf16_bits(bits16(inp.x))
+    w_r = oracle.from_f32(inp.w_router.cpu().numpy())
+    t0 = time.perf_counter()
+    r = oracle.route(x, w_r, None, cfg.k)
+    disp = oracle.dispatch(r.idx, cfg.E, cfg.C, 0)
+    ring = oracle.ring_fill(x, disp)
+    t_fixed = time.perf_counter() - t0
+    ring_y = np.zeros((cfg.C, cfg.d))
+    t_exp, rows, sampled = 0.0, 0, 0
+    for e in range(cfg.E):
+        slots = oracle.segment_slots(disp, e)
+        if slots.size == 0:
+            continue
+        w = tuple(oracle.from_bf16_bits(bits16(t[e])) for t in (inp.w_gate, inp.w_up, inp.w_down))
+        if sampled % 8 == 0:
+            progress(f"oracle expert {e}: {t_exp:.1f} s of expert work so far")
+        t1 = time.perf_counter()
+        ring_y[slots] = oracle.swiglu(ring[slots], *w)
+        t_exp += time.perf_counter() - t1
+        rows += slots.size
+        sampled += 1
+        if t_exp >= budget_s:
+            break
+    t2 = time.perf_counter()
+    oracle.combine(ring_y, disp.copy_slot, r.gate)
+    t_fixed += time.perf_counter() - t2
+    est = t_fixed + t_exp * (cfg.n / rows)
+    return {"value": round(cfg.T / est, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 numpy oracle: router, dispatch, ring fill and combine over all "
+                       f"{cfg.T} tokens ({t_fixed:.2f} s); expert SwiGLU on {sampled} of {cfg.E} "
+                       f"experts ({rows} of {cfg.n} copies, {t_exp:.2f} s), full layer "
+                       f"extrapolated by the copy share to {est:.1f} s")}
+
+
+def secondary(torch, moe, steps):
+    import numpy as np
+    from gen import DECODE, FWD_MXFP8, SHARE_BF16, SHARE_MXFP8, make_layer, make_share
+    out = {}
+    # ---- small-batch decode: two kernels, output-parallel
+    dec, prev = {}, None
+    for B in (1, 4, 8):
+        cfg = DECODE(B)
+        progress(f"decode B={B}")
+        inp = make_layer(cfg, "cuda", reuse=prev)
+        prev = inp
+        layer = moe.Layer.create(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, fs=cfg.fs)
+        args = (inp.x, inp.w_router, inp.b_router, inp.w_gate, inp.w_up, inp.w_down,
+                inp.ws_gate, inp.ws_up, inp.ws_down)
+        for _ in range(3):
+            layer.decode(*args)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            layer.decode(*args)
+        e.record()
+        torch.cuda.synchronize()
+        us = s.elapsed_time(e) * 1e3 / steps
+        U = int(np.unique(layer.bufs["topk_idx"].cpu().numpy()).size)
+        nbytes = (U + 1) * 3 * cfg.f * cfg.d * 2 + cfg.E * cfg.d * 4 + 2 * B * cfg.d * 2
+        dec[f"B{B}"] = {"us_per_call": round(us, 2), "us_per_token": round(us / B, 2),
+                        "unique_experts": U, "alg_bytes": nbytes,
+                        "GBps": round(nbytes / us / 1e3, 1),
+                        "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    out["decode"] = dec
+    del prev, inp, layer
+    torch.cuda.empty_cache()
+    # ---- one GPU's expert-parallel share: grouped GEMMs alone, MFMA-bound
+    for scfg, peak in ((SHARE_BF16, BF16_PEAK_TFS), (SHARE_MXFP8, FP8_PEAK_TFS)):
+        progress(f"expert-parallel share {scfg.name}")
+        sh = make_share(scfg, "cuda")
+        mx = scfg.dtype == "mxfp8"
+        shape = moe.make_shape(scfg.rows, scfg.d, scfg.E, 1, scfg.f, scfg.C, dtype=scfg.dtype)
+        off = torch.tensor(np.concatenate([[0], np.cumsum(sh.counts)]), dtype=torch.int32, device="cuda")
+        ws = moe.workspace(shape, moe.OP_EXPERT_FFN, "cuda")
+        ring_y = torch.empty((scfg.C, scfg.d), dtype=torch.bfloat16, device="cuda")
+        if mx:
+            xq, xs = moe.quantize_mx(sh.ring_x)
+            q = [moe.quantize_mx(w) for w in (sh.w_gate, sh.w_up, sh.w_down)]
+            wargs = [c for c, _ in q] + [s for _, s in q]
+        else:
+            xq, xs = sh.ring_x, None
+            wargs = [sh.w_gate, sh.w_up, sh.w_down, None, None, None]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(3 + steps):
+            ev = evs[i - 3] if i >= 3 else [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            moe.moe_expert_ffn_timed(shape, xq, xs, off, 0, *wargs, ring_y, None, ws, ev)
+        torch.cuda.synchronize()
+        g1 = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+        g2 = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+        f1 = 2.0 * scfg.rows * scfg.d * 2 * scfg.f
+        f2 = 2.0 * scfg.rows * scfg.f * scfg.d
+        out[scfg.name] = {"rows": scfg.rows, "experts": scfg.E, "gemm1_ms": round(g1, 4),
+                          "gemm2_ms": round(g2, 4), "ffn_ms": round(g1 + g2, 4),
+                          "TFLOPs": round((f1 + f2) / (g1 + g2) / 1e9, 1),
+                          "mfma_frac": round((f1 + f2) / (g1 + g2) / 1e9 / peak, 4),
+                          "gemm1_mfma_frac": round(f1 / g1 / 1e9 / peak, 4),
+                          "gemm2_mfma_frac": round(f2 / g2 / 1e9 / peak, 4)}
+        del sh, ws, ring_y, xq, xs, wargs
+        torch.cuda.empty_cache()
+    # ---- MXFP8 forward at the same 2,048-token shape
+    cfg = FWD_MXFP8
+    progress(f"forward {cfg.name}")
+    inp = make_layer(cfg, "cuda")
+    q = [moe.quantize_mx(w) for w in (inp.w_gate, inp.w_up, inp.w_down)]
+    ms, g1, g2, layer = measure_forward(torch, moe, inp, cfg, steps, 3,
+                                        scales=tuple(s for _, s in q), wq=tuple(c for c, _ in q))
+    out["fwd_mxfp8_t2048"] = {"tokens_per_s": round(cfg.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+                              "gemm1_ms": round(g1, 4), "gemm2_ms": round(g2, 4)}
+    return out
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU; the layer has no multi-GPU path "
+              "(no collectives, no sharding), so --gpus must be 1.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_33_amd as moe
+    from gen import FWD_BF16, make_layer
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    cfg = FWD_BF16
+    progress(f"drawing inputs of {cfg.name}")
+    inp = make_layer(cfg, "cuda")
+    torch.cuda.synchronize()
+    progress(f"timing {args.steps} steps after {args.warmup} warm-up steps")
+    t0 = time.perf_counter()
+    ms, g1, g2, layer = measure_forward(torch, moe, inp, cfg, args.steps, args.warmup)
+    wall = time.perf_counter() - t0
+    counts = layer.bufs["expert_count"].cpu().numpy()
+    used, w_gu, w_d = expert_bytes(counts, cfg.d, cfg.f, 2)
+    n = cfg.n
+    alg1 = w_gu + n * cfg.d * 2 + n * cfg.f * 2           # weights + ring rows + H
+    alg2 = w_d + n * cfg.f * 2 + n * cfg.d * 2            # weights + H + ring_y
+    flops1 = 2.0 * n * cfg.d * 2 * cfg.f
+    flops2 = 2.0 * n * cfg.f * cfg.d
+    ach1 = alg1 / (g1 * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.d, "experts": cfg.E,
+                   "top_k": cfg.k, "ffn": cfg.f, "capacity": cfg.C, "ring_head": 0,
+                   "step": "route+dispatch+gate/up GEMM+down GEMM+combine"},
+        "roofline": {"kernel": "gg_mfma_kernel<128,256,2,2,SWIGLU,bf16> (gate/up + SwiGLU)",
+                     "bound": "hbm", "achieved": round(ach1, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach1 / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("gemm1_swiglu_bf16", alg1),
+                     "alg_bytes_per_launch": alg1, "avg_launch_ms": round(g1, 4),
+                     "mfma_TFLOPs": round(flops1 / (g1 * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(flops1 / (g1 * 1e-3) / 1e12 / BF16_PEAK_TFS, 4)},
+        "kernels": {"gemm2_down": {"avg_launch_ms": round(g2, 4), "alg_bytes_per_launch": alg2,
+                                   "GBps": round(alg2 / (g2 * 1e-3) / 1e9, 1),
+                                   "hbm_frac": round(alg2 / (g2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                   "mfma_frac": round(flops2 / (g2 * 1e-3) / 1e12 / BF16_PEAK_TFS, 4)},
+                    "experts_used": used,
+                    "layer_hbm_frac": round((alg1 + alg2) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "timed_wall_s": round(wall, 3),
+    }
+    progress(f"forward {ms:.3f} ms/step, gate/up GEMM {g1:.3f} ms, down GEMM {g2:.3f} ms")
+    if not args.no_secondary:
+        result["secondary"] = secondary(torch, moe, max(5, args.steps // 2))
+    if not args.no_cpu_baseline:
+        progress("timing the fp64 oracle on the host (bounded sample)")
+        result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -160,24 +160,31 @@ def _expert_stack(cfg, tensor, E, rows, cols, std, device, dtype):
     return out
 
 
-def make_layer(cfg: LayerConfig, device="cpu") -> LayerInputs:
-    """Draw every input of one workload onto ``device``."""
+def make_layer(cfg: LayerConfig, device="cpu", reuse: Optional[LayerInputs] = None) -> LayerInputs:
+    """Draw every input of one workload onto ``device``.  With ``reuse``, expert weights
+    drawn for another batch of the same workload (same seed substream and shapes) are
+    shared instead of drawn again."""
     device = torch.device(device)
     dt = torch_dtype(cfg.dtype)
     w_r, b, x, redrawn = draw_router_and_tokens(cfg)
     sd = float(np.float32(1.0 / math.sqrt(cfg.d)))
     sf = float(np.float32(1.0 / math.sqrt(cfg.f)))
+    same = (reuse is not None and reuse.cfg.cid == cfg.cid and reuse.cfg.d == cfg.d
+            and reuse.cfg.E == cfg.E and reuse.cfg.f == cfg.f and reuse.cfg.fs == cfg.fs
+            and reuse.cfg.dtype == cfg.dtype and reuse.w_gate.device.type == device.type)
     inp = LayerInputs(
         cfg=cfg,
         x=torch.from_numpy(x).to(dt).to(device),
         w_router=torch.from_numpy(w_r).to(device),
         b_router=None if b is None else torch.from_numpy(b).to(device),
-        w_gate=_expert_stack(cfg, S_WGATE, cfg.E, cfg.f, cfg.d, sd, device, dt),
-        w_up=_expert_stack(cfg, S_WUP, cfg.E, cfg.f, cfg.d, sd, device, dt),
-        w_down=_expert_stack(cfg, S_WDOWN, cfg.E, cfg.d, cfg.f, sf, device, dt),
+        w_gate=reuse.w_gate if same else _expert_stack(cfg, S_WGATE, cfg.E, cfg.f, cfg.d, sd, device, dt),
+        w_up=reuse.w_up if same else _expert_stack(cfg, S_WUP, cfg.E, cfg.f, cfg.d, sd, device, dt),
+        w_down=reuse.w_down if same else _expert_stack(cfg, S_WDOWN, cfg.E, cfg.d, cfg.f, sf, device, dt),
         redrawn=redrawn,
     )
-    if cfg.fs:
+    if same and cfg.fs:
+        inp.ws_gate, inp.ws_up, inp.ws_down = reuse.ws_gate, reuse.ws_up, reuse.ws_down
+    elif cfg.fs:
         sfs = float(np.float32(1.0 / math.sqrt(cfg.fs)))
         inp.ws_gate = _expert_stack(cfg, S_WSGATE, 1, cfg.fs, cfg.d, sd, device, dt)[0]
         inp.ws_up = _expert_stack(cfg, S_WSUP, 1, cfg.fs, cfg.d, sd, device, dt)[0]

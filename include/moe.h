@@ -140,6 +140,20 @@ int moe_expert_ffn(const moe_shape* shape, const void* ring_x, const uint8_t* ri
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_expert_ffn_timed: moe_expert_ffn for measurement.  When `events` is not
+ * NULL, events[0] is recorded on `stream` before GEMM-1, events[1] between GEMM-1
+ * and GEMM-2, events[2] after GEMM-2 (caller-created hipEvent_t handles).  No
+ * host synchronisation; results identical to moe_expert_ffn.
+ */
+int moe_expert_ffn_timed(const moe_shape* shape, const void* ring_x, const uint8_t* ring_x_scale,
+                         const int32_t* expert_offset, int64_t ring_head,
+                         const void* w_gate, const void* w_up, const void* w_down,
+                         const uint8_t* w_gate_scale, const uint8_t* w_up_scale,
+                         const uint8_t* w_down_scale, void* ring_y, void* saved_au,
+                         void* workspace, size_t workspace_bytes, hipEvent_t* events,
+                         hipStream_t stream);
+
+/*
  * moe_combine: y[t] = sum_j g[t,j] ring_y[copy_slot[t,j]], j in ascending expert
  * order, fp32 accumulation, one final rounding (deterministic gather; dzen.guru,
  * megakernel paragraph).
@@ -182,7 +196,8 @@ int moe_decode(const moe_shape* shape, const void* x, const float* w_router,
  *      moe_expert_ffn; w_gate, w_up, w_down bf16.
  * Out: dx [T,d] bf16; dw_gate, dw_up [E,f,d] bf16; dw_down [E,d,f] bf16 (zero for
  *      experts with no rows); dw_router [E,d] f32.
- * workspace: moe_workspace_bytes(shape, MOE_OP_BACKWARD) bytes.  MOE_BF16 only.
+ * workspace: moe_workspace_bytes(shape, MOE_OP_BACKWARD) bytes.  MOE_BF16 only; d and f
+ * must be multiples of 128 (MOE_ERR_SHAPE otherwise).
  */
 int moe_backward(const moe_shape* shape, const void* dy, const void* x,
                  const float* w_router, const int32_t* topk_idx, const float* topk_gate,

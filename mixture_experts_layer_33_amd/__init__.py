@@ -16,6 +16,7 @@ from ._lib import (DTYPES, MOE_BF16, MOE_F32, MOE_MXFP8, OP_BACKWARD, OP_COMBINE
                    OP_DISPATCH, OP_EXPERT_FFN, OP_ROUTE, LIB_PATH, MoeError, MoeShape, check, lib)
 
 __all__ = ["make_shape", "workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn",
+           "moe_expert_ffn_timed",
            "moe_combine", "moe_decode", "moe_backward", "moe_quantize_mx", "Layer", "MoeError",
            "LIB_PATH"]
 
@@ -72,6 +73,21 @@ def moe_expert_ffn(shape, ring_x, ring_x_scale, expert_offset, ring_head, w_gate
         shape, _p(ring_x), _p(ring_x_scale), _p(expert_offset), int(ring_head), _p(w_gate),
         _p(w_up), _p(w_down), _p(w_gate_scale), _p(w_up_scale), _p(w_down_scale), _p(ring_y),
         _p(saved_au), _p(ws), ws.numel(), _s(stream)))
+
+
+def moe_expert_ffn_timed(shape, ring_x, ring_x_scale, expert_offset, ring_head, w_gate, w_up,
+                         w_down, w_gate_scale, w_up_scale, w_down_scale, ring_y, saved_au, ws,
+                         events, stream=None):
+    """moe_expert_ffn that records events[0..2] (torch.cuda.Event) around GEMM-1 and GEMM-2."""
+    import ctypes
+    for e in events:          # torch creates the HIP event on its first record()
+        if e.cuda_event == 0:
+            e.record()
+    arr = (ctypes.c_void_p * 3)(*[e.cuda_event for e in events])
+    check("moe_expert_ffn_timed", lib().moe_expert_ffn_timed(
+        shape, _p(ring_x), _p(ring_x_scale), _p(expert_offset), int(ring_head), _p(w_gate),
+        _p(w_up), _p(w_down), _p(w_gate_scale), _p(w_up_scale), _p(w_down_scale), _p(ring_y),
+        _p(saved_au), _p(ws), ws.numel(), ctypes.cast(arr, ctypes.c_void_p), _s(stream)))
 
 
 def moe_combine(shape, ring_y, copy_slot, topk_gate, y, stream=None):
@@ -161,13 +177,18 @@ class Layer:
         return ring, rsc, off, cs, sc
 
     def expert_ffn(self, ring_x, ring_x_scale, expert_offset, head, w_gate, w_up, w_down,
-                   scales=(None, None, None), save_au=False):
+                   scales=(None, None, None), save_au=False, events=None):
         s = self.shape
         ydt = torch.float32 if s.dtype == MOE_F32 else torch.bfloat16
         ring_y = self._buf("ring_y", (s.capacity, s.hidden), ydt)
         au = self._buf("saved_au", (s.capacity, 2 * s.ffn), torch.bfloat16) if save_au else None
-        moe_expert_ffn(s, ring_x, ring_x_scale, expert_offset, head, w_gate, w_up, w_down,
-                       scales[0], scales[1], scales[2], ring_y, au, self._ws(OP_EXPERT_FFN))
+        if events is None:
+            moe_expert_ffn(s, ring_x, ring_x_scale, expert_offset, head, w_gate, w_up, w_down,
+                           scales[0], scales[1], scales[2], ring_y, au, self._ws(OP_EXPERT_FFN))
+        else:
+            moe_expert_ffn_timed(s, ring_x, ring_x_scale, expert_offset, head, w_gate, w_up, w_down,
+                                 scales[0], scales[1], scales[2], ring_y, au,
+                                 self._ws(OP_EXPERT_FFN), events)
         return ring_y, au
 
     def combine(self, ring_y, copy_slot, topk_gate):
@@ -177,10 +198,11 @@ class Layer:
         return y
 
     def forward(self, x, w_router, b_router, w_gate, w_up, w_down, scales=(None, None, None),
-                head=0, save_au=False):
+                head=0, save_au=False, events=None):
         idx, gate, cnt = self.route(x, w_router, b_router)
         ring, rsc, off, cs, sc = self.dispatch(x, idx, head)
-        ring_y, au = self.expert_ffn(ring, rsc, off, head, w_gate, w_up, w_down, scales, save_au)
+        ring_y, au = self.expert_ffn(ring, rsc, off, head, w_gate, w_up, w_down, scales, save_au,
+                                     events)
         y = self.combine(ring_y, cs, gate)
         return y
 

@@ -31,6 +31,7 @@ SIGNATURES = {
     "moe_route": [SHP, P, P, P, P, P, P, P, SZ, P],
     "moe_dispatch": [SHP, P, P, I64, P, P, P, P, P, P, SZ, P],
     "moe_expert_ffn": [SHP, P, P, P, I64, P, P, P, P, P, P, P, P, P, SZ, P],
+    "moe_expert_ffn_timed": [SHP, P, P, P, I64, P, P, P, P, P, P, P, P, P, SZ, P, P],
     "moe_combine": [SHP, P, P, P, P, P],
     "moe_decode": [SHP, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_backward": [SHP, P, P, P, P, P, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, P, SZ, P],

@@ -111,11 +111,12 @@ int moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx, int
   }
 }
 
-int moe_expert_ffn(const moe_shape* s, const void* ring_x, const uint8_t* ring_x_scale,
+int moe_expert_ffn_timed(const moe_shape* s, const void* ring_x, const uint8_t* ring_x_scale,
                    const int32_t* expert_offset, int64_t ring_head, const void* w_gate,
                    const void* w_up, const void* w_down, const uint8_t* w_gate_scale,
                    const uint8_t* w_up_scale, const uint8_t* w_down_scale, void* ring_y,
-                   void* saved_au, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                   void* saved_au, void* workspace, size_t workspace_bytes,
+                         hipEvent_t* events, hipStream_t stream) {
   try {
     int st = check_shape(s);
     if (st) return st;
@@ -131,10 +132,20 @@ int moe_expert_ffn(const moe_shape* s, const void* ring_x, const uint8_t* ring_x
     return hip_status(moe::launch_ffn(s->dtype, ring_x, ring_x_scale, expert_offset, ring_head,
                                       s->capacity, s->tokens * s->top_k, s->hidden, s->experts,
                                       s->ffn, w_gate, w_up, w_down, w_gate_scale, w_up_scale,
-                                      w_down_scale, ring_y, saved_au, workspace, stream));
+                                      w_down_scale, ring_y, saved_au, workspace, events, stream));
   } catch (...) {
     return MOE_ERR_HIP;
   }
+}
+
+int moe_expert_ffn(const moe_shape* s, const void* ring_x, const uint8_t* ring_x_scale,
+                   const int32_t* expert_offset, int64_t ring_head, const void* w_gate,
+                   const void* w_up, const void* w_down, const uint8_t* w_gate_scale,
+                   const uint8_t* w_up_scale, const uint8_t* w_down_scale, void* ring_y,
+                   void* saved_au, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return moe_expert_ffn_timed(s, ring_x, ring_x_scale, expert_offset, ring_head, w_gate, w_up,
+                              w_down, w_gate_scale, w_up_scale, w_down_scale, ring_y, saved_au,
+                              workspace, workspace_bytes, nullptr, stream);
 }
 
 int moe_combine(const moe_shape* s, const void* ring_y, const int32_t* copy_slot,
@@ -185,6 +196,7 @@ int moe_backward(const moe_shape* s, const void* dy, const void* x, const float*
     int st = check_shape(s);
     if (st) return st;
     if (s->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (s->hidden % 128 || s->ffn % 128) return MOE_ERR_SHAPE;   // 128 x 128 gradient tiles
     if (!dy || !x || !w_router || !topk_idx || !topk_gate || !ring_x || !expert_offset ||
         !copy_slot || !slot_copy || !saved_au || !w_gate || !w_up || !w_down || !dx || !dw_gate ||
         !dw_up || !dw_down || !dw_router || !workspace)

@@ -48,6 +48,12 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   if (e == 1023) *ntiles = sc[1023];
 }
 
+hipError_t launch_build_tiles(const int32_t* expert_offset, int E, int BM, int32_t* tiles,
+                              int32_t* ntiles, hipStream_t st) {
+  build_tiles_kernel<<<1, 1024, 0, st>>>(expert_offset, E, BM, tiles, ntiles);
+  return hipGetLastError();
+}
+
 // ============================================================ bf16 / MX MFMA GEMM
 // Workgroup tile BM x BN, K staged in 128-byte row slices (64 bf16 or 128 fp8)
 // through double-buffered LDS.  16-byte chunks of a row are XOR-swizzled by
@@ -437,7 +443,8 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
                       const int32_t* expert_offset, int64_t head, int64_t C, int64_t n, int d,
                       int E, int f, const void* w_gate, const void* w_up, const void* w_down,
                       const uint8_t* wg_scale, const uint8_t* wu_scale, const uint8_t* wd_scale,
-                      void* ring_y, void* saved_au, void* ws, hipStream_t st) {
+                      void* ring_y, void* saved_au, void* ws, hipEvent_t* events,
+                      hipStream_t st) {
   const int BM = dtype == 0 ? FT_M : MFMA_BM;
   const int max_tiles = max_tiles_for(n, E, BM);
   int32_t* ntiles = (int32_t*)ws;
@@ -448,14 +455,18 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
   build_tiles_kernel<<<1, 1024, 0, st>>>(expert_offset, E, BM, tiles, ntiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  auto mark = [&](int i) { return events ? hipEventRecord(events[i], st) : hipSuccess; };
+  if ((err = mark(0)) != hipSuccess) return err;
 
   if (dtype == 0) {
     gg_f32_kernel<true><<<dim3((f + FT_N - 1) / FT_N, max_tiles), 256, 0, st>>>(
         (const float*)ring_x, (const float*)w_gate, (const float*)w_up, d, f, expert_offset,
         tiles, ntiles, head, C, (float*)H);
+    if ((err = mark(1)) != hipSuccess) return err;
     gg_f32_kernel<false><<<dim3((d + FT_N - 1) / FT_N, max_tiles), 256, 0, st>>>(
         (const float*)H, (const float*)w_down, nullptr, f, d, expert_offset, tiles, ntiles, head,
         C, (float*)ring_y);
+    if ((err = mark(2)) != hipSuccess) return err;
     return hipGetLastError();
   }
   GemmArgs g1{};
@@ -487,14 +498,13 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
   g2.out = (uint8_t*)ring_y;
   g2.out_scale = nullptr;
   g2.saved_au = nullptr;
-  if (dtype == 1) {
-    err = run_mfma<MFMA_BM, 256, 2, 2, true, false>(g1, max_tiles, st);
-    if (err != hipSuccess) return err;
-    return run_mfma<MFMA_BM, 256, 2, 2, false, false>(g2, max_tiles, st);
-  }
-  err = run_mfma<MFMA_BM, 256, 2, 2, true, true>(g1, max_tiles, st);
+  if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, true, false>(g1, max_tiles, st);
+  else err = run_mfma<MFMA_BM, 256, 2, 2, true, true>(g1, max_tiles, st);
+  if (err != hipSuccess || (err = mark(1)) != hipSuccess) return err;
+  if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, false, false>(g2, max_tiles, st);
+  else err = run_mfma<MFMA_BM, 256, 2, 2, false, true>(g2, max_tiles, st);
   if (err != hipSuccess) return err;
-  return run_mfma<MFMA_BM, 256, 2, 2, false, true>(g2, max_tiles, st);
+  return mark(2);
 }
 
 }  // namespace moe

@@ -21,12 +21,16 @@ hipError_t launch_dispatch(const void* x, int elem_bytes, bool mx, const int32_t
                            int32_t* slot_copy, void* ws, hipStream_t st);
 
 // expert FFN (grouped GEMMs)
+// tiles[2i] = expert, tiles[2i+1] = first segment row of row-tile i (height BM); *ntiles = count
+hipError_t launch_build_tiles(const int32_t* expert_offset, int E, int BM, int32_t* tiles,
+                              int32_t* ntiles, hipStream_t st);
 size_t ffn_workspace_bytes(int64_t n, int64_t C, int d, int E, int f, int dtype);
 hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale,
                       const int32_t* expert_offset, int64_t head, int64_t C, int64_t n, int d,
                       int E, int f, const void* w_gate, const void* w_up, const void* w_down,
                       const uint8_t* wg_scale, const uint8_t* wu_scale, const uint8_t* wd_scale,
-                      void* ring_y, void* saved_au, void* ws, hipStream_t st);
+                      void* ring_y, void* saved_au, void* ws, hipEvent_t* events,
+                      hipStream_t st);
 
 // combine
 hipError_t launch_combine(bool f32, const void* ring_y, const int32_t* copy_slot,

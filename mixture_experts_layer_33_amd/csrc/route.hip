@@ -43,6 +43,9 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
       ws[kk + q][r] = (e < E && kq < d) ? w[(int64_t)e * d + kq] : 0.f;
     }
     __syncthreads();
+    // two-level sum: a partial over this K slice, then the running total, so the
+    // rounding error grows with d/32 + 32 terms rather than d
+    float part[4][4] = {};
 #pragma unroll 8
     for (int kq = 0; kq < RT_K; ++kq) {
       float a[4], b[4];
@@ -53,8 +56,12 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) part[i][j] = fmaf(a[i], b[j], part[i][j]);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] += part[i][j];
     __syncthreads();
   }
 #pragma unroll

@@ -23,7 +23,7 @@ def check_decode(cfg, reps=5):
     b = None if inp.b_router is None else to_oracle(inp.b_router)
     r = oracle.route(x, w_r, b, cfg.k)
     np.testing.assert_array_equal(idx.cpu().numpy(), r.idx)
-    np.testing.assert_allclose(gate.cpu().numpy(), r.gate, rtol=0, atol=2e-6)
+    assert rel(gate.cpu().numpy(), r.gate) <= 1e-5   # fp32 router output
     lw = LazyWeights(inp.w_gate, inp.w_up, inp.w_down)
     shared = tuple(to_oracle(w) for w in (inp.ws_gate, inp.ws_up, inp.ws_down)) if cfg.fs else None
     ref = oracle.forward_tokens(range(cfg.T), x, r, lw, shared=shared)

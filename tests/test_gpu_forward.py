@@ -79,7 +79,7 @@ def test_forward_parity(cfg):
         # router: bit-exact selection and counts, gates to fp32 accuracy
         np.testing.assert_array_equal(out["topk_idx"].cpu().numpy(), ref_r.idx)
         np.testing.assert_array_equal(out["expert_count"].cpu().numpy(), ref_r.count)
-        np.testing.assert_allclose(out["topk_gate"].cpu().numpy(), ref_r.gate, rtol=0, atol=2e-6)
+        assert rel(out["topk_gate"].cpu().numpy(), ref_r.gate) <= 1e-5   # fp32 router output
         # dispatch: bit-exact permutation and offsets
         disp = oracle.dispatch(ref_r.idx, cfg.E, cfg.C, head)
         np.testing.assert_array_equal(out["expert_offset"].cpu().numpy(), disp.offset)
@@ -134,7 +134,7 @@ def test_forward_full_size_sampled(cfg):
     out = run_forward(layer, inp, head, scales, wq)
     np.testing.assert_array_equal(out["topk_idx"].cpu().numpy(), ref_r.idx)
     np.testing.assert_array_equal(out["expert_count"].cpu().numpy(), ref_r.count)
-    np.testing.assert_allclose(out["topk_gate"].cpu().numpy(), ref_r.gate, rtol=0, atol=2e-6)
+    assert rel(out["topk_gate"].cpu().numpy(), ref_r.gate) <= 1e-5   # fp32 router output
     disp = oracle.dispatch(ref_r.idx, cfg.E, cfg.C, head)
     np.testing.assert_array_equal(out["expert_offset"].cpu().numpy(), disp.offset)
     np.testing.assert_array_equal(out["copy_slot"].cpu().numpy(), disp.copy_slot)
