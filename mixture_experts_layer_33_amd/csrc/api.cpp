@@ -44,7 +44,7 @@ size_t moe_workspace_bytes(const moe_shape* s, int op) {
   if (!s || check_shape(s) != MOE_OK) return 0;
   const int64_t T = s->tokens, n = s->tokens * s->top_k, C = s->capacity;
   switch (op) {
-    case MOE_OP_ROUTE: return align256(moe::route_workspace_bytes(T, s->experts));
+    case MOE_OP_ROUTE: return align256(moe::route_workspace_bytes(T, s->experts, s->hidden));
     case MOE_OP_DISPATCH: return align256(moe::dispatch_workspace_bytes(T, s->experts));
     case MOE_OP_EXPERT_FFN:
       return align256(moe::ffn_workspace_bytes(n, C, s->hidden, s->experts, s->ffn, s->dtype));

@@ -16,6 +16,8 @@
 // Paths: bf16 MFMA (v_mfma_f32_32x32x16_bf16), MX fp8 MFMA
 // (v_mfma_scale_f32_32x32x64_f8f6f4: E4M3 operands, one E8M0 scale per 32 K),
 // and an fp32 VALU path for fp32 layers.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -86,112 +88,147 @@ struct GemmArgs {
   uint16_t* saved_au;      // SWIGLU + bf16: [C, 2f] or null
 };
 
-template <int BM, int BN, int WM, int WN, bool SWIGLU, bool MX>
+// Tile order.  The grid is 1-D; workgroup b runs on XCD b % 8 (round-robin
+// dispatch).  Logical tile L = (row tile, column tile), column tiles fastest,
+// is given to XCD x as one contiguous range of ceil(V / 8) tiles, V the number
+// of live tiles read on the device: all column tiles of one expert's row tile
+// then share the token rows through one XCD's L2.
+__device__ __forceinline__ bool xcd_tile(int nt_cols, int ntiles, int& mt, int& ct) {
+  const int V = ntiles * nt_cols;
+  const int per = (V + 7) / 8;
+  const int b = blockIdx.x;
+  const int li = b >> 3, x = b & 7;
+  if (li >= per) return false;
+  const int L = x * per + li;
+  if (L >= V) return false;
+  mt = L / nt_cols;
+  ct = L - mt * nt_cols;
+  return true;
+}
+
+// Global -> LDS copies of 16 (or 4) bytes per lane, issued from asm so that the
+// compiler does not wait for them: the kernel places its own vmcnt waits.  The
+// wave's 64 lanes write one contiguous run of LDS at m0 (+ lane * size).
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Stage layout in LDS: A tile [BM][128 B] | B tile [BN][128 B] | MX: A scale dwords,
+// one private copy of [BM] per wave | B scale dwords [BN].  S stages form a ring.
+template <int BM, int BN, bool MX>
+struct StageLayout {
+  static constexpr int A = 0;
+  static constexpr int B = BM * KBYTES;
+  static constexpr int ASC = B + BN * KBYTES;
+  static constexpr int BSC = ASC + (MX ? 4 * BM * 4 : 0);
+  static constexpr int SIZE = BSC + (MX ? BN * 4 : 0);
+};
+
+template <int BM, int BN, int WM, int WN, bool SWIGLU, bool MX, int S>
 __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
   constexpr int EB = MX ? 1 : 2;                 // element bytes
   constexpr int WTM = BM / WM, WTN = BN / WN;    // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int A_LD = BM * CHUNKS / 256, B_LD = BN * CHUNKS / 256;   // 16B loads per thread
-  static_assert(BM * CHUNKS % 256 == 0 && BN * CHUNKS % 256 == 0, "tile / thread mismatch");
+  using SL = StageLayout<BM, BN, MX>;
+  constexpr int NA = BM * KBYTES / 4096, NB = BN * KBYTES / 4096;   // 1 KB copies per wave
+  constexpr int NASC = MX ? BM * 4 / 256 : 0, NBSC = MX ? BN * 4 / 1024 : 0;
+  constexpr int L = NA + NB + NASC + NBSC;       // copies per wave per stage
+  static_assert(BM * KBYTES % 4096 == 0 && BN * KBYTES % 4096 == 0, "tile / wave mismatch");
+  static_assert(!MX || (BM * 4 % 256 == 0 && BN * 4 % 1024 == 0), "scale copies");
   static_assert(!SWIGLU || (FN % 2 == 0), "gate/up fragments come in pairs");
+  static_assert(S >= 2 && S <= 4, "stages");
 
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* As = lds;                               // [2][BM * KBYTES]
-  uint8_t* Bs = lds + 2 * BM * KBYTES;             // [2][BN * KBYTES]
-  uint32_t* Asc = (uint32_t*)(Bs + 2 * BN * KBYTES);   // MX: [2][BM]
-  uint32_t* Bsc = Asc + 2 * BM;                        // MX: [2][BN]
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
 
-  const int mt = blockIdx.y;
-  if (mt >= *p.ntiles) return;
+  const int nt_cols = SWIGLU ? (p.N + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
+  int mt, ct;
+  if (!xcd_tile(nt_cols, *p.ntiles, mt, ct)) return;
   const int e = p.tiles[2 * mt];
   const int row0 = p.tiles[2 * mt + 1];
   const int32_t seg = p.offset[e];
   const int rows = min(BM, p.offset[e + 1] - seg - row0);
-  const int n0 = blockIdx.x * (SWIGLU ? BN / 2 : BN);   // first output column
+  const int n0 = ct * (SWIGLU ? BN / 2 : BN);   // first output column
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave / WN, wn = wave % WN;
-  const int64_t Kb = (int64_t)p.K * EB;                 // row bytes
+  const uint32_t Kb = (uint32_t)p.K * EB;                 // row bytes
+  const uint32_t Ks = (uint32_t)p.K / 32;                 // MX scale bytes per row
 
-  // per-thread global row pointers (rows past the segment reuse its last row)
-  const uint8_t* a_src[A_LD];
+  // Copy i of this wave fills 16-byte chunks j = (4 i + wave) * 64 + lane of a tile:
+  // row j / 8, swizzled slot j % 8, which holds global chunk (slot ^ (row & 7)).
+  uint32_t a_off[NA], b_off[NB];
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int r = (tid + 256 * i) / CHUNKS;
-    const int64_t s = ring_slot(p.head, seg, row0 + min(r, rows - 1), p.C);
-    a_src[i] = p.A + s * Kb + ((tid + 256 * i) % CHUNKS) * 16;
+  for (int i = 0; i < NA; ++i) {
+    const int j = (4 * i + wave) * 64 + lane, r = j >> 3, c = (j & 7) ^ (r & 7);
+    const int64_t sl = ring_slot(p.head, seg, row0 + min(r, rows - 1), p.C);
+    a_off[i] = (uint32_t)sl * Kb + c * 16;
   }
-  const uint8_t* b_src[B_LD];
+  // B rows: SWIGLU stacks BN/2 rows of W_gate over BN/2 rows of W_up; a copy covers
+  // 8 rows, so each copy reads from a single matrix (decided by its first row).
+  const uint8_t* b_base[NB];
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int r = (tid + 256 * i) / CHUNKS;
-    int64_t wrow;
-    const uint8_t* base;
-    if (SWIGLU) {
-      const bool up = r >= BN / 2;
-      wrow = (int64_t)e * p.N + min(n0 + (up ? r - BN / 2 : r), p.N - 1);
-      base = up ? p.B1 : p.B0;
-    } else {
-      wrow = (int64_t)e * p.N + min(n0 + r, p.N - 1);
-      base = p.B0;
+  for (int i = 0; i < NB; ++i) {
+    const int j = (4 * i + wave) * 64 + lane, r = j >> 3, c = (j & 7) ^ (r & 7);
+    const bool up = SWIGLU && (4 * i + wave) * 8 >= BN / 2;
+    const int rr = up ? r - BN / 2 : r;
+    b_base[i] = (up ? p.B1 : p.B0) + (int64_t)e * p.N * Kb;
+    b_off[i] = (uint32_t)min(n0 + rr, p.N - 1) * Kb + c * 16;
+  }
+  uint32_t asc_off[NASC > 0 ? NASC : 1], bsc_off[NBSC > 0 ? NBSC : 1];
+  const uint8_t* bsc_base[NBSC > 0 ? NBSC : 1];
+  if (MX) {
+#pragma unroll
+    for (int i = 0; i < NASC; ++i) {          // every wave copies all BM scale rows
+      const int r = i * 64 + lane;
+      asc_off[i] = (uint32_t)ring_slot(p.head, seg, row0 + min(r, rows - 1), p.C) * Ks;
     }
-    b_src[i] = base + wrow * Kb + ((tid + 256 * i) % CHUNKS) * 16;
+#pragma unroll
+    for (int i = 0; i < NBSC; ++i) {          // the waves share the BN scale rows
+      const int r = (4 * i + wave) * 64 + lane;
+      const bool up = SWIGLU && (4 * i + wave) * 64 >= BN / 2;
+      const int rr = up ? r - BN / 2 : r;
+      bsc_base[i] = (up ? p.B1_scale : p.B0_scale) + (int64_t)e * p.N * Ks;
+      bsc_off[i] = (uint32_t)min(n0 + rr, p.N - 1) * Ks;
+    }
   }
-
-  u32x4 ra[A_LD], rb[B_LD];
-  uint32_t rsa = 0, rsb[2] = {0, 0};
-  auto gload = [&](int kt) {
-    const int64_t kb = (int64_t)kt * KBYTES;
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    const uint32_t st = lds0 + (uint32_t)(kt % S) * SL::SIZE;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = *(const u32x4*)(a_src[i] + kb);
+    for (int i = 0; i < NA; ++i)
+      dma16(p.A + (size_t)kt * KBYTES, a_off[i], __builtin_amdgcn_readfirstlane(st + SL::A + (4 * i + wave) * 1024));
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) rb[i] = *(const u32x4*)(b_src[i] + kb);
+    for (int i = 0; i < NB; ++i)
+      dma16(b_base[i] + (size_t)kt * KBYTES, b_off[i], __builtin_amdgcn_readfirstlane(st + SL::B + (4 * i + wave) * 1024));
     if (MX) {
-      // one scale dword (4 blocks of 32) per row: threads 0..BM-1 take A rows,
-      // threads 0..BN-1 take B rows
-      if (tid < BM) {
-        const int64_t s = ring_slot(p.head, seg, row0 + min(tid, rows - 1), p.C);
-        rsa = *(const uint32_t*)(p.A_scale + s * (p.K / 32) + kt * 4);
-      }
 #pragma unroll
-      for (int h = 0; h < (BN + 255) / 256; ++h) {
-        const int r = tid + 256 * h;
-        if (r < BN) {
-          int64_t wrow;
-          const uint8_t* sbase;
-          if (SWIGLU) {
-            const bool up = r >= BN / 2;
-            wrow = (int64_t)e * p.N + min(n0 + (up ? r - BN / 2 : r), p.N - 1);
-            sbase = up ? p.B1_scale : p.B0_scale;
-          } else {
-            wrow = (int64_t)e * p.N + min(n0 + r, p.N - 1);
-            sbase = p.B0_scale;
-          }
-          rsb[h] = *(const uint32_t*)(sbase + wrow * (p.K / 32) + kt * 4);
-        }
-      }
+      for (int i = 0; i < NASC; ++i)
+        dma4(p.A_scale + (size_t)kt * 4, asc_off[i],
+             __builtin_amdgcn_readfirstlane(st + SL::ASC + wave * BM * 4 + i * 256));
+#pragma unroll
+      for (int i = 0; i < NBSC; ++i)
+        dma4(bsc_base[i] + (size_t)kt * 4, bsc_off[i],
+             __builtin_amdgcn_readfirstlane(st + SL::BSC + (4 * i + wave) * 256));
     }
   };
-  auto sstore = [&](int buf) {
-    uint8_t* as = As + buf * BM * KBYTES;
-    uint8_t* bs = Bs + buf * BN * KBYTES;
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int q = tid + 256 * i;
-      *(u32x4*)(as + swz(q / CHUNKS, q % CHUNKS)) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int q = tid + 256 * i;
-      *(u32x4*)(bs + swz(q / CHUNKS, q % CHUNKS)) = rb[i];
-    }
-    if (MX) {
-      if (tid < BM) Asc[buf * BM + tid] = rsa;
-#pragma unroll
-      for (int h = 0; h < (BN + 255) / 256; ++h)
-        if (tid + 256 * h < BN) Bsc[buf * BN + tid + 256 * h] = rsb[h];
-    }
+  // wait until this wave's copies of the stage issued `later` stages before the
+  // newest one have landed
+  auto wait_stage = [&](int later) __attribute__((always_inline)) {
+    if (later <= 0) wait_vm<0>();
+    else if (later == 1) wait_vm<L>();
+    else if (later == 2) wait_vm<2 * L>();
+    else wait_vm<3 * L>();
   };
 
   // B fragment row (inside the B tile) of fragment fn
@@ -212,16 +249,10 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = (int)(Kb / KBYTES);
-  gload(0);
-  sstore(0);
-  __syncthreads();
   const int lr = lane & 31, lg = lane >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const uint8_t* as = As + cur * BM * KBYTES;
-    const uint8_t* bs = Bs + cur * BN * KBYTES;
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    const uint8_t* as = lds + buf * SL::SIZE + SL::A;
+    const uint8_t* bs = lds + buf * SL::SIZE + SL::B;
     if constexpr (!MX) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {           // 4 x 16 K per stage
@@ -244,8 +275,8 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
     } else {
-      const uint32_t* asc = Asc + cur * BM;
-      const uint32_t* bsc = Bsc + cur * BN;
+      const uint32_t* asc = (const uint32_t*)(lds + buf * SL::SIZE + SL::ASC) + wave * BM;
+      const uint32_t* bsc = (const uint32_t*)(lds + buf * SL::SIZE + SL::BSC);
       // Operand layout of the 32x32x64 E4M3 MFMA: of a lane's 32 bytes, bytes
       // 0-15 belong to the first 32-element scale block of the 64-wide K step and
       // bytes 16-31 to the second; lane group g (= lane / 32) holds elements
@@ -282,9 +313,21 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
                 af[i], bfr[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
       }
     }
-    if (kt + 1 < KT) sstore(cur ^ 1);
+  };
+
+  // S-stage ring: stages kt+1 .. kt+S-1 stream in while stage kt is computed.
+  // One barrier per stage: it publishes stage kt (every wave waited for its own
+  // copies) and retires the buffer of stage kt-1, which the copies of stage kt+S-1
+  // then overwrite.
+  const int KT = (int)(Kb / KBYTES);
+  for (int s = 0; s < S - 1 && s < KT; ++s) issue(s);
+  for (int kt = 0; kt < KT; ++kt) {
+    wait_stage(min(S - 2, KT - 1 - kt));
     __syncthreads();
+    if (kt + S - 1 < KT) issue(kt + S - 1);
+    compute(kt % S);
   }
+  __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
   // acc register r of a 32x32 fragment: row 8*(r/4) + 4*(lane/32) + r%4, column lane%32.
@@ -337,11 +380,11 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool SWIGLU, bool MX>
+template <int BM, int BN, int WM, int WN, bool SWIGLU, bool MX, int S>
 static hipError_t run_mfma(const GemmArgs& a, int max_tiles, hipStream_t st) {
   const int nt = SWIGLU ? (a.N + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
-  const size_t lds = 2 * (BM + BN) * KBYTES + (MX ? 2 * (BM + BN) * 4 : 0);
-  auto kern = gg_mfma_kernel<BM, BN, WM, WN, SWIGLU, MX>;
+  const size_t lds = (size_t)S * StageLayout<BM, BN, MX>::SIZE;
+  auto kern = gg_mfma_kernel<BM, BN, WM, WN, SWIGLU, MX, S>;
   static bool attr_set = false;   // opt in to more than 64 KB of LDS once per process
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute((const void*)kern,
@@ -349,7 +392,9 @@ static hipError_t run_mfma(const GemmArgs& a, int max_tiles, hipStream_t st) {
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  kern<<<dim3(nt, max_tiles), 256, lds, st>>>(a);
+  const int64_t vmax = (int64_t)max_tiles * nt;          // bound on live tiles
+  const int64_t grid = 8 * ((vmax + 7) / 8);
+  kern<<<(unsigned)grid, 256, lds, st>>>(a);
   return hipGetLastError();
 }
 
@@ -426,6 +471,10 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
 // ============================================================ launcher
 // Row-tile height of the MFMA paths and the fp32 path.
 constexpr int MFMA_BM = 128;
+#ifndef MOE_MFMA_STAGES
+#define MOE_MFMA_STAGES 3
+#endif
+constexpr int MFMA_PF = MOE_MFMA_STAGES;   // LDS ring stages of the grouped GEMMs
 
 static int max_tiles_for(int64_t n, int E, int BM) { return (int)((n + BM - 1) / BM) + E; }
 
@@ -498,11 +547,11 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
   g2.out = (uint8_t*)ring_y;
   g2.out_scale = nullptr;
   g2.saved_au = nullptr;
-  if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, true, false>(g1, max_tiles, st);
-  else err = run_mfma<MFMA_BM, 256, 2, 2, true, true>(g1, max_tiles, st);
+  if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, true, false, MFMA_PF>(g1, max_tiles, st);
+  else err = run_mfma<MFMA_BM, 256, 2, 2, true, true, MFMA_PF>(g1, max_tiles, st);
   if (err != hipSuccess || (err = mark(1)) != hipSuccess) return err;
-  if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, false, false>(g2, max_tiles, st);
-  else err = run_mfma<MFMA_BM, 256, 2, 2, false, true>(g2, max_tiles, st);
+  if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, false, false, MFMA_PF>(g2, max_tiles, st);
+  else err = run_mfma<MFMA_BM, 256, 2, 2, false, true, MFMA_PF>(g2, max_tiles, st);
   if (err != hipSuccess) return err;
   return mark(2);
 }

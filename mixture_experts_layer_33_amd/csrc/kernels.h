@@ -8,7 +8,7 @@
 namespace moe {
 
 // router
-size_t route_workspace_bytes(int64_t T, int E);
+size_t route_workspace_bytes(int64_t T, int E, int d);
 hipError_t launch_route(const void* x, bool x_f32, const float* w_r, const float* b_r, int64_t T,
                         int d, int E, int k, float* logits, int32_t* topk_idx, float* topk_gate,
                         int32_t* expert_count, hipStream_t st);
