@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle expert work in the CPU baseline sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (reference for counter scaling)")
     return ap.parse_args()
 
 
@@ -293,6 +295,12 @@ def main():
         "timed_wall_s": round(wall, 3),
     }
     progress(f"forward {ms:.3f} ms/step, gate/up GEMM {g1:.3f} ms, down GEMM {g2:.3f} ms")
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_secondary:
         result["secondary"] = secondary(torch, moe, max(5, args.steps // 2))
     if not args.no_cpu_baseline:

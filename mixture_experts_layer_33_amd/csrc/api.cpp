@@ -161,6 +161,11 @@ int moe_combine(const moe_shape* s, const void* ring_y, const int32_t* copy_slot
   }
 }
 
+size_t moe_decode_flag_offset(const moe_shape* s) {
+  if (!s || check_shape(s) != MOE_OK) return 0;
+  return moe::decode_flag_offset((int)s->tokens, s->experts, s->top_k, s->ffn, s->shared_ffn);
+}
+
 int moe_decode(const moe_shape* s, const void* x, const float* w_router, const float* b_router,
                const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
                const void* ws_up, const void* ws_down, void* y, int32_t* topk_idx,
@@ -170,7 +175,8 @@ int moe_decode(const moe_shape* s, const void* x, const float* w_router, const f
     if (st) return st;
     if (s->dtype != MOE_BF16) return MOE_ERR_DTYPE;
     if (s->tokens < 1 || s->tokens > 8 || s->top_k > 16) return MOE_ERR_SHAPE;
-    if (s->hidden % 512 || s->ffn % 512 || s->shared_ffn % 512) return MOE_ERR_SHAPE;
+    if (s->hidden % 512 || s->ffn % 512 || s->hidden > 8192 || s->ffn > 4096) return MOE_ERR_SHAPE;
+    if (s->shared_ffn != 0 && s->shared_ffn != s->ffn) return MOE_ERR_SHAPE;
     if (!x || !w_router || !w_gate || !w_up || !w_down || !y || !topk_idx || !topk_gate ||
         !workspace)
       return MOE_ERR_NULL;

@@ -5,7 +5,7 @@
 // two kernels, and the staging buffers of the expert-centric scheme disappear.
 // On gfx950 the unit is a 64-lane wavefront owning a group of output elements.
 //
-// Kernel 1 (cooperative, persistent):
+// Kernel 1 (cooperative launch, every workgroup resident):
 //   A. router logits (one wavefront per expert row of W_r, all B tokens) and
 //      the shared expert's gate/up rows: hs[b][i] = silu(a) u, fp32;
 //   B. grid barrier;
@@ -21,19 +21,17 @@
 // h stays fp32 end to end (the page reports decode output closer to the fp32
 // reference).  Weight rows are read with 16-byte loads, one contiguous KB per
 // wavefront instruction.
-#include <hip/hip_cooperative_groups.h>
-
 #include "common.h"
 #include "kernels.h"
-
-namespace cg = cooperative_groups;
 
 namespace moe {
 
 constexpr int DEC_BMAX = 8;      // largest batch
 constexpr int DEC_KMAX = 16;     // largest top-k
-constexpr int DEC_THREADS = 512;
-constexpr int DEC_R = 8;         // output rows per wavefront in kernel 2
+constexpr int DEC_THREADS = 256;
+constexpr int DQ = 16;           // largest row, in groups of 512 elements (d <= 8192)
+constexpr int DEC_R = 4;         // output rows per wavefront in kernel 2
+constexpr int DEC_NF = 8;        // largest f (and fs) in groups of 512 in kernel 2
 
 struct DecodeArgs {
   const bf16_t* x;
@@ -50,40 +48,79 @@ struct DecodeArgs {
   float* hs;       // [B][fs]
   float* h;        // [B][k][f]
   int32_t* uniq;   // [DEC_BMAX*DEC_KMAX + 1]: selected experts ascending, then their count
+  uint32_t* sync;  // [0] arrivals at kernel 1's grid barrier, [1] sticky barrier time-out flag
   int32_t* topk_idx;
   float* topk_gate;
   bf16_t* y;
 };
 
-// dot of a bf16 weight row with the B tokens held in LDS (bf16), per-lane partials.
-// Lane handles elements q*512 + lane*8 + [0, 8).
-__device__ __forceinline__ void row_dots_bf16(const bf16_t* __restrict__ wrow,
-                                              const bf16_t* __restrict__ xs, int B, int d,
-                                              float* part) {
-  const int lane = threadIdx.x & 63;
-  for (int b = 0; b < DEC_BMAX; ++b) part[b] = 0.f;
-  for (int q = lane * 8; q < d; q += 512) {
-    const u32x4 w = *(const u32x4*)(wrow + q);
-    float wf[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) { wf[2 * r] = lo_bf(w[r]); wf[2 * r + 1] = hi_bf(w[r]); }
-#pragma unroll
-    for (int b = 0; b < DEC_BMAX; ++b) {
-      if (b >= B) break;
-      const u32x4 xv = *(const u32x4*)(xs + b * d + q);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        part[b] = fmaf(wf[2 * r], lo_bf(xv[r]), part[b]);
-        part[b] = fmaf(wf[2 * r + 1], hi_bf(xv[r]), part[b]);
+// Grid barrier of kernel 1.  Thread 0 of each workgroup publishes the
+// workgroup's writes (agent-scope release), counts itself in, and waits for all
+// workgroups with a bounded spin: if the count is not reached within about a
+// second the wait gives up and sets the sticky flag sync[1] (every wait ends).
+// Kernel 2 resets the counter for the next call; the workspace must be zero
+// before its first use.
+constexpr uint32_t DEC_SPIN_LIMIT = 1u << 22;
+
+__device__ __forceinline__ void grid_barrier(uint32_t* sync) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    atomicAdd(&sync[0], 1u);
+    uint32_t spins = 0;
+    while (__hip_atomic_load(&sync[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x) {
+      __builtin_amdgcn_s_sleep(8);
+      if (++spins > DEC_SPIN_LIMIT) {
+        atomicOr(&sync[1], 1u);
+        break;
       }
     }
+    __threadfence();
   }
+  __syncthreads();
 }
 
+// Lane `lane` owns elements c*512 + lane*8 + [0, 8) of a row, c < nq.  All loads
+// of a row are issued before any is used, so a wavefront keeps the whole row
+// (up to 16 KB) in flight.
+template <int NQ>
+__device__ __forceinline__ void load_row(const bf16_t* __restrict__ row, u32x4 (&w)[NQ]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int c = 0; c < NQ; ++c) w[c] = *(const u32x4*)(row + c * 512 + lane * 8);
+}
+
+// per-lane partial of <row, x_b> with x_b (bf16) in LDS
+template <int NQ>
+__device__ __forceinline__ float part_dot(const u32x4 (&w)[NQ], const bf16_t* __restrict__ xb) {
+  const int lane = threadIdx.x & 63;
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NQ; ++c) {
+    const u32x4 xv = *(const u32x4*)(xb + c * 512 + lane * 8);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s = fmaf(lo_bf(w[c][r]), lo_bf(xv[r]), s);
+      s = fmaf(hi_bf(w[c][r]), hi_bf(xv[r]), s);
+    }
+  }
+  return s;
+}
+
+// 64-bit masks of the (token, slot) pairs q = b*k + j whose expert is e (B*k <= 128)
+__device__ __forceinline__ void pairs_of(const int32_t* sel, int B, int k, int e,
+                                         unsigned long long& m0, unsigned long long& m1) {
+  const int lane = threadIdx.x & 63;
+  const int q0 = lane, q1 = lane + 64;
+  m0 = __ballot(q0 < B * k && sel[(q0 / k) * DEC_KMAX + q0 % k] == e);
+  m1 = __ballot(q1 < B * k && sel[(q1 / k) * DEC_KMAX + q1 % k] == e);
+}
+
+template <int NQ>   // d = NQ * 512
 __global__ __launch_bounds__(DEC_THREADS) void decode_k1(DecodeArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   bf16_t* xs = (bf16_t*)lds;                                   // [B][d]
-  int32_t* sel = (int32_t*)(lds + (size_t)p.B * p.d * 2);      // [B][k]
+  int32_t* sel = (int32_t*)(lds + (size_t)p.B * p.d * 2);      // [B][DEC_KMAX]
   int32_t* uniq = sel + DEC_BMAX * DEC_KMAX;                   // [<= B*k]
   int32_t* nuniq = uniq + DEC_BMAX * DEC_KMAX;
   uint32_t* bits = (uint32_t*)(nuniq + 1);                     // [E/32]
@@ -91,52 +128,54 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_k1(DecodeArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = tid >> 6, nwave = DEC_THREADS / 64;
   const int gw = blockIdx.x * nwave + wave, W = gridDim.x * nwave;
-  const int B = p.B, d = p.d, E = p.E, k = p.k, f = p.f, fs = p.fs;
+  const int B = p.B, E = p.E, k = p.k, f = p.f, fs = p.fs;
+  constexpr int d = NQ * 512;
 
   for (int v = tid; v < B * d / 8; v += DEC_THREADS) ((u32x4*)xs)[v] = ((const u32x4*)p.x)[v];
   __syncthreads();
 
-  // ---- A: router rows and shared gate/up rows
+  // ---- A: router rows (fp32) and shared gate/up rows, all B tokens each
   for (int item = gw; item < E + fs; item += W) {
-    float part[DEC_BMAX];
     if (item < E) {
       const float* wr = p.w_r + (int64_t)item * d;
-      for (int b = 0; b < DEC_BMAX; ++b) part[b] = 0.f;
-      for (int q = lane * 8; q < d; q += 512) {
-        const f32x4 w0 = *(const f32x4*)(wr + q), w1 = *(const f32x4*)(wr + q + 4);
+      f32x4 w0[NQ], w1[NQ];
 #pragma unroll
-        for (int b = 0; b < DEC_BMAX; ++b) {
-          if (b >= B) break;
-          const u32x4 xv = *(const u32x4*)(xs + b * d + q);
-          part[b] = fmaf(w0[0], lo_bf(xv[0]), part[b]);
-          part[b] = fmaf(w0[1], hi_bf(xv[0]), part[b]);
-          part[b] = fmaf(w0[2], lo_bf(xv[1]), part[b]);
-          part[b] = fmaf(w0[3], hi_bf(xv[1]), part[b]);
-          part[b] = fmaf(w1[0], lo_bf(xv[2]), part[b]);
-          part[b] = fmaf(w1[1], hi_bf(xv[2]), part[b]);
-          part[b] = fmaf(w1[2], lo_bf(xv[3]), part[b]);
-          part[b] = fmaf(w1[3], hi_bf(xv[3]), part[b]);
-        }
+      for (int c = 0; c < NQ; ++c) {
+        w0[c] = *(const f32x4*)(wr + c * 512 + lane * 8);
+        w1[c] = *(const f32x4*)(wr + c * 512 + lane * 8 + 4);
       }
       for (int b = 0; b < B; ++b) {
-        const float l = wave_sum(part[b]);
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) {
+          const u32x4 xv = *(const u32x4*)(xs + b * d + c * 512 + lane * 8);
+          s = fmaf(w0[c][0], lo_bf(xv[0]), s);
+          s = fmaf(w0[c][1], hi_bf(xv[0]), s);
+          s = fmaf(w0[c][2], lo_bf(xv[1]), s);
+          s = fmaf(w0[c][3], hi_bf(xv[1]), s);
+          s = fmaf(w1[c][0], lo_bf(xv[2]), s);
+          s = fmaf(w1[c][1], hi_bf(xv[2]), s);
+          s = fmaf(w1[c][2], lo_bf(xv[3]), s);
+          s = fmaf(w1[c][3], hi_bf(xv[3]), s);
+        }
+        const float l = wave_sum(s);
         if (lane == 0) p.logits[b * E + item] = l + (p.b_r ? p.b_r[item] : 0.f);
       }
     } else {
       const int i = item - E;
-      float pu[DEC_BMAX];
-      row_dots_bf16(p.ws_gate + (int64_t)i * d, xs, B, d, part);
-      row_dots_bf16(p.ws_up + (int64_t)i * d, xs, B, d, pu);
+      u32x4 wg[NQ], wu[NQ];
+      load_row<NQ>(p.ws_gate + (int64_t)i * d, wg);
+      load_row<NQ>(p.ws_up + (int64_t)i * d, wu);
       for (int b = 0; b < B; ++b) {
-        const float a = wave_sum(part[b]);
-        const float u = wave_sum(pu[b]);
+        const float a = wave_sum(part_dot<NQ>(wg, xs + b * d));
+        const float u = wave_sum(part_dot<NQ>(wu, xs + b * d));
         if (lane == 0) p.hs[b * fs + i] = silu(a) * u;
       }
     }
   }
 
   // ---- B: every workgroup waits for all logits
-  cg::this_grid().sync();
+  grid_barrier(p.sync);
 
   // ---- C: routing in LDS (one wavefront per token), then the selected experts' rows
   for (int b = wave; b < B; b += nwave) {
@@ -153,13 +192,15 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_k1(DecodeArgs p) {
   }
   for (int w = tid; w < (E + 31) / 32; w += DEC_THREADS) bits[w] = 0u;
   __syncthreads();
-  for (int q = tid; q < B * k; q += DEC_THREADS)
-    atomicOr(&bits[sel[(q / k) * DEC_KMAX + q % k] >> 5], 1u << (sel[(q / k) * DEC_KMAX + q % k] & 31));
+  for (int q = tid; q < B * k; q += DEC_THREADS) {
+    const int e = sel[(q / k) * DEC_KMAX + q % k];
+    atomicOr(&bits[e >> 5], 1u << (e & 31));
+  }
   __syncthreads();
   if (tid == 0) {
     int u = 0;
-    for (int e = 0; e < E; ++e)
-      if ((bits[e >> 5] >> (e & 31)) & 1u) uniq[u++] = e;
+    for (int w = 0; w < (E + 31) / 32; ++w)
+      for (uint32_t m = bits[w]; m; m &= m - 1) uniq[u++] = w * 32 + __builtin_ctz(m);
     *nuniq = u;
     if (blockIdx.x == 0) {       // the list kernel 2 reads
       for (int q = 0; q < u; ++q) p.uniq[q] = uniq[q];
@@ -170,20 +211,26 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_k1(DecodeArgs p) {
   const int U = *nuniq;
   for (int item = gw; item < U * f; item += W) {
     const int e = uniq[item / f], i = item % f;
-    float pa[DEC_BMAX], pu[DEC_BMAX];
-    row_dots_bf16(p.w_gate + ((int64_t)e * f + i) * d, xs, B, d, pa);
-    row_dots_bf16(p.w_up + ((int64_t)e * f + i) * d, xs, B, d, pu);
-    for (int b = 0; b < B; ++b) {
-      int j = -1;
-      for (int q = 0; q < k; ++q) j = sel[b * DEC_KMAX + q] == e ? q : j;
-      if (j < 0) continue;                 // uniform across the wave
-      const float a = wave_sum(pa[b]);
-      const float u = wave_sum(pu[b]);
-      if (lane == 0) p.h[((int64_t)b * k + j) * f + i] = silu(a) * u;
-    }
+    u32x4 wg[NQ], wu[NQ];
+    load_row<NQ>(p.w_gate + ((int64_t)e * f + i) * d, wg);
+    load_row<NQ>(p.w_up + ((int64_t)e * f + i) * d, wu);
+    unsigned long long m0, m1;
+    pairs_of(sel, B, k, e, m0, m1);
+    for (int half = 0; half < 2; ++half)
+      for (unsigned long long m = half ? m1 : m0; m; m &= m - 1) {
+        const int q = half * 64 + __builtin_ctzll(m), b = q / k, j = q % k;
+        const float a = wave_sum(part_dot<NQ>(wg, xs + b * d));
+        const float u = wave_sum(part_dot<NQ>(wu, xs + b * d));
+        if (lane == 0) p.h[((int64_t)b * k + j) * f + i] = silu(a) * u;
+      }
   }
 }
 
+// Kernel 2: a wavefront owns DEC_R output rows.  For every selected expert (then
+// the shared one) it issues the loads of its DEC_R W_down rows at once, and adds
+// g * <row, h> for each token that chose the expert into per-lane partials;
+// one fixed-order wave reduction per (row, token) at the end.
+template <int NF>   // f = fs (when present) = NF * 512
 __global__ __launch_bounds__(256) void decode_k2(DecodeArgs p) {
   __shared__ int32_t sel[DEC_BMAX * DEC_KMAX];
   __shared__ float gate[DEC_BMAX * DEC_KMAX];
@@ -191,12 +238,19 @@ __global__ __launch_bounds__(256) void decode_k2(DecodeArgs p) {
   __shared__ int32_t nuniq;
   const int tid = threadIdx.x, lane = tid & 63;
   const int B = p.B, d = p.d, k = p.k, f = p.f, fs = p.fs;
-  for (int q = tid; q < B * k; q += 256) {
-    sel[q] = p.topk_idx[q];
-    gate[q] = p.topk_gate[q];
+  (void)f;
+  for (int q = tid; q < DEC_BMAX * DEC_KMAX; q += 256) {
+    sel[q] = -1;
+    gate[q] = 0.f;
     uniq[q] = p.uniq[q];
   }
   if (tid == 0) nuniq = p.uniq[DEC_BMAX * DEC_KMAX];
+  if (blockIdx.x == 0 && tid == 0) p.sync[0] = 0u;   // kernel 1 has finished: re-arm its barrier
+  __syncthreads();
+  for (int q = tid; q < B * k; q += 256) {   // b < B <= 8, j < k <= 16: index < 128
+    sel[(q / k) * DEC_KMAX + q % k] = p.topk_idx[q];
+    gate[(q / k) * DEC_KMAX + q % k] = p.topk_gate[q];
+  }
   __syncthreads();
   const int o0 = (blockIdx.x * 4 + (tid >> 6)) * DEC_R;
   if (o0 >= d) return;
@@ -211,48 +265,49 @@ __global__ __launch_bounds__(256) void decode_k2(DecodeArgs p) {
     const bool shared = ui == U;
     if (shared && fs == 0) break;
     const int e = shared ? -1 : uniq[ui];
-    const int ff = shared ? fs : f;
-    const bf16_t* wbase = shared ? p.ws_down : p.w_down + (int64_t)e * d * f;
-    for (int q0 = 0; q0 < ff; q0 += 512) {
-      const int q = q0 + lane * 8;
-      const bool ok = q < ff;
-      float w[DEC_R][8];
+    constexpr int ff = NF * 512;
+    const bf16_t* wbase = shared ? p.ws_down : p.w_down + (int64_t)e * d * ff;
+    u32x4 w[DEC_R][NF];
 #pragma unroll
-      for (int r = 0; r < DEC_R; ++r) {
-        const int o = min(o0 + r, d - 1);
-        const u32x4 v = ok ? *(const u32x4*)(wbase + (int64_t)o * ff + q) : u32x4{0, 0, 0, 0};
+    for (int r = 0; r < DEC_R; ++r) {
+      const int o = min(o0 + r, d - 1);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) { w[r][2 * c] = lo_bf(v[c]); w[r][2 * c + 1] = hi_bf(v[c]); }
-      }
-#pragma unroll
-      for (int b = 0; b < DEC_BMAX; ++b) {
-        if (b >= B) break;
-        int j = -1;
-        float g = 1.f;
-        if (!shared) {
-          for (int qq = 0; qq < k; ++qq)
-            if (sel[b * k + qq] == e) { j = qq; g = gate[b * k + qq]; }
-          if (j < 0) continue;
-        }
-        const float* hv = shared ? p.hs + (int64_t)b * fs : p.h + ((int64_t)b * k + j) * f;
-        float hh[8];
-        if (ok) {
-          const f32x4 h0 = *(const f32x4*)(hv + q), h1 = *(const f32x4*)(hv + q + 4);
-          hh[0] = h0[0]; hh[1] = h0[1]; hh[2] = h0[2]; hh[3] = h0[3];
-          hh[4] = h1[0]; hh[5] = h1[1]; hh[6] = h1[2]; hh[7] = h1[3];
-        } else {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) hh[c] = 0.f;
-        }
-#pragma unroll
-        for (int r = 0; r < DEC_R; ++r) {
-          float s = 0.f;
-#pragma unroll
-          for (int c = 0; c < 8; ++c) s = fmaf(w[r][c], hh[c], s);
-          acc[r][b] = fmaf(g, s, acc[r][b]);
-        }
-      }
+      for (int c = 0; c < NF; ++c)
+        w[r][c] = *(const u32x4*)(wbase + (int64_t)o * ff + c * 512 + lane * 8);
     }
+    unsigned long long m0 = 0, m1 = 0;
+    if (shared) m0 = B >= 64 ? ~0ull : ((1ull << B) - 1);   // bit b: token b, weight 1
+    else pairs_of(sel, B, k, e, m0, m1);
+    for (int half = 0; half < 2; ++half)
+      for (unsigned long long m = half ? m1 : m0; m; m &= m - 1) {
+        const int q = half * 64 + __builtin_ctzll(m);
+        const int b = shared ? q : q / k, j = shared ? 0 : q % k;
+        const float g = shared ? 1.f : gate[b * DEC_KMAX + j];
+        const float* hv = shared ? p.hs + (int64_t)b * fs : p.h + ((int64_t)b * k + j) * f;
+        float s[DEC_R] = {};
+#pragma unroll
+        for (int c = 0; c < NF; ++c) {
+          const f32x4 h0 = *(const f32x4*)(hv + c * 512 + lane * 8);
+          const f32x4 h1 = *(const f32x4*)(hv + c * 512 + lane * 8 + 4);
+#pragma unroll
+          for (int r = 0; r < DEC_R; ++r) {
+            s[r] = fmaf(lo_bf(w[r][c][0]), h0[0], s[r]);
+            s[r] = fmaf(hi_bf(w[r][c][0]), h0[1], s[r]);
+            s[r] = fmaf(lo_bf(w[r][c][1]), h0[2], s[r]);
+            s[r] = fmaf(hi_bf(w[r][c][1]), h0[3], s[r]);
+            s[r] = fmaf(lo_bf(w[r][c][2]), h1[0], s[r]);
+            s[r] = fmaf(hi_bf(w[r][c][2]), h1[1], s[r]);
+            s[r] = fmaf(lo_bf(w[r][c][3]), h1[2], s[r]);
+            s[r] = fmaf(hi_bf(w[r][c][3]), h1[3], s[r]);
+          }
+        }
+        // add into the accumulator of token b (static index for the registers)
+#pragma unroll
+        for (int bb = 0; bb < DEC_BMAX; ++bb)
+          if (bb == b)
+#pragma unroll
+            for (int r = 0; r < DEC_R; ++r) acc[r][bb] = fmaf(g, s[r], acc[r][bb]);
+      }
   }
 #pragma unroll
   for (int r = 0; r < DEC_R; ++r)
@@ -264,9 +319,19 @@ __global__ __launch_bounds__(256) void decode_k2(DecodeArgs p) {
     }
 }
 
-size_t decode_workspace_bytes(int B, int E, int k, int f, int fs) {
+// Workspace: logits [B,E] f32 | shared h [B,max(fs,1)] f32 | h [B,k,f] f32 |
+// unique-expert list [DEC_BMAX*DEC_KMAX + 1] i32 | barrier counter u32 | time-out flag u32.
+static size_t decode_sync_offset(int B, int E, int k, int f, int fs) {
   return ((size_t)B * E + (size_t)B * (fs > 0 ? fs : 1) + (size_t)B * k * f) * sizeof(float) +
          (DEC_BMAX * DEC_KMAX + 1) * sizeof(int32_t);
+}
+
+size_t decode_workspace_bytes(int B, int E, int k, int f, int fs) {
+  return decode_sync_offset(B, E, k, f, fs) + 2 * sizeof(uint32_t);
+}
+
+size_t decode_flag_offset(int B, int E, int k, int f, int fs) {
+  return decode_sync_offset(B, E, k, f, fs) + sizeof(uint32_t);
 }
 
 hipError_t launch_decode(const void* x, const float* w_r, const float* b_r, const void* w_gate,
@@ -274,7 +339,8 @@ hipError_t launch_decode(const void* x, const float* w_r, const float* b_r, cons
                          const void* ws_up, const void* ws_down, int B, int d, int E, int k,
                          int f, int fs, void* y, int32_t* topk_idx, float* topk_gate, void* ws,
                          hipStream_t st) {
-  if (B > DEC_BMAX || k > DEC_KMAX || d % 512 != 0 || f % 512 != 0 || (fs && fs % 512 != 0))
+  if (B > DEC_BMAX || k > DEC_KMAX || d % 512 != 0 || f % 512 != 0 || (fs && fs != f) ||
+      d > DQ * 512 || f > DEC_NF * 512)
     return hipErrorInvalidValue;
   DecodeArgs a;
   a.x = (const bf16_t*)x;
@@ -291,29 +357,48 @@ hipError_t launch_decode(const void* x, const float* w_r, const float* b_r, cons
   a.hs = a.logits + (size_t)B * E;
   a.h = a.hs + (size_t)B * (fs > 0 ? fs : 1);
   a.uniq = (int32_t*)(a.h + (size_t)B * k * f);
+  a.sync = (uint32_t*)((char*)ws + decode_sync_offset(B, E, k, f, fs));
   a.topk_idx = topk_idx;
   a.topk_gate = topk_gate;
   a.y = (bf16_t*)y;
 
+  const void* k1 = nullptr;
+  switch (d / 512) {
+#define K1_CASE(n) case n: k1 = (const void*)decode_k1<n>; break;
+    K1_CASE(1) K1_CASE(2) K1_CASE(3) K1_CASE(4) K1_CASE(5) K1_CASE(6) K1_CASE(7) K1_CASE(8)
+    K1_CASE(9) K1_CASE(10) K1_CASE(11) K1_CASE(12) K1_CASE(13) K1_CASE(14) K1_CASE(15) K1_CASE(16)
+#undef K1_CASE
+    default: return hipErrorInvalidValue;
+  }
   const size_t lds = (size_t)B * d * 2 + (2 * DEC_BMAX * DEC_KMAX + 1) * 4 + ((E + 31) / 32) * 4;
   int dev = 0, ncu = 0, per_cu = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
-  err = hipFuncSetAttribute((const void*)decode_k1, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds);
+  err = hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
-  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_k1, DEC_THREADS, lds);
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k1, DEC_THREADS, lds);
   if (err != hipSuccess) return err;
   if (per_cu < 1) return hipErrorInvalidConfiguration;
-  const int grid = ncu * per_cu;   // every workgroup resident: the grid barrier cannot stall
+  // at most 2 workgroups per CU: well inside the residency limit the cooperative
+  // launch checks, and enough wavefronts to keep every row's loads in flight
+  const int grid = ncu * (per_cu < 2 ? per_cu : 2);
   void* kargs[] = {&a};
-  err = hipLaunchCooperativeKernel((const void*)decode_k1, dim3(grid), dim3(DEC_THREADS), kargs,
-                                   (unsigned)lds, st);
+  err = hipLaunchCooperativeKernel(k1, dim3(grid), dim3(DEC_THREADS), kargs, (unsigned)lds, st);
   if (err != hipSuccess) return err;
-  const int waves = (d + DEC_R - 1) / DEC_R;
-  decode_k2<<<(waves + 3) / 4, 256, 0, st>>>(a);
+  const unsigned g2 = (unsigned)(((d + DEC_R - 1) / DEC_R + 3) / 4);
+  switch (f / 512) {
+    case 1: decode_k2<1><<<g2, 256, 0, st>>>(a); break;
+    case 2: decode_k2<2><<<g2, 256, 0, st>>>(a); break;
+    case 3: decode_k2<3><<<g2, 256, 0, st>>>(a); break;
+    case 4: decode_k2<4><<<g2, 256, 0, st>>>(a); break;
+    case 5: decode_k2<5><<<g2, 256, 0, st>>>(a); break;
+    case 6: decode_k2<6><<<g2, 256, 0, st>>>(a); break;
+    case 7: decode_k2<7><<<g2, 256, 0, st>>>(a); break;
+    case 8: decode_k2<8><<<g2, 256, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

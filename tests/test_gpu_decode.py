@@ -18,6 +18,7 @@ def check_decode(cfg, reps=5):
     y, idx, gate = layer.decode(inp.x, inp.w_router, inp.b_router, inp.w_gate, inp.w_up,
                                 inp.w_down, inp.ws_gate, inp.ws_up, inp.ws_down)
     torch.cuda.synchronize()
+    assert not layer.decode_barrier_timed_out(), "decode grid barrier timed out"
     x = to_oracle(inp.x)
     w_r = to_oracle(inp.w_router)
     b = None if inp.b_router is None else to_oracle(inp.b_router)
@@ -36,13 +37,14 @@ def check_decode(cfg, reps=5):
                                        inp.w_down, inp.ws_gate, inp.ws_up, inp.ws_down)
         torch.cuda.synchronize()
         assert torch.equal(y2, y0) and torch.equal(idx2, idx)
+    assert not layer.decode_barrier_timed_out(), "decode grid barrier timed out"
     return err
 
 
 @pytest.mark.parametrize("cfg", [
     LayerConfig("dec_small_b3", T=3, d=1024, E=32, k=4, f=512, fs=512, cid=40),
     LayerConfig("dec_small_b8_noshared", T=8, d=512, E=64, k=8, f=1024, fs=0, cid=41),
-    LayerConfig("dec_small_b5_bias", T=5, d=1536, E=48, k=6, f=512, fs=1024, zipf_s=1.1,
+    LayerConfig("dec_small_b5_bias", T=5, d=1536, E=48, k=6, f=512, fs=512, zipf_s=1.1,
                 hot_ratio=4.0, cid=42),
 ], ids=lambda c: c.name)
 def test_decode_small(cfg):
