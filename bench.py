@@ -107,9 +107,11 @@ def expert_bytes(counts, d, f, elem_bytes, scale_bytes_per_elem=0.0):
 
 
 def cpu_baseline(inp, cfg, budget_s):
-    """The oracle on the host: router, dispatch and combine over all tokens, the expert
-    FFN on a sample of experts (ascending id) until `budget_s` seconds of expert work;
-    the full-layer time is extrapolated by the sampled share of token copies."""
+    """The oracle on the host over the whole layer: router, dispatch, ring fill, the expert
+    FFN of every expert (ascending id) and combine.  When one pass is short, each step is
+    repeated `reps` times so that about `budget_s` seconds of oracle work are timed; when it
+    is long, experts are sampled in ascending id until the budget and the expert time is
+    extrapolated by the sampled share of token copies."""
     import numpy as np
     import oracle
     from gen import bits16
@@ -124,32 +126,46 @@ def cpu_baseline(inp, cfg, budget_s):
     r = oracle.route(x, w_r, None, cfg.k)
     disp = oracle.dispatch(r.idx, cfg.E, cfg.C, 0)
     ring = oracle.ring_fill(x, disp)
-    t_fixed = time.perf_counter() - t0
+    t_fixed1 = time.perf_counter() - t0
     ring_y = np.zeros((cfg.C, cfg.d))
-    t_exp, rows, sampled = 0.0, 0, 0
+    t_exp, rows, sampled, reps = 0.0, 0, 0, None
     for e in range(cfg.E):
         slots = oracle.segment_slots(disp, e)
         if slots.size == 0:
             continue
         w = tuple(oracle.from_bf16_bits(bits16(t[e])) for t in (inp.w_gate, inp.w_up, inp.w_down))
+        if reps is None:   # size the repetition count from the first expert's cost
+            t1 = time.perf_counter()
+            oracle.swiglu(ring[slots], *w)
+            probe = (time.perf_counter() - t1) * cfg.n / slots.size + t_fixed1
+            reps = int(max(1, min(20, budget_s // max(probe, 1e-9))))
         if sampled % 8 == 0:
-            progress(f"oracle expert {e}: {t_exp:.1f} s of expert work so far")
+            progress(f"oracle expert {e}: {t_exp:.1f} s of expert work so far ({reps} reps)")
         t1 = time.perf_counter()
-        ring_y[slots] = oracle.swiglu(ring[slots], *w)
+        for _ in range(reps):
+            ring_y[slots] = oracle.swiglu(ring[slots], *w)
         t_exp += time.perf_counter() - t1
         rows += slots.size
         sampled += 1
         if t_exp >= budget_s:
             break
+    reps = reps or 1
     t2 = time.perf_counter()
-    oracle.combine(ring_y, disp.copy_slot, r.gate)
-    t_fixed += time.perf_counter() - t2
+    for i in range(reps):
+        if i:   # the router, dispatch and ring fill again, once per extra repetition
+            r = oracle.route(x, w_r, None, cfg.k)
+            disp = oracle.dispatch(r.idx, cfg.E, cfg.C, 0)
+            ring = oracle.ring_fill(x, disp)
+        oracle.combine(ring_y, disp.copy_slot, r.gate)
+    t_fixed = t_fixed1 + time.perf_counter() - t2
     est = t_fixed + t_exp * (cfg.n / rows)
-    return {"value": round(cfg.T / est, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"fp64 numpy oracle: router, dispatch, ring fill and combine over all "
-                       f"{cfg.T} tokens ({t_fixed:.2f} s); expert SwiGLU on {sampled} of {cfg.E} "
-                       f"experts ({rows} of {cfg.n} copies, {t_exp:.2f} s), full layer "
-                       f"extrapolated by the copy share to {est:.1f} s")}
+    return {"value": round(reps * cfg.T / est, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"fp64 numpy oracle, {reps} repetition(s) of each step: router, dispatch, "
+                       f"ring fill and combine over all {cfg.T} tokens ({t_fixed:.2f} s); expert "
+                       f"SwiGLU on {sampled} of {cfg.E} experts ({rows} of {cfg.n} copies, "
+                       f"{t_exp:.2f} s); {reps} full layer(s) "
+                       + ("timed" if rows == cfg.n else "extrapolated by the copy share")
+                       + f" in {est:.1f} s")}
 
 
 def secondary(torch, moe, steps):
