@@ -29,7 +29,11 @@ FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", INCLUDE, 
          "-Wno-unused-command-line-argument",
          # m0 is set inside the asm that issues global->LDS copies; no compiler code
          # in these kernels keeps a value in m0 across them
-         "-Wno-inline-asm"]
+         "-Wno-inline-asm",
+         # fully unroll the GEMM epilogues (256 accumulators per lane in the largest
+         # tile); a partly unrolled loop would index the accumulators dynamically and
+         # move them to scratch memory
+         "-mllvm", "-pragma-unroll-threshold=262144"]
 
 
 def _compile(src: str) -> str:

@@ -16,6 +16,7 @@
 // Paths: bf16 MFMA (v_mfma_f32_32x32x16_bf16), MX fp8 MFMA
 // (v_mfma_scale_f32_32x32x64_f8f6f4: E4M3 operands, one E8M0 scale per 32 K),
 // and an fp32 VALU path for fp32 layers.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -57,18 +58,26 @@ hipError_t launch_build_tiles(const int32_t* expert_offset, int E, int BM, int32
 }
 
 // ============================================================ bf16 / MX MFMA GEMM
-// Workgroup tile BM x BN, K staged in 128-byte row slices (64 bf16 or 128 fp8)
-// through double-buffered LDS.  16-byte chunks of a row are XOR-swizzled by
-// (row & 7) so that the fragment reads of 8 consecutive rows hit distinct
-// banks.  4 waves in a WM x WN grid; each wave owns FM x FN 32x32 fragments.
+// Workgroup tile BM x BN, K staged in KB-byte row slices (KB = 128: 64 bf16 or
+// 128 fp8; KB = 64: 32 bf16) through an S-stage LDS ring.  4 waves in a WM x WN
+// grid; each wave owns FM x FN 32x32 fragments.
 //
 // SWIGLU: the B tile stacks BN/2 rows of W_gate over the same BN/2 rows of
 // W_up, and every wave holds matching gate and up fragments, so the epilogue
 // forms h = silu(a) * u in registers.
-constexpr int KBYTES = 128;            // bytes of K per row per stage
-constexpr int CHUNKS = KBYTES / 16;    // 16-byte chunks per row slice
-
-__device__ __forceinline__ int swz(int r, int c) { return r * KBYTES + ((c ^ (r & 7)) << 4); }
+//
+// LDS serves a 128-bit read in groups of 8 lanes (128 bytes per clock); a
+// fragment read has lanes 0..7 on 8 consecutive rows at the same logical 16-byte
+// chunk.  The chunks of a row are XOR-swizzled so that those 8 reads hit 8
+// distinct 16-byte bank groups: by (row & 7) for 128-byte rows, by
+// ((row >> 1) & 3) for 64-byte rows (two rows share a 128-byte bank line).
+// Both were measured conflict-free (the same rate as contiguous addresses).
+template <int KB>
+__device__ __forceinline__ int swz(int r, int c) {
+  static_assert(KB == 128 || KB == 64, "row slice");
+  if constexpr (KB == 128) return r * 128 + ((c ^ (r & 7)) << 4);
+  else return r * 64 + ((c ^ ((r >> 1) & 3)) << 4);
+}
 
 struct GemmArgs {
   const uint8_t* A;        // ring rows [C, K] (bf16 or E4M3)
@@ -122,27 +131,43 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Stage layout in LDS: A tile [BM][128 B] | B tile [BN][128 B] | MX: A scale dwords,
+// Stage layout in LDS: A tile [BM][KB] | B tile [BN][KB] | MX: A scale dwords,
 // one private copy of [BM] per wave | B scale dwords [BN].  S stages form a ring.
-template <int BM, int BN, bool MX>
+template <int BM, int BN, int KB, bool MX>
 struct StageLayout {
   static constexpr int A = 0;
-  static constexpr int B = BM * KBYTES;
-  static constexpr int ASC = B + BN * KBYTES;
+  static constexpr int B = BM * KB;
+  static constexpr int ASC = B + BN * KB;
   static constexpr int BSC = ASC + (MX ? 4 * BM * 4 : 0);
   static constexpr int SIZE = BSC + (MX ? BN * 4 : 0);
 };
 
-template <int BM, int BN, int WM, int WN, bool SWIGLU, bool MX, int S>
+// Epilogue staging in LDS: the output tile row-major, OUTC columns of OEB bytes,
+// rows padded by 16 bytes (the two row groups a fragment store touches then fall on
+// different banks).  CPR 16-byte pieces per row.
+template <int BM, int BN, bool SWIGLU, bool MX>
+struct EpiLayout {
+  static constexpr int OUTC = SWIGLU ? BN / 2 : BN;
+  static constexpr int OEB = (SWIGLU && MX) ? 1 : 2;
+  static constexpr int RS = OUTC * OEB + 16;
+  static constexpr int CPR = OUTC * OEB / 16;
+  static constexpr int SIZE = BM * RS;
+};
+
+template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S>
 __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
   constexpr int EB = MX ? 1 : 2;                 // element bytes
   constexpr int WTM = BM / WM, WTN = BN / WN;    // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  using SL = StageLayout<BM, BN, MX>;
-  constexpr int NA = BM * KBYTES / 4096, NB = BN * KBYTES / 4096;   // 1 KB copies per wave
+  constexpr int CH = KB / 16;                    // 16-byte chunks per row slice
+  constexpr int RPC = 64 / CH;                   // rows per 1 KB copy
+  using SL = StageLayout<BM, BN, KB, MX>;
+  constexpr int NA = BM * KB / 4096, NB = BN * KB / 4096;   // 1 KB copies per wave
   constexpr int NASC = MX ? BM * 4 / 256 : 0, NBSC = MX ? BN * 4 / 1024 : 0;
   constexpr int L = NA + NB + NASC + NBSC;       // copies per wave per stage
-  static_assert(BM * KBYTES % 4096 == 0 && BN * KBYTES % 4096 == 0, "tile / wave mismatch");
+  static_assert(BM * KB % 4096 == 0 && BN * KB % 4096 == 0, "tile / wave mismatch");
+  static_assert(!MX || KB == 128, "MX stages hold whole 128-element scale groups");
+  static_assert(WM * WN == 4, "four waves");
   static_assert(!MX || (BM * 4 % 256 == 0 && BN * 4 % 1024 == 0), "scale copies");
   static_assert(!SWIGLU || (FN % 2 == 0), "gate/up fragments come in pairs");
   static_assert(S >= 2 && S <= 4, "stages");
@@ -167,21 +192,24 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
   const uint32_t Ks = (uint32_t)p.K / 32;                 // MX scale bytes per row
 
   // Copy i of this wave fills 16-byte chunks j = (4 i + wave) * 64 + lane of a tile:
-  // row j / 8, swizzled slot j % 8, which holds global chunk (slot ^ (row & 7)).
+  // row j / CH, slot j % CH, which holds the global chunk whose swizzled slot it is
+  // (the swizzle is an involution on the chunk index: swz(r, c) - r * KB = 16 * slot).
   uint32_t a_off[NA], b_off[NB];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int j = (4 * i + wave) * 64 + lane, r = j >> 3, c = (j & 7) ^ (r & 7);
+    const int j = (4 * i + wave) * 64 + lane, r = j / CH;
+    const int c = (swz<KB>(r, j % CH) - r * KB) >> 4;
     const int64_t sl = ring_slot(p.head, seg, row0 + min(r, rows - 1), p.C);
     a_off[i] = (uint32_t)sl * Kb + c * 16;
   }
   // B rows: SWIGLU stacks BN/2 rows of W_gate over BN/2 rows of W_up; a copy covers
-  // 8 rows, so each copy reads from a single matrix (decided by its first row).
+  // RPC rows, so each copy reads from a single matrix (decided by its first row).
   const uint8_t* b_base[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int j = (4 * i + wave) * 64 + lane, r = j >> 3, c = (j & 7) ^ (r & 7);
-    const bool up = SWIGLU && (4 * i + wave) * 8 >= BN / 2;
+    const int j = (4 * i + wave) * 64 + lane, r = j / CH;
+    const int c = (swz<KB>(r, j % CH) - r * KB) >> 4;
+    const bool up = SWIGLU && (4 * i + wave) * RPC >= BN / 2;
     const int rr = up ? r - BN / 2 : r;
     b_base[i] = (up ? p.B1 : p.B0) + (int64_t)e * p.N * Kb;
     b_off[i] = (uint32_t)min(n0 + rr, p.N - 1) * Kb + c * 16;
@@ -203,24 +231,27 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
       bsc_off[i] = (uint32_t)min(n0 + rr, p.N - 1) * Ks;
     }
   }
-  auto issue = [&](int kt) __attribute__((always_inline)) {
+  // Copy c (0 <= c < L) of this wave for K step kt, into ring buffer kt % S.
+  auto issue_one = [&](int kt, int c) __attribute__((always_inline)) {
     const uint32_t st = lds0 + (uint32_t)(kt % S) * SL::SIZE;
-#pragma unroll
-    for (int i = 0; i < NA; ++i)
-      dma16(p.A + (size_t)kt * KBYTES, a_off[i], __builtin_amdgcn_readfirstlane(st + SL::A + (4 * i + wave) * 1024));
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-      dma16(b_base[i] + (size_t)kt * KBYTES, b_off[i], __builtin_amdgcn_readfirstlane(st + SL::B + (4 * i + wave) * 1024));
-    if (MX) {
-#pragma unroll
-      for (int i = 0; i < NASC; ++i)
-        dma4(p.A_scale + (size_t)kt * 4, asc_off[i],
-             __builtin_amdgcn_readfirstlane(st + SL::ASC + wave * BM * 4 + i * 256));
-#pragma unroll
-      for (int i = 0; i < NBSC; ++i)
-        dma4(bsc_base[i] + (size_t)kt * 4, bsc_off[i],
-             __builtin_amdgcn_readfirstlane(st + SL::BSC + (4 * i + wave) * 256));
+    if (c < NA) {
+      dma16(p.A + (size_t)kt * KB, a_off[c], __builtin_amdgcn_readfirstlane(st + SL::A + (4 * c + wave) * 1024));
+    } else if (c < NA + NB) {
+      const int i = c - NA;
+      dma16(b_base[i] + (size_t)kt * KB, b_off[i], __builtin_amdgcn_readfirstlane(st + SL::B + (4 * i + wave) * 1024));
+    } else if (c < NA + NB + NASC) {
+      const int i = c - NA - NB;
+      dma4(p.A_scale + (size_t)kt * 4, asc_off[i],
+           __builtin_amdgcn_readfirstlane(st + SL::ASC + wave * BM * 4 + i * 256));
+    } else {
+      const int i = c - NA - NB - NASC;
+      dma4(bsc_base[i] + (size_t)kt * 4, bsc_off[i],
+           __builtin_amdgcn_readfirstlane(st + SL::BSC + (4 * i + wave) * 256));
     }
+  };
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < L; ++c) issue_one(kt, c);
   };
   // wait until this wave's copies of the stage issued `later` stages before the
   // newest one have landed
@@ -250,68 +281,71 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int lr = lane & 31, lg = lane >> 5;
-  auto compute = [&](int buf) __attribute__((always_inline)) {
-    const uint8_t* as = lds + buf * SL::SIZE + SL::A;
-    const uint8_t* bs = lds + buf * SL::SIZE + SL::B;
+  // One stage: KK sub-steps of FM x FN MFMAs.  The schedule is fixed by hand (the
+  // compiler would otherwise group all memory instructions at the start): the
+  // fragments of sub-step kk + 1 are read between the MFMAs of sub-step kk, and the
+  // L copies of the stage `next` (the one that will be computed S - 1 stages later;
+  // negative for none) are spread evenly over all MFMAs of the stage.  A wave
+  // issues in order, so a copy placed after an MFMA is handed to the memory
+  // pipeline while the MFMA executes instead of before all of them.
+  constexpr int KK = MX ? KB / 128 * 2 : KB / 32;   // sub-steps per stage
+  constexpr int NMF = KK * FM * FN;                  // MFMAs per stage
+  using Frag = std::conditional_t<MX, i32x8, bf16x8>;
+  Frag af[2][FM], bfr[2][FN];
+  int sa[2][FM], sb[2][FN];
+  auto stage_ptrs = [&](int buf, const uint8_t*& as, const uint8_t*& bs, const uint32_t*& asc,
+                        const uint32_t*& bsc) __attribute__((always_inline)) {
+    as = lds + buf * SL::SIZE + SL::A;
+    bs = lds + buf * SL::SIZE + SL::B;
+    asc = (const uint32_t*)(lds + buf * SL::SIZE + SL::ASC) + wave * BM;
+    bsc = (const uint32_t*)(lds + buf * SL::SIZE + SL::BSC);
+  };
+  // fragment q of sub-step kk of ring buffer buf into register set `set`: q < FM is
+  // A fragment q, else B fragment q - FM
+  auto read = [&](int buf, int kk, int q, int set) __attribute__((always_inline)) {
+    const uint8_t *as, *bs;
+    const uint32_t *asc, *bsc;
+    stage_ptrs(buf, as, bs, asc, bsc);
+    const bool isa = q < FM;
+    const int r = isa ? wm * WTM + q * 32 + lr : brow(q - FM) + lr;
+    const uint8_t* base = isa ? as : bs;
     if constexpr (!MX) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {           // 4 x 16 K per stage
-        const int c = kk * 2 + lg;
-        bf16x8 af[FM], bfr[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int r = wm * WTM + i * 32 + lr;
-          af[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(as + swz(r, c)));
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int r = brow(j) + lr;
-          bfr[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(bs + swz(r, c)));
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
+      const bf16x8 v = __builtin_bit_cast(bf16x8, *(const u32x4*)(base + swz<KB>(r, kk * 2 + lg)));
+      if (isa) af[set][q] = v; else bfr[set][q - FM] = v;
     } else {
-      const uint32_t* asc = (const uint32_t*)(lds + buf * SL::SIZE + SL::ASC) + wave * BM;
-      const uint32_t* bsc = (const uint32_t*)(lds + buf * SL::SIZE + SL::BSC);
       // Operand layout of the 32x32x64 E4M3 MFMA: of a lane's 32 bytes, bytes
       // 0-15 belong to the first 32-element scale block of the 64-wide K step and
       // bytes 16-31 to the second; lane group g (= lane / 32) holds elements
       // [16g, 16g + 16) of each block and supplies the scale of block g.
+      const int ca = kk * 4 + lg, cb = kk * 4 + 2 + lg;
+      const int blk = kk * 2 + lg;             // its scale byte inside the row's dword
+      const u32x4 lo = *(const u32x4*)(base + swz<KB>(r, ca));
+      const u32x4 hi = *(const u32x4*)(base + swz<KB>(r, cb));
+      const i32x8 v = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      const int sc = (int)(((isa ? asc : bsc)[r] >> (8 * blk)) & 0xffu);
+      if (isa) { af[set][q] = v; sa[set][q] = sc; }
+      else { bfr[set][q - FM] = v; sb[set][q - FM] = sc; }
+    }
+  };
+  // The FM x FN MFMAs of one sub-step on register set `set`, with interleaved work:
+  // the FM + FN fragment reads of (rbuf, rkk) into set ^ 1 (rbuf < 0: none), and the
+  // copies [c0, c1) of K step `next` (next < 0: none) spread evenly.
+  auto substep = [&](int set, int rbuf, int rkk, int next, int c0, int c1)
+      __attribute__((always_inline)) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {           // 2 x 64 K per stage
-        const int ca = kk * 4 + lg, cb = kk * 4 + 2 + lg;   // 16-byte chunks of this lane
-        const int blk = kk * 2 + lg;             // its scale byte inside the row's dword
-        i32x8 af[FM], bfr[FN];
-        int sa[FM], sb[FN];
+    for (int m = 0; m < FM * FN; ++m) {
+      const int i = m / FN, j = m % FN;
+      if constexpr (!MX)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[set][i], bfr[set][j], acc[i][j], 0, 0, 0);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            af[set][i], bfr[set][j], acc[i][j], 0, 0, 0, sa[set][i], 0, sb[set][j]);
+      if (rbuf >= 0 && m < FM + FN) read(rbuf, rkk, m, set ^ 1);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int r = wm * WTM + i * 32 + lr;
-          const u32x4 lo = *(const u32x4*)(as + swz(r, ca));
-          const u32x4 hi = *(const u32x4*)(as + swz(r, cb));
-          af[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          sa[i] = (int)((asc[r] >> (8 * blk)) & 0xffu);
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int r = brow(j) + lr;
-          const u32x4 lo = *(const u32x4*)(bs + swz(r, ca));
-          const u32x4 hi = *(const u32x4*)(bs + swz(r, cb));
-          bfr[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          sb[j] = (int)((bsc[r] >> (8 * blk)) & 0xffu);
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[i], bfr[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
-      }
+      for (int c = c0; c < c1; ++c)   // copy c goes after MFMA number floor((c - c0) * FM * FN / (c1 - c0))
+        if ((c - c0) * FM * FN / (c1 - c0) == m && next >= 0) issue_one(next, c);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -319,72 +353,125 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
   // One barrier per stage: it publishes stage kt (every wave waited for its own
   // copies) and retires the buffer of stage kt-1, which the copies of stage kt+S-1
   // then overwrite.
-  const int KT = (int)(Kb / KBYTES);
+  const int KT = (int)(Kb / KB);
   for (int s = 0; s < S - 1 && s < KT; ++s) issue(s);
-  for (int kt = 0; kt < KT; ++kt) {
-    wait_stage(min(S - 2, KT - 1 - kt));
+  if constexpr (S < 4) {
+    // Barrier at the start of each stage; the stage's copies (K step kt + S - 1)
+    // spread over all its MFMAs.
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_stage(min(S - 2, KT - 1 - kt));
+      __syncthreads();
+      const int buf = kt % S, next = kt + S - 1 < KT ? kt + S - 1 : -1;
+#pragma unroll
+      for (int q = 0; q < FM + FN; ++q) read(buf, 0, q, 0);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        substep(kk & 1, kk + 1 < KK ? buf : -1, kk + 1, next, kk * L / KK, (kk + 1) * L / KK);
+    }
+  } else {
+    // Barrier before the last sub-step of each stage: the next stage is waited for
+    // and published there, so its first fragments are read while the last MFMAs of
+    // this stage run (no exposed LDS latency at stage starts), and the buffer it
+    // frees (stage kt - 1, finished by every wave) takes the copies of K step
+    // kt + S - 1 during that last sub-step.
+    static_assert(KK % 2 == 0, "sub-step 0 of every stage uses register set 0");
+    wait_stage(min(S - 2, KT - 1));
     __syncthreads();
-    if (kt + S - 1 < KT) issue(kt + S - 1);
-    compute(kt % S);
+#pragma unroll
+    for (int q = 0; q < FM + FN; ++q) read(0, 0, q, 0);
+    for (int kt = 0; kt < KT; ++kt) {
+      const int buf = kt % S;
+#pragma unroll
+      for (int kk = 0; kk + 1 < KK; ++kk) substep(kk & 1, buf, kk + 1, -1, 0, 0);
+      const bool more = kt + 1 < KT;
+      if (more) {
+        wait_stage(min(kt + S - 2, KT - 1) - (kt + 1));
+        __syncthreads();
+      }
+      substep((KK - 1) & 1, more ? (kt + 1) % S : -1, 0, kt + S - 1 < KT ? kt + S - 1 : -1, 0, L);
+    }
   }
   __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
   // acc register r of a 32x32 fragment: row 8*(r/4) + 4*(lane/32) + r%4, column lane%32.
-  if (SWIGLU) {
+  // The output tile is staged row-major in LDS (the ring is idle now: every copy has
+  // landed and the barrier below retires the last reads) and written out as whole
+  // 16-byte pieces of rows, instead of 2-byte stores scattered over rows.
+  using EL = EpiLayout<BM, BN, SWIGLU, MX>;
+  uint8_t* stg = lds;
+  __syncthreads();
+  // Copy the staged plane to dst (row pitch `pitch` bytes, tile columns from byte
+  // col0b); rows beyond the segment and columns beyond N are not written.
+  auto flush = [&](uint8_t* dst, int64_t pitch, int col0b, int rowb) __attribute__((always_inline)) {
+    __syncthreads();
+#pragma unroll 4
+    for (int q = tid; q < BM * EL::CPR; q += 256) {
+      const int m = q / EL::CPR, cb = (q % EL::CPR) * 16;
+      if (m < rows && col0b + cb < rowb) {
+        const int64_t sl = ring_slot(p.head, seg, row0 + m, p.C);
+        *(u32x4*)(dst + sl * pitch + col0b + cb) = *(const u32x4*)(stg + m * EL::RS + cb);
+      }
+    }
+    __syncthreads();
+  };
+  if constexpr (SWIGLU) {
     constexpr int HALF = FN / 2;
+    // plane 0: h = silu(a) * u (bf16, or E4M3 codes with per-32 scales); with saved
+    // A|U, planes 1 and 2 hold a and u in bf16
+    const int nplanes = (!MX && p.saved_au) ? 3 : 1;
+    for (int plane = 0; plane < nplanes; ++plane) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < HALF; ++j) {
-        const int col = n0 + wn * (WTN / 2) + j * 32 + lr;   // f index
+        for (int j = 0; j < HALF; ++j) {
+          const int cl = wn * (WTN / 2) + j * 32 + lr;   // column inside the tile
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = wm * WTM + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-          const float a = acc[i][j][r], u = acc[i][j + HALF][r];
-          const float h = silu(a) * u;
-          const bool live = m < rows && col < p.N;
-          const int64_t s = ring_slot(p.head, seg, row0 + min(m, rows - 1), p.C);
-          if (MX) {
-            // the 32 columns of one row's block sit in the 32 lanes of a half-wave
-            const float am = group_max<32>(fabsf(h));
-            const int X = mx_block_exp(am);
-            if (live) {
-              p.out[s * p.N + col] = (uint8_t)e4m3_encode(h, X);
-              if (lr == 0) p.out_scale[s * (p.N / 32) + col / 32] = (uint8_t)(X + 127);
-            }
-          } else if (live) {
-            ((uint16_t*)p.out)[s * p.N + col] = f2bf(h);
-            if (p.saved_au) {
-              p.saved_au[s * 2 * p.N + col] = f2bf(a);
-              p.saved_au[s * 2 * p.N + p.N + col] = f2bf(u);
+          for (int r = 0; r < 16; ++r) {
+            const int m = wm * WTM + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+            const float a = acc[i][j][r], u = acc[i][j + HALF][r];
+            if constexpr (MX) {
+              const float h = silu(a) * u;
+              // the 32 columns of one row's block sit in the 32 lanes of a half-wave
+              const float am = group_max<32>(fabsf(h));
+              const int X = mx_block_exp(am);
+              stg[m * EL::RS + cl] = (uint8_t)e4m3_encode(h, X);
+              const int col = n0 + cl;
+              if (lr == 0 && m < rows && col < p.N)
+                p.out_scale[ring_slot(p.head, seg, row0 + m, p.C) * (p.N / 32) + col / 32] =
+                    (uint8_t)(X + 127);
+            } else {
+              const float v = plane == 0 ? silu(a) * u : plane == 1 ? a : u;
+              *(uint16_t*)(stg + m * EL::RS + cl * 2) = f2bf(v);
             }
           }
         }
-      }
+      if (plane == 0) flush(p.out, (int64_t)p.N * EL::OEB, n0 * EL::OEB, p.N * EL::OEB);
+      else flush((uint8_t*)p.saved_au + (plane == 2 ? (int64_t)p.N * 2 : 0), (int64_t)p.N * 4,
+                 n0 * 2, p.N * 2);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * WTN + j * 32 + lr;
+        const int cl = wn * WTN + j * 32 + lr;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = wm * WTM + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-          if (m < rows && col < p.N) {
-            const int64_t s = ring_slot(p.head, seg, row0 + m, p.C);
-            ((uint16_t*)p.out)[s * p.N + col] = f2bf(acc[i][j][r]);
-          }
+          *(uint16_t*)(stg + m * EL::RS + cl * 2) = f2bf(acc[i][j][r]);
         }
       }
+    flush(p.out, (int64_t)p.N * 2, n0 * 2, p.N * 2);
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool SWIGLU, bool MX, int S>
+template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S>
 static hipError_t run_mfma(const GemmArgs& a, int max_tiles, hipStream_t st) {
   const int nt = SWIGLU ? (a.N + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
-  const size_t lds = (size_t)S * StageLayout<BM, BN, MX>::SIZE;
-  auto kern = gg_mfma_kernel<BM, BN, WM, WN, SWIGLU, MX, S>;
+  const size_t lds = std::max<size_t>((size_t)S * StageLayout<BM, BN, KB, MX>::SIZE,
+                                      EpiLayout<BM, BN, SWIGLU, MX>::SIZE);
+  auto kern = gg_mfma_kernel<BM, BN, WM, WN, KB, SWIGLU, MX, S>;
   static bool attr_set = false;   // opt in to more than 64 KB of LDS once per process
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute((const void*)kern,
@@ -469,17 +556,27 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
 }
 
 // ============================================================ launcher
-// Row-tile height of the MFMA paths and the fp32 path.
-constexpr int MFMA_BM = 128;
-#ifndef MOE_MFMA_STAGES
-#define MOE_MFMA_STAGES 3
-#endif
-constexpr int MFMA_PF = MOE_MFMA_STAGES;   // LDS ring stages of the grouped GEMMs
+// Two bf16 MFMA tile shapes.
+//  * 128 x 256, 128-byte K slices, 3 stages: one row tile holds every row of an
+//    expert with up to 128 rows, so each weight is read from HBM once; the
+//    2,048-token layer (64 rows per expert on average) is bound by that stream.
+//  * 256 x 256, 64-byte K slices, 4 stages (128 KB), 128 x 128 per wave: with
+//    many rows per expert every row tile re-reads the weights and the kernel is
+//    bound inside the CU.  Per 32-wide K stage a SIMD runs 32 MFMAs (1024 clocks)
+//    while LDS serves 64 KB of fragment reads and 32 KB of copies (768 clocks at
+//    128 B/clock); the 128 x 256 tile needs 1152 LDS clocks per 1024 MFMA clocks.
+// MX keeps the first shape (its stages hold whole 128-element scale groups).
+constexpr int MFMA_BM = 128, MFMA_BM_BIG = 256;
+constexpr int BIG_ROWS_MIN = 256;   // mean rows per expert from which the 256-row tile is used
+
+static bool use_big(int dtype, int64_t n, int E) {
+  return dtype == 1 && n >= (int64_t)BIG_ROWS_MIN * E;
+}
 
 static int max_tiles_for(int64_t n, int E, int BM) { return (int)((n + BM - 1) / BM) + E; }
 
 size_t ffn_workspace_bytes(int64_t n, int64_t C, int d, int E, int f, int dtype) {
-  const int BM = dtype == 0 ? FT_M : MFMA_BM;
+  const int BM = dtype == 0 ? FT_M : MFMA_BM;   // the larger count of the two MFMA shapes
   size_t b = (size_t)(2 * max_tiles_for(n, E, BM) + 64) * sizeof(int32_t);
   b = (b + 255) & ~(size_t)255;
   if (dtype == 0) b += (size_t)C * f * 4;                       // H fp32
@@ -494,7 +591,8 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
                       const uint8_t* wg_scale, const uint8_t* wu_scale, const uint8_t* wd_scale,
                       void* ring_y, void* saved_au, void* ws, hipEvent_t* events,
                       hipStream_t st) {
-  const int BM = dtype == 0 ? FT_M : MFMA_BM;
+  const bool big = use_big(dtype, n, E);
+  const int BM = dtype == 0 ? FT_M : big ? MFMA_BM_BIG : MFMA_BM;
   const int max_tiles = max_tiles_for(n, E, BM);
   int32_t* ntiles = (int32_t*)ws;
   int32_t* tiles = ntiles + 64;
@@ -547,11 +645,13 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
   g2.out = (uint8_t*)ring_y;
   g2.out_scale = nullptr;
   g2.saved_au = nullptr;
-  if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, true, false, MFMA_PF>(g1, max_tiles, st);
-  else err = run_mfma<MFMA_BM, 256, 2, 2, true, true, MFMA_PF>(g1, max_tiles, st);
+  if (big) err = run_mfma<MFMA_BM_BIG, 256, 2, 2, 64, true, false, 4>(g1, max_tiles, st);
+  else if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, 128, true, false, 3>(g1, max_tiles, st);
+  else err = run_mfma<MFMA_BM, 256, 2, 2, 128, true, true, 3>(g1, max_tiles, st);
   if (err != hipSuccess || (err = mark(1)) != hipSuccess) return err;
-  if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, false, false, MFMA_PF>(g2, max_tiles, st);
-  else err = run_mfma<MFMA_BM, 256, 2, 2, false, true, MFMA_PF>(g2, max_tiles, st);
+  if (big) err = run_mfma<MFMA_BM_BIG, 256, 2, 2, 64, false, false, 4>(g2, max_tiles, st);
+  else if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, 128, false, false, 3>(g2, max_tiles, st);
+  else err = run_mfma<MFMA_BM, 256, 2, 2, 128, false, true, 3>(g2, max_tiles, st);
   if (err != hipSuccess) return err;
   return mark(2);
 }

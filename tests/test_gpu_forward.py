@@ -9,7 +9,8 @@ import torch
 
 import mixture_experts_layer_33_amd as moe
 import oracle
-from gen import FWD_BF16, FWD_MXFP8, SKEW_BWD, TINY_F32, LayerConfig, make_layer
+from gen import (FWD_BF16, FWD_MXFP8, SHARE_BF16, SHARE_MXFP8, SKEW_BWD, TINY_F32, LayerConfig,
+                 make_layer, make_share)
 from layer_util import LazyWeights, rel, to_oracle
 
 pytestmark = pytest.mark.gpu
@@ -30,6 +31,13 @@ MEDIUM = [
     LayerConfig("med_mx", T=300, d=256, E=16, k=4, f=256, dtype="mxfp8", cid=34),
     LayerConfig("med_mx_skew", T=400, d=384, E=24, k=3, f=128, dtype="mxfp8", zipf_s=1.1,
                 hot_ratio=6.0, cid=35),
+    # more than 96 rows per expert on average: the 128-row tile shape (the cases above
+    # take the 64-row one); ragged last row tiles
+    LayerConfig("med_bf16_bigtile", T=600, d=320, E=8, k=2, f=192, cid=36),
+    LayerConfig("med_mx_bigtile", T=700, d=256, E=6, k=2, f=256, dtype="mxfp8", cid=37),
+    # at least 256 rows per expert on average: the bf16 256 x 256 tile with 64-byte K
+    # slices; ragged in rows, columns and K
+    LayerConfig("med_bf16_big256", T=1100, d=320, E=8, k=2, f=192, cid=38),
 ]
 
 
@@ -177,3 +185,41 @@ def test_forward_full_size_sampled(cfg):
     assert torch.equal(again["ring_y"][sl], out["ring_y"][sl])
     del layer, inp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("scfg", [SHARE_BF16, SHARE_MXFP8], ids=lambda c: c.name)
+def test_share_shape_sampled(scfg):
+    """The grouped GEMMs at one GPU's expert-parallel share (4 experts x 16,384 rows),
+    in the launch configuration the benchmark times; sampled rows of every expert."""
+    print(f"\n[case] share-shape expert FFN {scfg.name}", flush=True)
+    sh = make_share(scfg, DEV)
+    mx = scfg.dtype == "mxfp8"
+    shape = moe.make_shape(scfg.rows, scfg.d, scfg.E, 1, scfg.f, scfg.C, dtype=scfg.dtype)
+    off = torch.tensor(np.concatenate([[0], np.cumsum(sh.counts)]), dtype=torch.int32, device=DEV)
+    ws = moe.workspace(shape, moe.OP_EXPERT_FFN, DEV)
+    ring_y = torch.empty((scfg.C, scfg.d), dtype=torch.bfloat16, device=DEV)
+    if mx:
+        xq, xs = moe.quantize_mx(sh.ring_x)
+        q = [moe.quantize_mx(w) for w in (sh.w_gate, sh.w_up, sh.w_down)]
+        wargs = [c for c, _ in q] + [s for _, s in q]
+    else:
+        xq, xs, q = sh.ring_x, None, None
+        wargs = [sh.w_gate, sh.w_up, sh.w_down, None, None, None]
+    moe.moe_expert_ffn(shape, xq, xs, off, 0, *wargs, ring_y, None, ws)
+    torch.cuda.synchronize()
+    lw = LazyWeights(sh.w_gate, sh.w_up, sh.w_down, mx_codes=tuple(q) if mx else None)
+    rng = np.random.default_rng(1)
+    offs = off.cpu().numpy()
+    for e in range(scfg.E):
+        rows = np.sort(rng.choice(np.arange(offs[e], offs[e + 1]), 6, replace=False))
+        rows = np.unique(np.concatenate([rows, [offs[e], offs[e + 1] - 1]]))
+        x = to_oracle(sh.ring_x[torch.from_numpy(rows).to(DEV)])
+        xe = oracle.mx.fake_quant(x, axis=1) if mx else x
+        ref = oracle.swiglu(xe, *lw(e), h_mx=mx)
+        err = rel(to_oracle(ring_y[torch.from_numpy(rows).to(DEV)]), ref)
+        print(f"  expert {e}: rows {rows.tolist()} max-abs-rel {err:.3e}", flush=True)
+        assert err <= TOL[scfg.dtype]
+    again = torch.empty_like(ring_y)
+    moe.moe_expert_ffn(shape, xq, xs, off, 0, *wargs, again, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(again[: scfg.rows], ring_y[: scfg.rows])
