@@ -185,16 +185,18 @@ def secondary(torch, moe, steps):
         for _ in range(3):
             layer.decode(*args)
         torch.cuda.synchronize()
+        # a decode call is short: time many back-to-back calls (about 0.1-0.5 s)
+        calls = max(100, 10 * steps)
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
-        for _ in range(steps):
+        for _ in range(calls):
             layer.decode(*args)
         e.record()
         torch.cuda.synchronize()
-        us = s.elapsed_time(e) * 1e3 / steps
+        us = s.elapsed_time(e) * 1e3 / calls
         U = int(np.unique(layer.bufs["topk_idx"].cpu().numpy()).size)
         nbytes = (U + 1) * 3 * cfg.f * cfg.d * 2 + cfg.E * cfg.d * 4 + 2 * B * cfg.d * 2
-        dec[f"B{B}"] = {"us_per_call": round(us, 2), "us_per_token": round(us / B, 2),
+        dec[f"B{B}"] = {"calls": calls, "us_per_call": round(us, 2), "us_per_token": round(us / B, 2),
                         "unique_experts": U, "alg_bytes": nbytes,
                         "GBps": round(nbytes / us / 1e3, 1),
                         "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}

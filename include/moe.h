@@ -164,9 +164,10 @@ int moe_combine(const moe_shape* shape, const void* ring_y, const int32_t* copy_
 
 /*
  * moe_decode: small-batch decode parallelised over outputs, in two kernels and
- * with no permuted buffer (toolnavs.com warp-decode page, "1.84x plus de vitesse…").
- * Kernel 1: router and shared-expert gate/up, a grid barrier, then each
- * wavefront streams rows of W_gate/W_up of the experts the batch selected and
+ * with no permuted buffer (toolnavs.com warp-decode page, "1.84x plus de vitesse…"),
+ * after a router kernel that writes the fp32 logits.  Kernel 1: the routing (rebuilt
+ * in every workgroup), then each wavefront streams rows of W_gate/W_up of the shared
+ * expert and of the experts the batch selected and
  * writes h = silu(a) * u in fp32, token-major.  Kernel 2: each wavefront owns a
  * group of output rows, streams W_down rows of every selected expert and of the
  * shared expert, and writes y = sum_j g_j (W_down h_j) + W_s_down h_s in bf16.
@@ -174,14 +175,9 @@ int moe_combine(const moe_shape* shape, const void* ring_y, const int32_t* copy_
  *      w_gate/w_up/w_down bf16, shared ws_gate/ws_up [fs,d], ws_down [d,fs] bf16
  *      or NULL when shape->shared_ffn == 0.
  * Out: y [B,d] bf16, topk_idx [B,k], topk_gate [B,k].
- * workspace: moe_workspace_bytes(shape, MOE_OP_DECODE) bytes, zero-filled before its first
- * decode call; each call leaves it ready for the next.  Calls sharing one workspace must
- * be ordered (one stream).  MOE_BF16 only; d a multiple of 512 up to 8192, f a multiple of
- * 512 up to 4096, shared_ffn 0 or equal to f (MOE_ERR_SHAPE otherwise).
- * Kernel 1's grid barrier waits a bounded time: should it ever give up (only possible if
- * the runtime did not keep every workgroup resident), the kernel finishes, the results
- * are not valid, and a nonzero 32-bit word is left at byte moe_decode_flag_offset(shape)
- * of the workspace.  The flag is sticky until the caller clears it.
+ * workspace: moe_workspace_bytes(shape, MOE_OP_DECODE) bytes (no initial contents needed).
+ * MOE_BF16 only; d a multiple of 512 up to 8192, f a multiple of 512 up to 4096,
+ * shared_ffn 0 or equal to f (MOE_ERR_SHAPE otherwise).
  */
 int moe_decode(const moe_shape* shape, const void* x, const float* w_router,
                const float* b_router, const void* w_gate, const void* w_up,
@@ -213,10 +209,6 @@ int moe_backward(const moe_shape* shape, const void* dy, const void* x,
                  const void* w_gate, const void* w_up, const void* w_down,
                  void* dx, void* dw_gate, void* dw_up, void* dw_down, float* dw_router,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
-
-/* Byte offset in the decode workspace of the barrier time-out flag (0 for an invalid
- * shape).  Host only, no GPU call. */
-size_t moe_decode_flag_offset(const moe_shape* shape);
 
 /* Bytes of workspace `op` needs for `shape` (0 if none).  Host only, no GPU call. */
 size_t moe_workspace_bytes(const moe_shape* shape, int op);

@@ -216,14 +216,6 @@ class Layer:
                    gate, self._ws(OP_DECODE))
         return y, idx, gate
 
-    def decode_barrier_timed_out(self) -> bool:
-        """True if a decode grid barrier in this layer's workspace ever gave up waiting."""
-        ws = self.bufs.get(f"ws{OP_DECODE}")
-        if ws is None:
-            return False
-        off = int(lib().moe_decode_flag_offset(self.shape))
-        return bool(ws[off:off + 4].view(torch.int32).item())
-
     def backward(self, dy, x, w_router, w_gate, w_up, w_down, head=0):
         """Gradients after a forward(..., save_au=True) with the same buffers."""
         s = self.shape

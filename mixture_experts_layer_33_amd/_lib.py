@@ -36,11 +36,10 @@ SIGNATURES = {
     "moe_decode": [SHP, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_backward": [SHP, P, P, P, P, P, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_workspace_bytes": [SHP, C.c_int],
-    "moe_decode_flag_offset": [SHP],
     "moe_status_string": [C.c_int],
     "moe_quantize_mx": [P, I64, I64, P, P, P],
 }
-_RESTYPE = {"moe_workspace_bytes": SZ, "moe_decode_flag_offset": SZ, "moe_status_string": C.c_char_p}
+_RESTYPE = {"moe_workspace_bytes": SZ, "moe_status_string": C.c_char_p}
 
 _lib = None
 

@@ -161,11 +161,6 @@ int moe_combine(const moe_shape* s, const void* ring_y, const int32_t* copy_slot
   }
 }
 
-size_t moe_decode_flag_offset(const moe_shape* s) {
-  if (!s || check_shape(s) != MOE_OK) return 0;
-  return moe::decode_flag_offset((int)s->tokens, s->experts, s->top_k, s->ffn, s->shared_ffn);
-}
-
 int moe_decode(const moe_shape* s, const void* x, const float* w_router, const float* b_router,
                const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
                const void* ws_up, const void* ws_down, void* y, int32_t* topk_idx,

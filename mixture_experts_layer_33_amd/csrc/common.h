@@ -70,16 +70,16 @@ __device__ __forceinline__ float group_max(float v) {
 // ties to the lower expert id.  On return lane r < k holds the r-th selected
 // expert (`choice`), its rank in ascending expert order (`rank`) and its
 // renormalised gate p / sum_S p with p = exp(l - max) / sum_e exp(l - max).
-template <int VPL>
-__device__ __forceinline__ void wave_route_row(const float* __restrict__ l, int E, int k,
-                                               int& choice, int& rank, float& gate) {
+template <int VPL, typename LogitF>
+__device__ __forceinline__ void wave_route_row_f(LogitF logit, int E, int k, int& choice, int& rank,
+                                                 float& gate) {
   const int lane = threadIdx.x & 63;
   float v[VPL];
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? l[e] : -INFINITY;
+    v[i] = e < E ? logit(e) : -INFINITY;
     m = fmaxf(m, v[i]);
   }
   m = wave_max(m);
@@ -115,6 +115,12 @@ __device__ __forceinline__ void wave_route_row(const float* __restrict__ l, int 
   rank = 0;
   for (int i = 0; i < k; ++i) rank += (__shfl(choice, i, 64) < choice) ? 1 : 0;
   gate = p / ps;
+}
+
+template <int VPL>
+__device__ __forceinline__ void wave_route_row(const float* __restrict__ l, int E, int k,
+                                               int& choice, int& rank, float& gate) {
+  wave_route_row_f<VPL>([&](int e) { return l[e]; }, E, k, choice, rank, gate);
 }
 
 // ---------------------------------------------------------------- MX / E4M3

@@ -1,18 +1,19 @@
-// Small-batch decode in two kernels, parallel over outputs, with no permuted
+// Small-batch decode: the router, then two kernels parallel over outputs, with no permuted
 // token buffer.  The warp-decode page (toolnavs.com, sections "Cursor a réécrit
 // le décodage de MoE" and "1.84x plus de vitesse…") turns the parallel axis from
 // experts to outputs: each unit of work owns output values, the layer runs in
 // two kernels, and the staging buffers of the expert-centric scheme disappear.
 // On gfx950 the unit is a 64-lane wavefront owning a group of output elements.
 //
-// Kernel 1 (cooperative launch, every workgroup resident):
-//   A. router logits (one wavefront per expert row of W_r, all B tokens) and
-//      the shared expert's gate/up rows: hs[b][i] = silu(a) u, fp32;
-//   B. grid barrier;
-//   C. every workgroup rebuilds top-k and gates from the logits, and the list of
-//      experts the batch selected; one wavefront per (expert, row i) streams the
-//      W_gate and W_up rows once and writes h[b][j][i] = silu(a) u (fp32,
-//      token-major) for every token b that chose that expert as its j-th.
+// Kernel 0: the router logits, quarter rows of W_r (fp32) per wavefront, all B
+//   tokens each, the four partial sums kept apart (no cross-workgroup sync: the
+//   next launch consumes them).
+// Kernel 1: every workgroup rebuilds top-k and gates from the logits
+//   (((p0 + p1) + p2) + p3 + bias) and the list of experts the batch selected; then
+//   one wavefront per row streams the shared expert's gate/up rows,
+//   hs[b][i] = silu(a) u, and the selected experts' rows (expert, row i): the
+//   W_gate and W_up rows are read once and h[b][j][i] = silu(a) u (fp32,
+//   token-major) is written for every token b that chose that expert as its j-th.
 // Kernel 2: one wavefront per group of DEC_R output rows o streams W_down[e][o,:]
 //   of every selected expert and W_s_down[o,:], and writes
 //   y[b][o] = sum_j g[b][j] (W_down[e_bj][o,:] . h[b][j]) + W_s_down[o,:] . hs[b]
@@ -28,7 +29,8 @@ namespace moe {
 
 constexpr int DEC_BMAX = 8;      // largest batch
 constexpr int DEC_KMAX = 16;     // largest top-k
-constexpr int DEC_THREADS = 256;
+constexpr int DEC_THREADS = 512; // kernel 1: 8 wavefronts share the token rows in LDS
+constexpr int DEC_RP = 4;        // router row parts (kernel 0)
 constexpr int DQ = 16;           // largest row, in groups of 512 elements (d <= 8192)
 constexpr int DEC_R = 4;         // output rows per wavefront in kernel 2
 constexpr int DEC_NF = 8;        // largest f (and fs) in groups of 512 in kernel 2
@@ -44,41 +46,14 @@ struct DecodeArgs {
   const bf16_t* ws_up;
   const bf16_t* ws_down;
   int B, d, E, k, f, fs;
-  float* logits;   // [B][E]
+  float* logits;   // [DEC_RP][B][E]: the partial logits of the quarters of each W_r row
   float* hs;       // [B][fs]
   float* h;        // [B][k][f]
   int32_t* uniq;   // [DEC_BMAX*DEC_KMAX + 1]: selected experts ascending, then their count
-  uint32_t* sync;  // [0] arrivals at kernel 1's grid barrier, [1] sticky barrier time-out flag
   int32_t* topk_idx;
   float* topk_gate;
   bf16_t* y;
 };
-
-// Grid barrier of kernel 1.  Thread 0 of each workgroup publishes the
-// workgroup's writes (agent-scope release), counts itself in, and waits for all
-// workgroups with a bounded spin: if the count is not reached within about a
-// second the wait gives up and sets the sticky flag sync[1] (every wait ends).
-// Kernel 2 resets the counter for the next call; the workspace must be zero
-// before its first use.
-constexpr uint32_t DEC_SPIN_LIMIT = 1u << 22;
-
-__device__ __forceinline__ void grid_barrier(uint32_t* sync) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    atomicAdd(&sync[0], 1u);
-    uint32_t spins = 0;
-    while (__hip_atomic_load(&sync[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x) {
-      __builtin_amdgcn_s_sleep(8);
-      if (++spins > DEC_SPIN_LIMIT) {
-        atomicOr(&sync[1], 1u);
-        break;
-      }
-    }
-    __threadfence();
-  }
-  __syncthreads();
-}
 
 // Lane `lane` owns elements c*512 + lane*8 + [0, 8) of a row, c < nq.  All loads
 // of a row are issued before any is used, so a wavefront keeps the whole row
@@ -107,6 +82,27 @@ __device__ __forceinline__ float part_dot(const u32x4 (&w)[NQ], const bf16_t* __
   return s;
 }
 
+// per-lane partials of <gate row, x_b> and <up row, x_b>, each chunk of x_b read once
+template <int NQ>
+__device__ __forceinline__ void part_dot2(const u32x4 (&wg)[NQ], const u32x4 (&wu)[NQ],
+                                          const bf16_t* __restrict__ xb, float& sa, float& su) {
+  const int lane = threadIdx.x & 63;
+  sa = 0.f;
+  su = 0.f;
+#pragma unroll
+  for (int c = 0; c < NQ; ++c) {
+    const u32x4 xv = *(const u32x4*)(xb + c * 512 + lane * 8);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x0 = lo_bf(xv[r]), x1 = hi_bf(xv[r]);
+      sa = fmaf(lo_bf(wg[c][r]), x0, sa);
+      sa = fmaf(hi_bf(wg[c][r]), x1, sa);
+      su = fmaf(lo_bf(wu[c][r]), x0, su);
+      su = fmaf(hi_bf(wu[c][r]), x1, su);
+    }
+  }
+}
+
 // 64-bit masks of the (token, slot) pairs q = b*k + j whose expert is e (B*k <= 128)
 __device__ __forceinline__ void pairs_of(const int32_t* sel, int B, int k, int e,
                                          unsigned long long& m0, unsigned long long& m1) {
@@ -114,6 +110,47 @@ __device__ __forceinline__ void pairs_of(const int32_t* sel, int B, int k, int e
   const int q0 = lane, q1 = lane + 64;
   m0 = __ballot(q0 < B * k && sel[(q0 / k) * DEC_KMAX + q0 % k] == e);
   m1 = __ballot(q1 < B * k && sel[(q1 / k) * DEC_KMAX + q1 % k] == e);
+}
+
+// Kernel 0: wavefront w computes part w % DEC_RP of W_r row w / DEC_RP: chunks
+// [p QC, min(NQ, (p + 1) QC)) (loads past the end repeat the last chunk and are not
+// used; an empty part contributes 0).  x is read through the cache (B d bf16).
+template <int NQ>   // d = NQ * 512
+__global__ __launch_bounds__(256) void decode_router(DecodeArgs p) {
+  constexpr int d = NQ * 512;
+  constexpr int QC = (NQ + DEC_RP - 1) / DEC_RP;
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int B = p.B, E = p.E;
+  if (item >= DEC_RP * E) return;
+  const int e = item / DEC_RP, part = item % DEC_RP;
+  const int c0 = part * QC, nc = min(NQ - c0, QC);
+  const float* wr = p.w_r + (int64_t)e * d;
+  f32x4 w0[QC], w1[QC];
+#pragma unroll
+  for (int c = 0; c < QC; ++c) {
+    const int cc = min(c0 + c, NQ - 1);
+    w0[c] = *(const f32x4*)(wr + cc * 512 + lane * 8);
+    w1[c] = *(const f32x4*)(wr + cc * 512 + lane * 8 + 4);
+  }
+  for (int b = 0; b < B; ++b) {
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < QC; ++c) {
+      if (c >= nc) break;
+      const u32x4 xv = *(const u32x4*)(p.x + (int64_t)b * d + (c0 + c) * 512 + lane * 8);
+      s = fmaf(w0[c][0], lo_bf(xv[0]), s);
+      s = fmaf(w0[c][1], hi_bf(xv[0]), s);
+      s = fmaf(w0[c][2], lo_bf(xv[1]), s);
+      s = fmaf(w0[c][3], hi_bf(xv[1]), s);
+      s = fmaf(w1[c][0], lo_bf(xv[2]), s);
+      s = fmaf(w1[c][1], hi_bf(xv[2]), s);
+      s = fmaf(w1[c][2], lo_bf(xv[3]), s);
+      s = fmaf(w1[c][3], hi_bf(xv[3]), s);
+    }
+    const float l = wave_sum(s);
+    if (lane == 0) p.logits[((int64_t)part * B + b) * E + e] = l;
+  }
 }
 
 template <int NQ>   // d = NQ * 512
@@ -126,62 +163,23 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_k1(DecodeArgs p) {
   uint32_t* bits = (uint32_t*)(nuniq + 1);                     // [E/32]
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = tid >> 6, nwave = DEC_THREADS / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), nwave = DEC_THREADS / 64;
   const int gw = blockIdx.x * nwave + wave, W = gridDim.x * nwave;
   const int B = p.B, E = p.E, k = p.k, f = p.f, fs = p.fs;
   constexpr int d = NQ * 512;
 
   for (int v = tid; v < B * d / 8; v += DEC_THREADS) ((u32x4*)xs)[v] = ((const u32x4*)p.x)[v];
-  __syncthreads();
-
-  // ---- A: router rows (fp32) and shared gate/up rows, all B tokens each
-  for (int item = gw; item < E + fs; item += W) {
-    if (item < E) {
-      const float* wr = p.w_r + (int64_t)item * d;
-      f32x4 w0[NQ], w1[NQ];
-#pragma unroll
-      for (int c = 0; c < NQ; ++c) {
-        w0[c] = *(const f32x4*)(wr + c * 512 + lane * 8);
-        w1[c] = *(const f32x4*)(wr + c * 512 + lane * 8 + 4);
-      }
-      for (int b = 0; b < B; ++b) {
-        float s = 0.f;
-#pragma unroll
-        for (int c = 0; c < NQ; ++c) {
-          const u32x4 xv = *(const u32x4*)(xs + b * d + c * 512 + lane * 8);
-          s = fmaf(w0[c][0], lo_bf(xv[0]), s);
-          s = fmaf(w0[c][1], hi_bf(xv[0]), s);
-          s = fmaf(w0[c][2], lo_bf(xv[1]), s);
-          s = fmaf(w0[c][3], hi_bf(xv[1]), s);
-          s = fmaf(w1[c][0], lo_bf(xv[2]), s);
-          s = fmaf(w1[c][1], hi_bf(xv[2]), s);
-          s = fmaf(w1[c][2], lo_bf(xv[3]), s);
-          s = fmaf(w1[c][3], hi_bf(xv[3]), s);
-        }
-        const float l = wave_sum(s);
-        if (lane == 0) p.logits[b * E + item] = l + (p.b_r ? p.b_r[item] : 0.f);
-      }
-    } else {
-      const int i = item - E;
-      u32x4 wg[NQ], wu[NQ];
-      load_row<NQ>(p.ws_gate + (int64_t)i * d, wg);
-      load_row<NQ>(p.ws_up + (int64_t)i * d, wu);
-      for (int b = 0; b < B; ++b) {
-        const float a = wave_sum(part_dot<NQ>(wg, xs + b * d));
-        const float u = wave_sum(part_dot<NQ>(wu, xs + b * d));
-        if (lane == 0) p.hs[b * fs + i] = silu(a) * u;
-      }
-    }
-  }
-
-  // ---- B: every workgroup waits for all logits
-  grid_barrier(p.sync);
-
-  // ---- C: routing in LDS (one wavefront per token), then the selected experts' rows
+  // routing in LDS, one wavefront per token
   for (int b = wave; b < B; b += nwave) {
     int choice, rank;
     float gate;
-    wave_route_row<16>(p.logits + b * E, E, k, choice, rank, gate);
+    const float* l0 = p.logits + (int64_t)b * E;
+    const int64_t ps = (int64_t)B * E;   // stride between the partial-logit planes
+    wave_route_row_f<16>(
+        [&](int e) {
+          return (((l0[e] + l0[ps + e]) + l0[2 * ps + e]) + l0[3 * ps + e]) + (p.b_r ? p.b_r[e] : 0.f);
+        },
+        E, k, choice, rank, gate);
     if (lane < k) {
       sel[b * DEC_KMAX + rank] = choice;             // ascending expert id
       if (blockIdx.x == 0) {
@@ -208,8 +206,21 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_k1(DecodeArgs p) {
     }
   }
   __syncthreads();
+  // the shared expert's rows, then the selected experts' rows, as one sequence of
+  // rows dealt round-robin to the wavefronts
+  for (int i = gw; i < fs; i += W) {
+    u32x4 wg[NQ], wu[NQ];
+    load_row<NQ>(p.ws_gate + (int64_t)i * d, wg);
+    load_row<NQ>(p.ws_up + (int64_t)i * d, wu);
+    for (int b = 0; b < B; ++b) {
+      float sa, su;
+      part_dot2<NQ>(wg, wu, xs + b * d, sa, su);
+      const float a = wave_sum(sa), u = wave_sum(su);
+      if (lane == 0) p.hs[b * fs + i] = silu(a) * u;
+    }
+  }
   const int U = *nuniq;
-  for (int item = gw; item < U * f; item += W) {
+  for (int item = gw - fs % W + (gw < fs % W ? W : 0); item < U * f; item += W) {
     const int e = uniq[item / f], i = item % f;
     u32x4 wg[NQ], wu[NQ];
     load_row<NQ>(p.w_gate + ((int64_t)e * f + i) * d, wg);
@@ -219,8 +230,9 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_k1(DecodeArgs p) {
     for (int half = 0; half < 2; ++half)
       for (unsigned long long m = half ? m1 : m0; m; m &= m - 1) {
         const int q = half * 64 + __builtin_ctzll(m), b = q / k, j = q % k;
-        const float a = wave_sum(part_dot<NQ>(wg, xs + b * d));
-        const float u = wave_sum(part_dot<NQ>(wu, xs + b * d));
+        float sa, su;
+        part_dot2<NQ>(wg, wu, xs + b * d, sa, su);
+        const float a = wave_sum(sa), u = wave_sum(su);
         if (lane == 0) p.h[((int64_t)b * k + j) * f + i] = silu(a) * u;
       }
   }
@@ -245,7 +257,6 @@ __global__ __launch_bounds__(256) void decode_k2(DecodeArgs p) {
     uniq[q] = p.uniq[q];
   }
   if (tid == 0) nuniq = p.uniq[DEC_BMAX * DEC_KMAX];
-  if (blockIdx.x == 0 && tid == 0) p.sync[0] = 0u;   // kernel 1 has finished: re-arm its barrier
   __syncthreads();
   for (int q = tid; q < B * k; q += 256) {   // b < B <= 8, j < k <= 16: index < 128
     sel[(q / k) * DEC_KMAX + q % k] = p.topk_idx[q];
@@ -319,19 +330,11 @@ __global__ __launch_bounds__(256) void decode_k2(DecodeArgs p) {
     }
 }
 
-// Workspace: logits [B,E] f32 | shared h [B,max(fs,1)] f32 | h [B,k,f] f32 |
-// unique-expert list [DEC_BMAX*DEC_KMAX + 1] i32 | barrier counter u32 | time-out flag u32.
-static size_t decode_sync_offset(int B, int E, int k, int f, int fs) {
-  return ((size_t)B * E + (size_t)B * (fs > 0 ? fs : 1) + (size_t)B * k * f) * sizeof(float) +
-         (DEC_BMAX * DEC_KMAX + 1) * sizeof(int32_t);
-}
-
+// Workspace: partial logits [DEC_RP,B,E] f32 | shared h [B,max(fs,1)] f32 |
+// h [B,k,f] f32 | unique-expert list [DEC_BMAX*DEC_KMAX + 1] i32.
 size_t decode_workspace_bytes(int B, int E, int k, int f, int fs) {
-  return decode_sync_offset(B, E, k, f, fs) + 2 * sizeof(uint32_t);
-}
-
-size_t decode_flag_offset(int B, int E, int k, int f, int fs) {
-  return decode_sync_offset(B, E, k, f, fs) + sizeof(uint32_t);
+  return ((size_t)DEC_RP * B * E + (size_t)B * (fs > 0 ? fs : 1) + (size_t)B * k * f) * sizeof(float) +
+         (DEC_BMAX * DEC_KMAX + 1) * sizeof(int32_t);
 }
 
 hipError_t launch_decode(const void* x, const float* w_r, const float* b_r, const void* w_gate,
@@ -354,10 +357,9 @@ hipError_t launch_decode(const void* x, const float* w_r, const float* b_r, cons
   a.ws_down = (const bf16_t*)ws_down;
   a.B = B; a.d = d; a.E = E; a.k = k; a.f = f; a.fs = fs;
   a.logits = (float*)ws;
-  a.hs = a.logits + (size_t)B * E;
+  a.hs = a.logits + (size_t)DEC_RP * B * E;
   a.h = a.hs + (size_t)B * (fs > 0 ? fs : 1);
   a.uniq = (int32_t*)(a.h + (size_t)B * k * f);
-  a.sync = (uint32_t*)((char*)ws + decode_sync_offset(B, E, k, f, fs));
   a.topk_idx = topk_idx;
   a.topk_gate = topk_gate;
   a.y = (bf16_t*)y;
@@ -376,16 +378,33 @@ hipError_t launch_decode(const void* x, const float* w_r, const float* b_r, cons
   if (err != hipSuccess) return err;
   err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
-  err = hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (err != hipSuccess) return err;
+  static bool lds_opt_in[17] = {};   // per d / 512: the largest LDS any call may need
+  if (!lds_opt_in[d / 512]) {
+    err = hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)((size_t)DEC_BMAX * d * 2 + (2 * DEC_BMAX * DEC_KMAX + 1) * 4 +
+                                    (1024 / 32) * 4));
+    if (err != hipSuccess) return err;
+    lds_opt_in[d / 512] = true;
+  }
   err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k1, DEC_THREADS, lds);
   if (err != hipSuccess) return err;
   if (per_cu < 1) return hipErrorInvalidConfiguration;
-  // at most 2 workgroups per CU: well inside the residency limit the cooperative
-  // launch checks, and enough wavefronts to keep every row's loads in flight
+  // at most 2 workgroups per CU: enough wavefronts to keep every row's loads in flight
   const int grid = ncu * (per_cu < 2 ? per_cu : 2);
-  void* kargs[] = {&a};
-  err = hipLaunchCooperativeKernel(k1, dim3(grid), dim3(DEC_THREADS), kargs, (unsigned)lds, st);
+  const unsigned g0 = (unsigned)((DEC_RP * E + 3) / 4);
+  switch (d / 512) {
+#define K1_LAUNCH(n) \
+  case n:                                                  \
+    decode_router<n><<<g0, 256, 0, st>>>(a);               \
+    decode_k1<n><<<grid, DEC_THREADS, lds, st>>>(a);       \
+    break;
+    K1_LAUNCH(1) K1_LAUNCH(2) K1_LAUNCH(3) K1_LAUNCH(4) K1_LAUNCH(5) K1_LAUNCH(6) K1_LAUNCH(7)
+    K1_LAUNCH(8) K1_LAUNCH(9) K1_LAUNCH(10) K1_LAUNCH(11) K1_LAUNCH(12) K1_LAUNCH(13)
+    K1_LAUNCH(14) K1_LAUNCH(15) K1_LAUNCH(16)
+#undef K1_LAUNCH
+    default: return hipErrorInvalidValue;
+  }
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
   const unsigned g2 = (unsigned)(((d + DEC_R - 1) / DEC_R + 3) / 4);
   switch (f / 512) {

@@ -38,7 +38,6 @@ hipError_t launch_combine(bool f32, const void* ring_y, const int32_t* copy_slot
 
 // decode
 size_t decode_workspace_bytes(int B, int E, int k, int f, int fs);
-size_t decode_flag_offset(int B, int E, int k, int f, int fs);
 hipError_t launch_decode(const void* x, const float* w_r, const float* b_r, const void* w_gate,
                          const void* w_up, const void* w_down, const void* ws_gate,
                          const void* ws_up, const void* ws_down, int B, int d, int E, int k,

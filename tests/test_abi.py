@@ -25,8 +25,7 @@ def declared_functions():
 def test_header_declares_the_six_calls_and_helpers():
     names = declared_functions()
     for n in ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_decode",
-              "moe_backward", "moe_workspace_bytes", "moe_status_string", "moe_quantize_mx",
-              "moe_decode_flag_offset"]:
+              "moe_backward", "moe_workspace_bytes", "moe_status_string", "moe_quantize_mx"]:
         assert n in names
 
 
@@ -120,15 +119,6 @@ def test_ring_head_range_and_dtype_gates():
         sd = moe.make_shape(4, bad["d"], 16, 4, bad["f"], fs=bad["fs"], dtype="bf16")
         assert L.moe_decode(sd, *([FAKE] * 12), FAKE, 1 << 30, None) == _lib.MOE_ERR_SHAPE, bad
     assert L.moe_quantize_mx(FAKE, 4, 48, FAKE, FAKE, None) == _lib.MOE_ERR_SHAPE
-
-
-def test_decode_flag_sits_inside_the_decode_workspace():
-    import gen
-    for B in (1, 4, 8):
-        cfg = gen.DECODE(B)
-        s = moe.make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, fs=cfg.fs, dtype="bf16")
-        off = _lib.lib().moe_decode_flag_offset(s)
-        assert off % 4 == 0 and 0 < off and off + 4 <= moe.workspace_bytes(s, moe.OP_DECODE)
 
 
 def test_workspace_sizes_of_the_workloads():

@@ -18,7 +18,6 @@ def check_decode(cfg, reps=5):
     y, idx, gate = layer.decode(inp.x, inp.w_router, inp.b_router, inp.w_gate, inp.w_up,
                                 inp.w_down, inp.ws_gate, inp.ws_up, inp.ws_down)
     torch.cuda.synchronize()
-    assert not layer.decode_barrier_timed_out(), "decode grid barrier timed out"
     x = to_oracle(inp.x)
     w_r = to_oracle(inp.w_router)
     b = None if inp.b_router is None else to_oracle(inp.b_router)
@@ -37,7 +36,6 @@ def check_decode(cfg, reps=5):
                                        inp.w_down, inp.ws_gate, inp.ws_up, inp.ws_down)
         torch.cuda.synchronize()
         assert torch.equal(y2, y0) and torch.equal(idx2, idx)
-    assert not layer.decode_barrier_timed_out(), "decode grid barrier timed out"
     return err
 
 
