@@ -168,6 +168,57 @@ def cpu_baseline(inp, cfg, budget_s):
                        + f" in {est:.1f} s")}
 
 
+def skew_fwd_bwd(torch, moe, steps):
+    """Forward (saving A|U) and backward of the skewed workload, timed separately.
+    Algorithmic bytes: forward = used experts' three matrices + W_r (fp32) + x read twice
+    (router, dispatch) + ring written and read + H written and read + saved A|U written +
+    ring_y written and read + y written; backward = used experts' three matrices read +
+    all three weight gradients written (every expert, zeros included) + dW_r (fp32) +
+    dy, x, ring rows, saved A|U read + dx written."""
+    import numpy as np
+    from gen import SKEW_BWD, make_layer
+    cfg = SKEW_BWD
+    progress(f"skewed forward + backward {cfg.name}")
+    inp = make_layer(cfg, "cuda")
+    layer = moe.Layer.create(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.C)
+    args = (inp.x, inp.w_router, inp.b_router, inp.w_gate, inp.w_up, inp.w_down)
+    for _ in range(2):
+        layer.forward(*args, save_au=True)
+        layer.backward(inp.dy, inp.x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        layer.forward(*args, save_au=True)
+        ev[i][1].record()
+        layer.backward(inp.dy, inp.x, inp.w_router, inp.w_gate, inp.w_up, inp.w_down)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    fwd = [e[0].elapsed_time(e[1]) for e in ev]
+    bwd = [e[1].elapsed_time(e[2]) for e in ev]
+    counts = layer.bufs["expert_count"].cpu().numpy()
+    used = int((counts > 0).sum())
+    T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f
+    n = T * k
+    w_used = used * 3 * f * d * 2
+    fwd_bytes = (w_used + E * d * 4 + 2 * T * d * 2 + 2 * n * d * 2 + 2 * n * f * 2 + n * 2 * f * 2
+                 + 2 * n * d * 2 + T * d * 2)
+    bwd_bytes = (w_used + E * 3 * f * d * 2 + E * d * 4 + 2 * T * d * 2 + n * d * 2
+                 + n * 2 * f * 2 + T * d * 2)
+    fwd_flops = 2.0 * n * d * 3 * f + 2.0 * T * E * d
+    bwd_flops = 2 * 2.0 * n * d * 3 * f + 2 * 2.0 * n * d
+    fm, bm = float(np.median(fwd)), float(np.median(bwd))
+    return {"tokens": T, "fwd_ms_median": round(fm, 4), "fwd_ms_min": round(min(fwd), 4),
+            "bwd_ms_median": round(bm, 4), "bwd_ms_min": round(min(bwd), 4),
+            "tokens_per_s_fwd_bwd": round(T / ((fm + bm) * 1e-3), 1),
+            "fwd_alg_bytes": fwd_bytes, "fwd_hbm_frac": round(fwd_bytes / (fm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "fwd_mfma_frac": round(fwd_flops / (fm * 1e-3) / 1e12 / BF16_PEAK_TFS, 4),
+            "bwd_alg_bytes": bwd_bytes, "bwd_hbm_frac": round(bwd_bytes / (bm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bwd_mfma_frac": round(bwd_flops / (bm * 1e-3) / 1e12 / BF16_PEAK_TFS, 4),
+            "experts_used": used, "max_load": int(counts.max()), "mean_load": round(float(n / E), 2),
+            "max_over_mean": round(float(counts.max() / (n / E)), 2)}
+
+
 def secondary(torch, moe, steps):
     import numpy as np
     from gen import DECODE, FWD_MXFP8, SHARE_BF16, SHARE_MXFP8, make_layer, make_share
@@ -194,9 +245,25 @@ def secondary(torch, moe, steps):
         e.record()
         torch.cuda.synchronize()
         us = s.elapsed_time(e) * 1e3 / calls
+        # cold: each call timed alone after a 1 GiB fill that evicts the 256 MB Infinity
+        # Cache (the fill is outside the events)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cold = []
+        for _ in range(20):
+            flush.zero_()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            layer.decode(*args)
+            c1.record()
+            torch.cuda.synchronize()
+            cold.append(c0.elapsed_time(c1) * 1e3)
+        del flush
+        cold.sort()
         U = int(np.unique(layer.bufs["topk_idx"].cpu().numpy()).size)
         nbytes = (U + 1) * 3 * cfg.f * cfg.d * 2 + cfg.E * cfg.d * 4 + 2 * B * cfg.d * 2
         dec[f"B{B}"] = {"calls": calls, "us_per_call": round(us, 2), "us_per_token": round(us / B, 2),
+                        "cold_us_median": round(cold[len(cold) // 2], 2), "cold_us_min": round(cold[0], 2),
+                        "cold_us_p90": round(cold[int(0.9 * (len(cold) - 1))], 2),
                         "unique_experts": U, "alg_bytes": nbytes,
                         "GBps": round(nbytes / us / 1e3, 1),
                         "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
@@ -236,6 +303,9 @@ def secondary(torch, moe, steps):
                           "gemm2_mfma_frac": round(f2 / g2 / 1e9 / peak, 4)}
         del sh, ws, ring_y, xq, xs, wargs
         torch.cuda.empty_cache()
+    # ---- skewed forward + backward: 8,192 tokens, d 4096, E 512, k 10, f 1024
+    out["skew_fwd_bwd_t8192"] = skew_fwd_bwd(torch, moe, steps)
+    torch.cuda.empty_cache()
     # ---- MXFP8 forward at the same 2,048-token shape
     cfg = FWD_MXFP8
     progress(f"forward {cfg.name}")

@@ -17,10 +17,13 @@
 //   dgrad_kernel<UP>    [dA|dU] x [W_gate[e]; W_up[e]] (K = 2f rows) -> dX per copy (bf16)
 //   token_kernel        dg, dl per token; dx = sum_j dX[copy] + dl_j W_r[e_j] (bf16)
 //   router_wgrad        dW_r[e] = sum over the segment (last slot first) of dl x  (fp32)
-//   wgrad_kernel<DOWN>  dW_down[e] = dY_e^T (g H)_e;  <UP>  [dW_gate;dW_up][e] = [dA|dU]_e^T X_e
-// GEMM tiles are 128 x 128 with K in 64-element slices; operands whose K index is
-// the row index are transposed 8 x 8 in registers on the way into LDS.  No
-// floating-point atomics: every sum has one fixed order.
+//   gather_to_ring      dy rows copied into ring order, one per copy (t, j)
+//   wgrad_kernel        dW_down[e] = dY_e^T (g H)_e;  [dW_gate;dW_up][e] = [dA|dU]_e^T X_e
+// The dgrad tiles are 128 x 128 with K in 64-element slices; the weights, whose K
+// index is their row index, are transposed 8 x 8 in registers on the way into LDS.  The
+// weight gradients read both operands row-major through DMA and transposing LDS
+// reads (see the wgrad section).  No floating-point atomics: every sum has one
+// fixed order.
 #include "common.h"
 #include "kernels.h"
 
@@ -47,6 +50,31 @@ __device__ __forceinline__ int64_t tok_of_slot(const int32_t* slot_copy, int64_t
   return slot_copy[s] / k;
 }
 
+// Output tiles are staged row-major in LDS (BT rows of BT bf16, rows padded by 16
+// bytes) and written as whole 16-byte pieces of rows instead of 2-byte stores
+// scattered over rows.
+constexpr int SRS = BT * 2 + 16;            // staged row stride in bytes
+constexpr int STAGE_BYTES = BT * SRS;       // 34,816
+constexpr int SMEM_BYTES = 4 * BT * BKB;    // the two double-buffered operand tiles: 65,536
+
+__device__ __forceinline__ void stage_put(uint8_t* stg, int m, int n, float v) {
+  *(uint16_t*)(stg + m * SRS + n * 2) = f2bf(v);
+}
+
+// Write the staged tile: row m < rows goes to dst_row(m) (a pointer to the tile's first
+// column in that row), 16 bytes per thread and step.  Barriers before and after.
+template <typename RowF>
+__device__ __forceinline__ void stage_flush(const uint8_t* stg, int rows, RowF dst_row) {
+  __syncthreads();
+  constexpr int CPR = BT * 2 / 16;
+#pragma unroll 4
+  for (int q = threadIdx.x; q < BT * CPR; q += 256) {
+    const int m = q / CPR, c = q % CPR;
+    if (m < rows) *(u32x4*)((uint8_t*)dst_row(m) + c * 16) = *(const u32x4*)(stg + m * SRS + c * 16);
+  }
+  __syncthreads();
+}
+
 // ----------------------------------------------------------------------------- dgrad
 struct DgradArgs {
   const bf16_t* A;          // DOWN: dy [T, d] (gathered through slot_copy); UP: dAU [C, 2f]
@@ -70,8 +98,9 @@ struct DgradArgs {
 
 template <bool DOWN>
 __global__ __launch_bounds__(256) void dgrad_kernel(DgradArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][BT * BKB];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BT * BKB];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_BYTES];
+  uint8_t(*As)[BT * BKB] = (uint8_t(*)[BT * BKB])smem;
+  uint8_t(*Bs)[BT * BKB] = (uint8_t(*)[BT * BKB])(smem + 2 * BT * BKB);
   __shared__ float red[2][BT];
   const int mt = blockIdx.y;
   if (mt >= *p.ntiles) return;
@@ -160,7 +189,10 @@ __global__ __launch_bounds__(256) void dgrad_kernel(DgradArgs p) {
     __syncthreads();
   }
 
+  // the loop ended with a barrier: the operand tiles are free for staging
+  uint8_t* stg = smem;
   if (DOWN) {
+    // dA, dU and g*h are written directly (three outputs per element)
     const int f = p.f;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -202,16 +234,16 @@ __global__ __launch_bounds__(256) void dgrad_kernel(DgradArgs p) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + j * 32 + lr;
+        const int nl = wn * 64 + j * 32 + lr;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = wm * 64 + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-          if (m < rows) {
-            const int64_t s = ring_slot(p.head, seg, row0 + m, p.C);
-            p.dxc[s * p.N + n] = f2bf(acc[i][j][r]);
-          }
+          stage_put(stg, m, nl, acc[i][j][r]);
         }
       }
+    stage_flush(stg, rows, [&](int m) -> void* {
+      return p.dxc + ring_slot(p.head, seg, row0 + m, p.C) * p.N + n0;
+    });
   }
 }
 
@@ -298,118 +330,246 @@ __global__ __launch_bounds__(128) void router_wgrad_kernel(const int32_t* __rest
 }
 
 // ----------------------------------------------------------------------------- wgrad
-struct WgradArgs {
-  const bf16_t* A;          // DOWN: dy [T, d] (gathered); UP: dAU [C, 2f]
-  const bf16_t* B;          // DOWN: gH [C, f]; UP: ring_x [C, d]
-  int M, N;                 // DOWN: M = d, N = f; UP: M = 2f, N = d
-  int msplit;               // UP: rows m < msplit go to out0, the rest to out1
-  int lda, ldb;
-  const int32_t* offset;
-  const int32_t* slot_copy;
-  int k, E;
-  int64_t head, C;
-  bf16_t* out0;             // [E, msplit or M, N]
-  bf16_t* out1;
+// dW[e] = A_e^T B_e over expert e's ring rows.  Both operands are row-major with the
+// reduction index (the ring row) as the row, so a stage holds WK rows of each in
+// their natural layout, copied global -> LDS by DMA, and the MFMA fragments (8
+// consecutive K of one column) are read with ds_read_b64_tr_b16: within each
+// 16-lane group, lane 4q + s addresses row k0 + q, columns c0 + 4s .. 4s + 3, and
+// lane i receives column c0 + i at rows k0 .. k0 + 3 (measured on gfx950).  Two
+// such reads give a lane its 8 K values.
+//
+// The experts hold few rows each (K is short) while dW is large, so the kernel is
+// bound by writing dW.  Each workgroup computes one WM x WN tile in 4 waves of
+// 64 x WN/2 with WS stages of WK = 32 rows; small tiles and LDS used for the stages
+// only let several workgroups share a CU, so that one's loads, MFMAs and stores
+// overlap another's.  Stage kt holds the segment rows [n - WK (kt + 1), n - WK kt):
+// the expert's rows are consumed last slot first, and rows before the segment
+// start are read from a zero row (they add nothing).  The 16-byte chunks of a
+// staged row are XOR-swizzled by ((row & 3) << 2): a transposing read is served 32
+// lanes (4 rows x 64 bytes) at a time, and the four rows then fall on distinct banks.
+//
+// The MFMA is given the B fragment first, so it accumulates the transposed tile:
+// a lane holds one output row and, per group of 4 accumulators, 4 consecutive
+// columns.  Lanes l and l + 32 hold the two halves of 8 columns; one
+// v_permlane32_swap per packed word pair gives each lane 8 consecutive bf16 of one
+// row, which it writes straight from registers as one 16-byte piece.
+constexpr int WM_ = 128, WK_ = 32;
+
+template <int NJ>   // 32-column blocks per wave: tile width WN = 64 NJ
+struct WgShape {
+  static constexpr int WN = 64 * NJ;
+  static constexpr int ARB = WM_ * 2, BRB = WN * 2;   // staged row bytes of A and B
+  static constexpr int STAGE = WK_ * (ARB + BRB);
+  static constexpr int LA = WK_ * ARB / 4096, LB = WK_ * BRB / 4096;   // 1 KB copies per wave
+  static constexpr int L = LA + LB;
 };
 
-template <bool GATHER_A>
-__global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][BT * BKB];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BT * BKB];
-  const int e = p.E - 1 - (int)blockIdx.z;        // experts E-1 -> 0
-  const int m0 = blockIdx.y * BT, n0 = blockIdx.x * BT;
-  const int32_t seg = p.offset[e], nrows = p.offset[e + 1] - seg;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ int wsw(int r, int c) { return c ^ ((r & 3) << 2); }
+
+__device__ __forceinline__ void dma16_at(const void* addr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(addr), "s"(lds) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void bwait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <typename T>
+__device__ __forceinline__ T bld_meta(const T* q) {   // scalar load of data written by earlier kernels
+  return *(const __attribute__((address_space(4))) T*)q;
+}
+
+// Two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i16_t ds_tr16(const uint8_t* lds_ptr) {
+  typedef __attribute__((address_space(3))) v4i16_t lds_v4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4*)((__attribute__((address_space(3))) uint8_t*)lds_ptr));
+}
+
+struct WgradArgs {
+  const bf16_t* A;          // ring-ordered rows: DOWN dy gathered into ring order [C, d]; UP dAU [C, 2f]
+  const bf16_t* B;          // ring-ordered rows: DOWN gH [C, f]; UP ring_x [C, d]
+  int M, N;                 // DOWN: M = d, N = f; UP: M = 2f, N = d
+  int msplit;               // rows m < msplit go to out0, the rest to out1
+  int lda, ldb;             // row lengths (elements)
+  const int32_t* offset;
+  int E;
+  int64_t head, C;
+  const bf16_t* zero;       // >= 1024 zero bytes
+  bf16_t* out0;             // [E, msplit, N]
+  bf16_t* out1;             // [E, M - msplit, N]
+};
+
+template <int NJ, int WS, int OCC>
+__global__ __launch_bounds__(256, OCC) void wgrad_kernel(WgradArgs p) {
+  using S = WgShape<NJ>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  const int mtiles = (p.M + WM_ - 1) / WM_, ntiles = (p.N + S::WN - 1) / S::WN;
+  const int P = mtiles * ntiles;   // tiles per expert
+  // Workgroup b runs on XCD b % 8.  Each expert's P tiles are dealt to the 8 XCDs in
+  // 8 contiguous chunks, and XCD x walks its chunk of every expert, experts E-1 -> 0:
+  // each XCD gets the same share of every expert's rows, however skewed the loads.
+  // A chunk spans all tiles along the operand with the smaller panel (A when M < N),
+  // so every XCD's L2 reads the whole of that panel but only its slice of the other.
+  const int x = blockIdx.x & 7, li = blockIdx.x >> 3;
+  const int cbase = x * P / 8, cnt = (x + 1) * P / 8 - cbase;
+  if (cnt == 0 || li >= cnt * p.E) return;
+  const int e = p.E - 1 - li / cnt, jt = cbase + li % cnt;
+  const bool nmajor = p.M < p.N;
+  const int m0 = (nmajor ? jt % mtiles : jt / ntiles) * WM_;
+  const int n0 = (nmajor ? jt / mtiles : jt % ntiles) * S::WN;
+  const int32_t seg = bld_meta(p.offset + e);
+  const int nrows = bld_meta(p.offset + e + 1) - seg;
+  const int KT = max(1, (nrows + WK_ - 1) / WK_);
+  const int64_t hs = p.head + seg;   // ring slot of segment row i: hs + i, less C once past the end
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lg = lane >> 5;
-  // threads 0..127 stage A (8 K-rows x 8 M), threads 128..255 stage B (8 K-rows x 8 N)
-  const bool isA = tid < 128;
-  const int kb = (tid & 127) >> 4, cb = tid & 15;
-  const int KT = (nrows + 63) / 64;
 
-  u32x4 rr[8];
-  auto gload = [&](int kt) {
-    // stage kt holds segment rows [nrows - 64 (kt + 1), nrows - 64 kt): the last rows first
-    const int base = nrows - 64 * (kt + 1) + kb * 8;
+  // Per copy c of this wave (fixed for the tile): the staged row this lane fills and
+  // the byte offset of its 16-byte piece inside a source row.
+  int crow[S::L], ccol[S::L];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int i = base + q;
-      if (i < 0) {
-        rr[q] = u32x4{0, 0, 0, 0};
-        continue;
-      }
-      const int64_t s = ring_slot(p.head, seg, i, p.C);
-      if (isA) {
-        const int64_t row = GATHER_A ? tok_of_slot(p.slot_copy, s, p.k) : s;
-        rr[q] = *(const u32x4*)(p.A + row * p.lda + m0 + cb * 8);
-      } else {
-        rr[q] = *(const u32x4*)(p.B + s * p.ldb + n0 + cb * 8);
-      }
+  for (int c = 0; c < S::L; ++c) {
+    const bool isa = c < S::LA;
+    const int j = 4 * (isa ? c : c - S::LA) + wave;
+    const int rb = isa ? S::ARB : S::BRB;
+    const int q = lane / (rb / 16), r = j * (1024 / rb) + q, lc = wsw(r, lane % (rb / 16));
+    crow[c] = r;
+    ccol[c] = 2 * (isa ? min(m0 + lc * 8, p.M - 8) : min(n0 + lc * 8, p.N - 8));
+  }
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    const uint32_t st = lds0 + (uint32_t)(kt % WS) * S::STAGE;
+    const int rbase = nrows - WK_ * (kt + 1);   // segment row of staged row 0
+#pragma unroll
+    for (int c = 0; c < S::L; ++c) {
+      const bool isa = c < S::LA;
+      const int j = 4 * (isa ? c : c - S::LA) + wave;
+      const int i = rbase + crow[c];
+      int64_t sl = hs + i;
+      sl = sl >= p.C ? sl - p.C : sl;
+      const int64_t rowbytes = (int64_t)(isa ? p.lda : p.ldb) * 2;
+      const uint8_t* src = i >= 0 ? (const uint8_t*)(isa ? p.A : p.B) + sl * rowbytes + ccol[c]
+                                  : (const uint8_t*)p.zero + lane * 16;
+      dma16_at(src, __builtin_amdgcn_readfirstlane(st + (isa ? 0 : WK_ * S::ARB) + j * 1024));
     }
   };
-  auto sstore = [&](int buf) {
-    u32x4 o[8];
-    transpose8x8(rr, o);
-    uint8_t* dst = isA ? As[buf] : Bs[buf];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) *(u32x4*)(dst + bswz(cb * 8 + m, kb)) = o[m];
+  auto wait_stage = [&](int later) __attribute__((always_inline)) {
+    if (later <= 0) bwait_vm<0>();
+    else if (later == 1) bwait_vm<S::L>();
+    else bwait_vm<2 * S::L>();
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[NJ][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int jn = 0; jn < NJ; ++jn)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[jn][i][r] = 0.f;
 
-  if (KT > 0) {
-    gload(0);
-    sstore(0);
-    __syncthreads();
+  // Fragment q of sub-step 0: q < 2 is A fragment q (tile columns wm*64 + 32q), else B
+  // fragment q - 2 (columns wn*32*NJ + 32(q-2)).  Offset inside a stage of this lane's
+  // first transposing read (4 K rows); the second is 4 rows further (same swizzle,
+  // since it depends on row & 3), and sub-step kk is 16 rows further.
+  int foff[2 + NJ];
+  {
+    const int g = lane >> 4, gi = lane & 15, qq = gi >> 2, ss = gi & 3;
+    const int r0 = 8 * (g >> 1) + qq;
+#pragma unroll
+    for (int q = 0; q < 2 + NJ; ++q) {
+      const bool isa = q < 2;
+      const int col = (isa ? wm * 64 + q * 32 : wn * 32 * NJ + (q - 2) * 32) + 16 * (g & 1) + 4 * ss;
+      foff[q] = (isa ? 0 : WK_ * S::ARB) + r0 * (isa ? S::ARB : S::BRB) + wsw(r0, col >> 3) * 16 +
+                (col & 7) * 2;
+    }
   }
+  auto frag = [&](const uint8_t* sb, int kk, int q) __attribute__((always_inline)) -> bf16x8 {
+    const int rowb = q < 2 ? S::ARB : S::BRB;
+    const uint8_t* a = sb + foff[q] + kk * 16 * rowb;
+    const v4i16_t lo = ds_tr16(a), hi = ds_tr16(a + 4 * rowb);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  for (int s = 0; s < WS - 1 && s < KT; ++s) issue(s);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int c = kk * 2 + lg;
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(As[cur] + bswz(wm * 64 + i * 32 + lr, c)));
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bs[cur] + bswz(wn * 64 + j * 32 + lr, c)));
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) sstore(cur ^ 1);
+    wait_stage(min(WS - 2, KT - 1 - kt));
     __syncthreads();
+    if (kt + WS - 1 < KT) issue(kt + WS - 1);
+    const uint8_t* sb = lds + (kt % WS) * S::STAGE;
+    bf16x8 fa[2][2], fb[2][NJ];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fa[0][i] = frag(sb, 0, i);
+#pragma unroll
+    for (int jn = 0; jn < NJ; ++jn) fb[0][jn] = frag(sb, 0, 2 + jn);
+#pragma unroll
+    for (int kk = 0; kk < WK_ / 16; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < WK_ / 16) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) fa[cur ^ 1][i] = frag(sb, kk + 1, i);
+#pragma unroll
+        for (int jn = 0; jn < NJ; ++jn) fb[cur ^ 1][jn] = frag(sb, kk + 1, 2 + jn);
+      }
+#pragma unroll
+      for (int jn = 0; jn < NJ; ++jn)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          acc[jn][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][jn], fa[cur][i], acc[jn][i], 0, 0, 0);
+    }
   }
 
+  // acc[jn][i][r]: output row m0 + wm*64 + 32i + lr, column
+  // n0 + wn*32*NJ + 32jn + 8(r/4) + 4lg + r%4.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + wm * 64 + 32 * i + lr;
+    bf16_t* row = m < p.msplit ? p.out0 + ((int64_t)e * p.msplit + m) * p.N
+                               : p.out1 + ((int64_t)e * (p.M - p.msplit) + (m - p.msplit)) * p.N;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + j * 32 + lr;
+    for (int jn = 0; jn < NJ; ++jn)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-        bf16_t* dst = m < p.msplit ? p.out0 + ((int64_t)e * p.msplit + m) * p.N
-                                   : p.out1 + ((int64_t)e * (p.M - p.msplit) + (m - p.msplit)) * p.N;
-        dst[n] = f2bf(acc[i][j][r]);
+      for (int h = 0; h < 2; ++h) {
+        const f32x16& a = acc[jn][i];
+        // x: columns 16h + 4lg + 0..3, y: columns 16h + 8 + 4lg + 0..3.  The swap hands
+        // x of lanes 32..63 to lanes 0..31 and y of lanes 0..31 to lanes 32..63.
+        const uint32_t x0 = cvt_pk_bf16(a[8 * h + 0], a[8 * h + 1]), x1 = cvt_pk_bf16(a[8 * h + 2], a[8 * h + 3]);
+        const uint32_t y0 = cvt_pk_bf16(a[8 * h + 4], a[8 * h + 5]), y1 = cvt_pk_bf16(a[8 * h + 6], a[8 * h + 7]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+        const int n = n0 + wn * 32 * NJ + 32 * jn + 16 * h + 8 * lg;
+        if (m < p.M && n < p.N) *(u32x4*)(row + n) = v;
       }
-    }
+  }
+}
+
+// dy rows into ring order: rdy[copy_slot[t, j]] = dy[t] (the layout of the ring).
+__global__ __launch_bounds__(256) void gather_to_ring_kernel(const bf16_t* __restrict__ dy,
+                                                             const int32_t* __restrict__ copy_slot,
+                                                             int k, int d, bf16_t* __restrict__ rdy) {
+  const int64_t t = blockIdx.x;
+  const u32x4* src = (const u32x4*)(dy + t * d);
+  for (int v = threadIdx.x; v < d / 8; v += 256) {
+    const u32x4 val = src[v];
+    for (int j = 0; j < k; ++j) ((u32x4*)(rdy + (int64_t)copy_slot[t * k + j] * d))[v] = val;
+  }
 }
 
 // ----------------------------------------------------------------------------- launcher
 static int bwd_max_tiles(int64_t n, int E) { return (int)((n + BT - 1) / BT) + E; }
 
 struct BwdLayout {
-  size_t tiles, dau, gh, dgpart, dxc, dl, total;
+  size_t tiles, dau, gh, dgpart, dxc, dl, zero, rdy, total;
 };
 
 static BwdLayout bwd_layout(int64_t T, int64_t C, int d, int E, int k, int f) {
@@ -422,12 +582,38 @@ static BwdLayout bwd_layout(int64_t T, int64_t C, int d, int E, int k, int f) {
   L.dgpart = o; o += al((size_t)C * (f / BT) * 4);
   L.dxc = o;   o += al((size_t)C * d * 2);
   L.dl = o;    o += al((size_t)C * 4);
+  L.zero = o;  o += 1024;   // a zero row for the weight-gradient stages
+  L.rdy = o;   o += al((size_t)C * d * 2);   // dy in ring order
   L.total = o;
   return L;
 }
 
 size_t backward_workspace_bytes(int64_t T, int64_t C, int d, int E, int k, int f) {
   return bwd_layout(T, C, d, E, k, f).total;
+}
+
+__global__ void zero_fill_kernel(uint32_t* __restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+// 128 x 128 tiles, 2 stages, 4 workgroups per CU
+constexpr int WG_NJ = 2, WG_WS = 2, WG_OCC = 4;
+
+static hipError_t run_wgrad(const WgradArgs& a, hipStream_t st) {
+  auto kern = wgrad_kernel<WG_NJ, WG_WS, WG_OCC>;
+  constexpr int lds = WG_WS * WgShape<WG_NJ>::STAGE;
+  if (lds > 65536) {
+    static bool attr_set = false;   // opt in to more than 64 KB of LDS once per process
+    if (!attr_set) {
+      hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (err != hipSuccess) return err;
+      attr_set = true;
+    }
+  }
+  const int64_t P = (int64_t)((a.M + WM_ - 1) / WM_) * ((a.N + WgShape<WG_NJ>::WN - 1) / WgShape<WG_NJ>::WN);
+  kern<<<(unsigned)(8 * ((P + 7) / 8) * a.E), 256, lds, st>>>(a);   // 8 XCDs x the largest chunk
+  return hipGetLastError();
 }
 
 hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
@@ -484,8 +670,11 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
                                             w_r, d, k, dl, (bf16_t*)dx);
   router_wgrad_kernel<<<dim3(E, (d / 8 + 127) / 128), 128, 0, st>>>(
       expert_offset, head, C, (const bf16_t*)ring_x, dl, d, dw_r);
+  zero_fill_kernel<<<1, 256, 0, st>>>((uint32_t*)(w + L.zero), 256);
+  bf16_t* rdy = (bf16_t*)(w + L.rdy);
+  gather_to_ring_kernel<<<(unsigned)T, 256, 0, st>>>((const bf16_t*)dy, copy_slot, k, d, rdy);
   WgradArgs wd{};
-  wd.A = (const bf16_t*)dy;
+  wd.A = rdy;
   wd.B = gh;
   wd.M = d;
   wd.N = f;
@@ -493,14 +682,13 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
   wd.lda = d;
   wd.ldb = f;
   wd.offset = expert_offset;
-  wd.slot_copy = slot_copy;
-  wd.k = k;
   wd.E = E;
   wd.head = head;
   wd.C = C;
+  wd.zero = (const bf16_t*)(w + L.zero);
   wd.out0 = (bf16_t*)dw_down;
   wd.out1 = (bf16_t*)dw_down;
-  wgrad_kernel<true><<<dim3(f / BT, d / BT, E), 256, 0, st>>>(wd);
+  if ((err = run_wgrad(wd, st)) != hipSuccess) return err;
   WgradArgs wu = wd;
   wu.A = dau;
   wu.B = (const bf16_t*)ring_x;
@@ -511,7 +699,7 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
   wu.ldb = d;
   wu.out0 = (bf16_t*)dw_gate;
   wu.out1 = (bf16_t*)dw_up;
-  wgrad_kernel<false><<<dim3(d / BT, 2 * f / BT, E), 256, 0, st>>>(wu);
+  if ((err = run_wgrad(wu, st)) != hipSuccess) return err;
   return hipGetLastError();
 }
 
