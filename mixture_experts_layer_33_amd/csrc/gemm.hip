@@ -66,17 +66,17 @@ hipError_t launch_build_tiles(const int32_t* expert_offset, int E, int BM, int32
 // W_up, and every wave holds matching gate and up fragments, so the epilogue
 // forms h = silu(a) * u in registers.
 //
-// LDS serves a 128-bit read in groups of 8 lanes (128 bytes per clock); a
-// fragment read has lanes 0..7 on 8 consecutive rows at the same logical 16-byte
-// chunk.  The chunks of a row are XOR-swizzled so that those 8 reads hit 8
-// distinct 16-byte bank groups: by (row & 7) for 128-byte rows, by
-// ((row >> 1) & 3) for 64-byte rows (two rows share a 128-byte bank line).
-// Both were measured conflict-free (the same rate as contiguous addresses).
+// LDS serves a 128-bit read 16 lanes (256 bytes) at a time; a fragment read has
+// lanes 0..15 on 16 consecutive rows at the same logical 16-byte chunk.  The
+// chunks of a row are XOR-swizzled so that those 16 reads hit 16 distinct 16-byte
+// bank groups of the 256-byte bank line: by ((row >> 1) & 7) for 128-byte rows
+// (two rows per bank line), by ((row >> 2) & 3) for 64-byte rows (four rows per
+// bank line).  The bank-conflict counter reads zero for both.
 template <int KB>
 __device__ __forceinline__ int swz(int r, int c) {
   static_assert(KB == 128 || KB == 64, "row slice");
-  if constexpr (KB == 128) return r * 128 + ((c ^ (r & 7)) << 4);
-  else return r * 64 + ((c ^ ((r >> 1) & 3)) << 4);
+  if constexpr (KB == 128) return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+  else return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
 }
 
 struct GemmArgs {
@@ -155,19 +155,20 @@ struct EpiLayout {
 };
 
 template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S>
-__global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
+__global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   constexpr int EB = MX ? 1 : 2;                 // element bytes
   constexpr int WTM = BM / WM, WTN = BN / WN;    // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int CH = KB / 16;                    // 16-byte chunks per row slice
   constexpr int RPC = 64 / CH;                   // rows per 1 KB copy
   using SL = StageLayout<BM, BN, KB, MX>;
-  constexpr int NA = BM * KB / 4096, NB = BN * KB / 4096;   // 1 KB copies per wave
+  constexpr int NW = WM * WN, NT = NW * 64;      // waves, threads
+  constexpr int NA = BM * KB / (NW * 1024), NB = BN * KB / (NW * 1024);   // 1 KB copies per wave
   constexpr int NASC = MX ? BM * 4 / 256 : 0, NBSC = MX ? BN * 4 / 1024 : 0;
   constexpr int L = NA + NB + NASC + NBSC;       // copies per wave per stage
-  static_assert(BM * KB % 4096 == 0 && BN * KB % 4096 == 0, "tile / wave mismatch");
+  static_assert(BM * KB % (NW * 1024) == 0 && BN * KB % (NW * 1024) == 0, "tile / wave mismatch");
   static_assert(!MX || KB == 128, "MX stages hold whole 128-element scale groups");
-  static_assert(WM * WN == 4, "four waves");
+  static_assert(NW == 4 || (NW == 8 && !MX), "four waves, or eight without scales");
   static_assert(!MX || (BM * 4 % 256 == 0 && BN * 4 % 1024 == 0), "scale copies");
   static_assert(!SWIGLU || (FN % 2 == 0), "gate/up fragments come in pairs");
   static_assert(S >= 2 && S <= 4, "stages");
@@ -191,13 +192,13 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
   const uint32_t Kb = (uint32_t)p.K * EB;                 // row bytes
   const uint32_t Ks = (uint32_t)p.K / 32;                 // MX scale bytes per row
 
-  // Copy i of this wave fills 16-byte chunks j = (4 i + wave) * 64 + lane of a tile:
+  // Copy i of this wave fills 16-byte chunks j = (NW i + wave) * 64 + lane of a tile:
   // row j / CH, slot j % CH, which holds the global chunk whose swizzled slot it is
   // (the swizzle is an involution on the chunk index: swz(r, c) - r * KB = 16 * slot).
   uint32_t a_off[NA], b_off[NB];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int j = (4 * i + wave) * 64 + lane, r = j / CH;
+    const int j = (NW * i + wave) * 64 + lane, r = j / CH;
     const int c = (swz<KB>(r, j % CH) - r * KB) >> 4;
     const int64_t sl = ring_slot(p.head, seg, row0 + min(r, rows - 1), p.C);
     a_off[i] = (uint32_t)sl * Kb + c * 16;
@@ -207,9 +208,9 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
   const uint8_t* b_base[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int j = (4 * i + wave) * 64 + lane, r = j / CH;
+    const int j = (NW * i + wave) * 64 + lane, r = j / CH;
     const int c = (swz<KB>(r, j % CH) - r * KB) >> 4;
-    const bool up = SWIGLU && (4 * i + wave) * RPC >= BN / 2;
+    const bool up = SWIGLU && (NW * i + wave) * RPC >= BN / 2;
     const int rr = up ? r - BN / 2 : r;
     b_base[i] = (up ? p.B1 : p.B0) + (int64_t)e * p.N * Kb;
     b_off[i] = (uint32_t)min(n0 + rr, p.N - 1) * Kb + c * 16;
@@ -235,10 +236,10 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
   auto issue_one = [&](int kt, int c) __attribute__((always_inline)) {
     const uint32_t st = lds0 + (uint32_t)(kt % S) * SL::SIZE;
     if (c < NA) {
-      dma16(p.A + (size_t)kt * KB, a_off[c], __builtin_amdgcn_readfirstlane(st + SL::A + (4 * c + wave) * 1024));
+      dma16(p.A + (size_t)kt * KB, a_off[c], __builtin_amdgcn_readfirstlane(st + SL::A + (NW * c + wave) * 1024));
     } else if (c < NA + NB) {
       const int i = c - NA;
-      dma16(b_base[i] + (size_t)kt * KB, b_off[i], __builtin_amdgcn_readfirstlane(st + SL::B + (4 * i + wave) * 1024));
+      dma16(b_base[i] + (size_t)kt * KB, b_off[i], __builtin_amdgcn_readfirstlane(st + SL::B + (NW * i + wave) * 1024));
     } else if (c < NA + NB + NASC) {
       const int i = c - NA - NB;
       dma4(p.A_scale + (size_t)kt * 4, asc_off[i],
@@ -406,7 +407,7 @@ __global__ __launch_bounds__(256) void gg_mfma_kernel(GemmArgs p) {
   auto flush = [&](uint8_t* dst, int64_t pitch, int col0b, int rowb) __attribute__((always_inline)) {
     __syncthreads();
 #pragma unroll 4
-    for (int q = tid; q < BM * EL::CPR; q += 256) {
+    for (int q = tid; q < BM * EL::CPR; q += NT) {
       const int m = q / EL::CPR, cb = (q % EL::CPR) * 16;
       if (m < rows && col0b + cb < rowb) {
         const int64_t sl = ring_slot(p.head, seg, row0 + m, p.C);
@@ -481,7 +482,7 @@ static hipError_t run_mfma(const GemmArgs& a, int max_tiles, hipStream_t st) {
   }
   const int64_t vmax = (int64_t)max_tiles * nt;          // bound on live tiles
   const int64_t grid = 8 * ((vmax + 7) / 8);
-  kern<<<(unsigned)grid, 256, lds, st>>>(a);
+  kern<<<(unsigned)grid, WM * WN * 64, lds, st>>>(a);
   return hipGetLastError();
 }
 
@@ -560,11 +561,12 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
 //  * 128 x 256, 128-byte K slices, 3 stages: one row tile holds every row of an
 //    expert with up to 128 rows, so each weight is read from HBM once; the
 //    2,048-token layer (64 rows per expert on average) is bound by that stream.
-//  * 256 x 256, 64-byte K slices, 4 stages (128 KB), 128 x 128 per wave: with
-//    many rows per expert every row tile re-reads the weights and the kernel is
-//    bound inside the CU.  Per 32-wide K stage a SIMD runs 32 MFMAs (1024 clocks)
-//    while LDS serves 64 KB of fragment reads and 32 KB of copies (768 clocks at
-//    128 B/clock); the 128 x 256 tile needs 1152 LDS clocks per 1024 MFMA clocks.
+//  * 256 x 256, 64-byte K slices, 4 stages (128 KB), eight waves of 128 x 64 (two
+//    per SIMD, so that one wave's MFMAs run while the other waits): with many
+//    rows per expert every row tile re-reads the weights and the kernel is bound
+//    inside the CU.  Per 32-wide K stage a SIMD runs 32 MFMAs (1024 clocks) while
+//    LDS serves 96 KB of fragment reads and 32 KB of copies (512 clocks at 256
+//    B/clock).
 // MX keeps the first shape (its stages hold whole 128-element scale groups).
 constexpr int MFMA_BM = 128, MFMA_BM_BIG = 256;
 constexpr int BIG_ROWS_MIN = 256;   // mean rows per expert from which the 256-row tile is used
@@ -645,11 +647,11 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
   g2.out = (uint8_t*)ring_y;
   g2.out_scale = nullptr;
   g2.saved_au = nullptr;
-  if (big) err = run_mfma<MFMA_BM_BIG, 256, 2, 2, 64, true, false, 4>(g1, max_tiles, st);
+  if (big) err = run_mfma<MFMA_BM_BIG, 256, 2, 4, 64, true, false, 4>(g1, max_tiles, st);
   else if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, 128, true, false, 3>(g1, max_tiles, st);
   else err = run_mfma<MFMA_BM, 256, 2, 2, 128, true, true, 3>(g1, max_tiles, st);
   if (err != hipSuccess || (err = mark(1)) != hipSuccess) return err;
-  if (big) err = run_mfma<MFMA_BM_BIG, 256, 2, 2, 64, false, false, 4>(g2, max_tiles, st);
+  if (big) err = run_mfma<MFMA_BM_BIG, 256, 2, 4, 64, false, false, 4>(g2, max_tiles, st);
   else if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, 128, false, false, 3>(g2, max_tiles, st);
   else err = run_mfma<MFMA_BM, 256, 2, 2, 128, false, true, 3>(g2, max_tiles, st);
   if (err != hipSuccess) return err;
