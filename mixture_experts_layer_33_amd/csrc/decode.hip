@@ -169,17 +169,42 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_k1(DecodeArgs p) {
   constexpr int d = NQ * 512;
 
   for (int v = tid; v < B * d / 8; v += DEC_THREADS) ((u32x4*)xs)[v] = ((const u32x4*)p.x)[v];
-  // routing in LDS, one wavefront per token
+  for (int w = tid; w < (E + 31) / 32; w += DEC_THREADS) bits[w] = 0u;
+  __syncthreads();
+  // The shared expert's rows need no routing: while wavefronts 0..B-1 route one
+  // token each, the other wavefronts stream them (when B fills the workgroup, every
+  // wavefront streams them after the routing).
+  auto shared_rows = [&](int first, int stride) __attribute__((always_inline)) {
+    for (int i = first; i < fs; i += stride) {
+      u32x4 wg[NQ], wu[NQ];
+      load_row<NQ>(p.ws_gate + (int64_t)i * d, wg);
+      load_row<NQ>(p.ws_up + (int64_t)i * d, wu);
+      for (int b = 0; b < B; ++b) {
+        float sa, su;
+        part_dot2<NQ>(wg, wu, xs + b * d, sa, su);
+        const float a = wave_sum(sa), u = wave_sum(su);
+        if (lane == 0) p.hs[b * fs + i] = silu(a) * u;
+      }
+    }
+  };
+  const int nr = nwave - min(B, nwave);   // wavefronts of a workgroup that do not route
+  if (nr > 0 && wave >= B) shared_rows(blockIdx.x * nr + (wave - B), gridDim.x * nr);
+  // routing, one wavefront per token.  The logits (four partial planes + bias) of
+  // all of the lane's experts are loaded unconditionally (indices clamped, values
+  // past E masked afterwards), so the loads go out together instead of one guarded
+  // group after another.
   for (int b = wave; b < B; b += nwave) {
     int choice, rank;
     float gate;
     const float* l0 = p.logits + (int64_t)b * E;
     const int64_t ps = (int64_t)B * E;   // stride between the partial-logit planes
-    wave_route_row_f<16>(
-        [&](int e) {
-          return (((l0[e] + l0[ps + e]) + l0[2 * ps + e]) + l0[3 * ps + e]) + (p.b_r ? p.b_r[e] : 0.f);
-        },
-        E, k, choice, rank, gate);
+    float lv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = min(lane + 64 * i, E - 1);
+      lv[i] = (((l0[e] + l0[ps + e]) + l0[2 * ps + e]) + l0[3 * ps + e]) + (p.b_r ? p.b_r[e] : 0.f);
+    }
+    wave_route_row_f<16>([&](int e) { return lv[(e - lane) >> 6]; }, E, k, choice, rank, gate);
     if (lane < k) {
       sel[b * DEC_KMAX + rank] = choice;             // ascending expert id
       if (blockIdx.x == 0) {
@@ -188,7 +213,6 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_k1(DecodeArgs p) {
       }
     }
   }
-  for (int w = tid; w < (E + 31) / 32; w += DEC_THREADS) bits[w] = 0u;
   __syncthreads();
   for (int q = tid; q < B * k; q += DEC_THREADS) {
     const int e = sel[(q / k) * DEC_KMAX + q % k];
@@ -206,21 +230,12 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_k1(DecodeArgs p) {
     }
   }
   __syncthreads();
-  // the shared expert's rows, then the selected experts' rows, as one sequence of
-  // rows dealt round-robin to the wavefronts
-  for (int i = gw; i < fs; i += W) {
-    u32x4 wg[NQ], wu[NQ];
-    load_row<NQ>(p.ws_gate + (int64_t)i * d, wg);
-    load_row<NQ>(p.ws_up + (int64_t)i * d, wu);
-    for (int b = 0; b < B; ++b) {
-      float sa, su;
-      part_dot2<NQ>(wg, wu, xs + b * d, sa, su);
-      const float a = wave_sum(sa), u = wave_sum(su);
-      if (lane == 0) p.hs[b * fs + i] = silu(a) * u;
-    }
-  }
+  // the shared expert's rows (if the routing did not overlap them), then the selected
+  // experts' rows, as one sequence of rows dealt round-robin to the wavefronts
+  const int first = nr > 0 ? gw : gw - fs % W + (gw < fs % W ? W : 0);
+  if (nr == 0) shared_rows(gw, W);
   const int U = *nuniq;
-  for (int item = gw - fs % W + (gw < fs % W ? W : 0); item < U * f; item += W) {
+  for (int item = first; item < U * f; item += W) {
     const int e = uniq[item / f], i = item % f;
     u32x4 wg[NQ], wu[NQ];
     load_row<NQ>(p.w_gate + ((int64_t)e * f + i) * d, wg);
