@@ -561,12 +561,14 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
 //  * 128 x 256, 128-byte K slices, 3 stages: one row tile holds every row of an
 //    expert with up to 128 rows, so each weight is read from HBM once; the
 //    2,048-token layer (64 rows per expert on average) is bound by that stream.
-//  * 256 x 256, 64-byte K slices, 4 stages (128 KB), eight waves of 128 x 64 (two
+//  * 256 x 256, 128-byte K slices, 2 stages (128 KB), eight waves of 64 x 128 (two
 //    per SIMD, so that one wave's MFMAs run while the other waits): with many
 //    rows per expert every row tile re-reads the weights and the kernel is bound
-//    inside the CU.  Per 32-wide K stage a SIMD runs 32 MFMAs (1024 clocks) while
-//    LDS serves 96 KB of fragment reads and 32 KB of copies (512 clocks at 256
-//    B/clock).
+//    inside the CU, by the rate at which L2 serves the stages.  Whole 128-byte
+//    lines per copy and one barrier per 64 K measured ~2 % faster than 64-byte
+//    slices in 4 stages.  Per 64-wide K stage a SIMD runs 64 MFMAs (2048 clocks)
+//    while LDS serves 192 KB of fragment reads and 64 KB of copies (1024 clocks at
+//    256 B/clock).
 // MX keeps the first shape (its stages hold whole 128-element scale groups).
 constexpr int MFMA_BM = 128, MFMA_BM_BIG = 256;
 constexpr int BIG_ROWS_MIN = 256;   // mean rows per expert from which the 256-row tile is used
@@ -647,11 +649,11 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
   g2.out = (uint8_t*)ring_y;
   g2.out_scale = nullptr;
   g2.saved_au = nullptr;
-  if (big) err = run_mfma<MFMA_BM_BIG, 256, 2, 4, 64, true, false, 4>(g1, max_tiles, st);
+  if (big) err = run_mfma<MFMA_BM_BIG, 256, 4, 2, 128, true, false, 2>(g1, max_tiles, st);
   else if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, 128, true, false, 3>(g1, max_tiles, st);
   else err = run_mfma<MFMA_BM, 256, 2, 2, 128, true, true, 3>(g1, max_tiles, st);
   if (err != hipSuccess || (err = mark(1)) != hipSuccess) return err;
-  if (big) err = run_mfma<MFMA_BM_BIG, 256, 2, 4, 64, false, false, 4>(g2, max_tiles, st);
+  if (big) err = run_mfma<MFMA_BM_BIG, 256, 4, 2, 128, false, false, 2>(g2, max_tiles, st);
   else if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, 128, false, false, 3>(g2, max_tiles, st);
   else err = run_mfma<MFMA_BM, 256, 2, 2, 128, false, true, 3>(g2, max_tiles, st);
   if (err != hipSuccess) return err;
