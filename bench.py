@@ -216,7 +216,45 @@ def skew_fwd_bwd(torch, moe, steps):
             "bwd_alg_bytes": bwd_bytes, "bwd_hbm_frac": round(bwd_bytes / (bm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bwd_mfma_frac": round(bwd_flops / (bm * 1e-3) / 1e12 / BF16_PEAK_TFS, 4),
             "experts_used": used, "max_load": int(counts.max()), "mean_load": round(float(n / E), 2),
-            "max_over_mean": round(float(counts.max() / (n / E)), 2)}
+            "max_over_mean": round(float(counts.max() / (n / E)), 2),
+            "ring_stack": ring_stack(torch, moe, inp, layer, steps, fm, bm)}
+
+
+def ring_stack(torch, moe, inp, layer, steps, fwd_ms_1, bwd_ms_1, L=4):
+    """L layers of the skewed shape sharing one ring (the same weights in every layer): the
+    forwards advance the head, the backward consumes the layers last first with nothing
+    recomputed.  Reported next to the single-layer figures: per-layer time should match."""
+    import numpy as np
+    s1 = layer.shape
+    progress(f"ring stack: {L} layers sharing one ring")
+    st = moe.RingStack(L, s1.tokens, s1.hidden, s1.experts, s1.top_k, s1.ffn)
+    w = [(inp.w_router, inp.b_router, inp.w_gate, inp.w_up, inp.w_down)] * L
+    dw = (layer.bufs["dw_gate"], layer.bufs["dw_up"], layer.bufs["dw_down"], layer.bufs["dw_router"])
+    for _ in range(2):
+        st.forward(inp.x, w)
+        st.backward(inp.dy, w, dw=dw)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        st.forward(inp.x, w)
+        ev[i][1].record()
+        st.backward(inp.dy, w, dw=dw)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    fm = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    bm = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+    C = st.shape.capacity
+    resident = C * (s1.hidden * 2 + 2 * s1.ffn * 2 + 4)   # ring rows, saved [A|U], slot map
+    out = {"layers": L, "ring_rows": C, "ring_resident_bytes": resident,
+           "fwd_ms_median": round(fm, 4), "bwd_ms_median": round(bm, 4),
+           "fwd_ms_per_layer": round(fm / L, 4), "bwd_ms_per_layer": round(bm / L, 4),
+           "fwd_per_layer_over_single": round(fm / L / fwd_ms_1, 3),
+           "bwd_per_layer_over_single": round(bm / L / bwd_ms_1, 3),
+           "tokens_per_s_fwd_bwd": round(s1.tokens / ((fm + bm) * 1e-3), 1)}
+    del st
+    torch.cuda.empty_cache()
+    return out
 
 
 def secondary(torch, moe, steps):

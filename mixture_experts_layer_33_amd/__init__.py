@@ -7,6 +7,7 @@ with the C names take torch tensors for every buffer (outputs included);
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass, field
 from typing import Dict, Optional
 
@@ -229,3 +230,82 @@ class Layer:
                      b["expert_offset"], b["copy_slot"], b["slot_copy"], head, b["saved_au"],
                      w_gate, w_up, w_down, dx, dwg, dwu, dwd, dwr, self._ws(OP_BACKWARD))
         return dx, dwg, dwu, dwd, dwr
+
+
+class RingStack:
+    """L MoE layers of one shape sharing one token ring (dzen.guru page, ring-buffer
+    paragraph of "Три решения…": a fixed ring whose head advances layer by layer,
+    walked in reverse by the backward).
+
+    Layer l dispatches its n = T*k copies at head_l = (head_0 + l*n) mod C, so the
+    ring keeps every layer's dispatched rows and saved [A|U] until the backward,
+    which consumes the layers last first (the newest segment first) and, inside a
+    layer, experts E-1 -> 0 and rows last slot first: nothing is recomputed.  The
+    layers are chained directly (x_{l+1} = y_l).  C >= L*n, so no segment is
+    overwritten while it is live; segments may wrap past the end of the ring.
+    Every step is one of the library's calls; this class only keeps the buffers."""
+
+    def __init__(self, L, T, d, E, k, f, C=None, device="cuda"):
+        n = T * k
+        C = C if C is not None else L * int(math.ceil(1.25 * n))
+        if C < L * n:
+            raise ValueError(f"ring of {C} rows cannot hold {L} layers of {n} copies")
+        self.L, self.n = L, n
+        self.shape = make_shape(T, d, E, k, f, C)
+        self.device = torch.device(device)
+        dev = self.device
+        z = lambda *s, dtype=torch.int32: torch.zeros(s, dtype=dtype, device=dev)
+        self.ring_x = z(C, d, dtype=torch.bfloat16)
+        self.saved_au = z(C, 2 * f, dtype=torch.bfloat16)
+        self.ring_y = z(C, d, dtype=torch.bfloat16)
+        self.slot_copy = z(C)
+        self.per = [dict(idx=z(T, k), gate=z(T, k, dtype=torch.float32), cnt=z(E),
+                         off=z(E + 1), cs=z(T, k), x=z(T, d, dtype=torch.bfloat16),
+                         y=z(T, d, dtype=torch.bfloat16)) for _ in range(L)]
+        self.ws = {op: z(max(workspace_bytes(self.shape, op), 256), dtype=torch.uint8)
+                   for op in (OP_ROUTE, OP_DISPATCH, OP_EXPERT_FFN, OP_BACKWARD)}
+        self.heads = [0] * L
+
+    def forward(self, x, weights, head0=0):
+        """weights[l] = (w_router, b_router, w_gate, w_up, w_down).  Returns y_{L-1}."""
+        s, C = self.shape, self.shape.capacity
+        self.heads = [(head0 + l * self.n) % C for l in range(self.L)]
+        cur = x
+        for l, (w_r, b_r, w_g, w_u, w_d) in enumerate(weights):
+            p, h = self.per[l], self.heads[l]
+            p["x"].copy_(cur)
+            moe_route(s, p["x"], w_r, b_r, p["idx"], p["gate"], p["cnt"], self.ws[OP_ROUTE])
+            moe_dispatch(s, p["x"], p["idx"], h, self.ring_x, None, p["off"], p["cs"],
+                         self.slot_copy, self.ws[OP_DISPATCH])
+            moe_expert_ffn(s, self.ring_x, None, p["off"], h, w_g, w_u, w_d, None, None, None,
+                           self.ring_y, self.saved_au, self.ws[OP_EXPERT_FFN])
+            moe_combine(s, self.ring_y, p["cs"], p["gate"], p["y"])
+            cur = p["y"]
+        return cur
+
+    def backward(self, dy, weights, dw=None):
+        """Layers L-1 -> 0 (each layer's input gradient is kept as per[l]["dx"]).  Returns
+        dx_0 and, per layer, (dw_gate, dw_up, dw_down, dw_router);
+        with `dw` given (one set of gradient buffers) every layer writes into it and the
+        list holds that set L times (the caller consumes each layer's before the next)."""
+        s = self.shape
+        T, d, E, f = s.tokens, s.hidden, s.experts, s.ffn
+        dev = self.device
+        grads = [None] * self.L
+        cur = dy
+        for l in reversed(range(self.L)):
+            w_r, _, w_g, w_u, w_d = weights[l]
+            p = self.per[l]
+            g = dw if dw is not None else (
+                torch.empty(E, f, d, dtype=torch.bfloat16, device=dev),
+                torch.empty(E, f, d, dtype=torch.bfloat16, device=dev),
+                torch.empty(E, d, f, dtype=torch.bfloat16, device=dev),
+                torch.empty(E, d, dtype=torch.float32, device=dev))
+            dx = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+            moe_backward(s, cur, p["x"], w_r, p["idx"], p["gate"], self.ring_x, p["off"],
+                         p["cs"], self.slot_copy, self.heads[l], self.saved_au, w_g, w_u, w_d,
+                         dx, g[0], g[1], g[2], g[3], self.ws[OP_BACKWARD])
+            grads[l] = g
+            p["dx"] = dx
+            cur = dx
+        return cur, grads

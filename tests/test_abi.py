@@ -130,3 +130,12 @@ def test_workspace_sizes_of_the_workloads():
             assert b % 256 == 0 and b < (8 << 30)
     s = moe.make_shape(8, 7168, 256, 8, 2048, fs=2048)
     assert moe.workspace_bytes(s, _lib.OP_DECODE) >= 8 * 8 * 2048 * 4
+
+
+def test_ring_stack_capacity():
+    """A shared ring must hold every layer's copies; the default is 1.25x each."""
+    with pytest.raises(ValueError):
+        moe.RingStack(3, T=16, d=128, E=8, k=2, f=256, C=3 * 32 - 1, device="cpu")
+    st = moe.RingStack(3, T=16, d=128, E=8, k=2, f=256, device="cpu")
+    assert st.shape.capacity == 3 * 40 and st.n == 32
+    assert tuple(st.ring_x.shape) == (120, 128) and tuple(st.saved_au.shape) == (120, 512)
