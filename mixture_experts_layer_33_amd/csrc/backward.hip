@@ -596,8 +596,9 @@ __global__ void zero_fill_kernel(uint32_t* __restrict__ p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
 }
 
-// 128 x 128 tiles, 2 stages, 4 workgroups per CU
-constexpr int WG_NJ = 2, WG_WS = 2, WG_OCC = 4;
+// 128 x 256 tiles, 2 stages, 3 workgroups per CU (measured best of 128 x 128 / 128 x 256,
+// 2 / 3 stages, 2 to 4 workgroups per CU)
+constexpr int WG_NJ = 4, WG_WS = 2, WG_OCC = 3;
 
 static hipError_t run_wgrad(const WgradArgs& a, hipStream_t st) {
   auto kern = wgrad_kernel<WG_NJ, WG_WS, WG_OCC>;
