@@ -314,15 +314,32 @@ __global__ __launch_bounds__(128) void router_wgrad_kernel(const int32_t* __rest
   if (v * 8 >= d) return;
   const int32_t seg = offset[e], n = offset[e + 1] - seg;
   float acc[8] = {};
-  for (int i = n - 1; i >= 0; --i) {
-    const int64_t s = ring_slot(head, seg, i, C);
-    const float l = dl_slot[s];
-    const u32x4 w = ((const u32x4*)(ring_x + s * d))[v];
+  auto add = [&](float l, const u32x4& w) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       acc[2 * q] = fmaf(l, lo_bf(w[q]), acc[2 * q]);
       acc[2 * q + 1] = fmaf(l, hi_bf(w[q]), acc[2 * q + 1]);
     }
+  };
+  // rows last slot first; the loads of RB rows are issued together, then added in
+  // that same order (a hot expert has over a thousand rows)
+  constexpr int RB = 16;
+  int i = n - 1;
+  for (; i >= RB - 1; i -= RB) {
+    float l[RB];
+    u32x4 w[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int64_t s = ring_slot(head, seg, i - u, C);
+      l[u] = dl_slot[s];
+      w[u] = ((const u32x4*)(ring_x + s * d))[v];
+    }
+#pragma unroll
+    for (int u = 0; u < RB; ++u) add(l[u], w[u]);
+  }
+  for (; i >= 0; --i) {
+    const int64_t s = ring_slot(head, seg, i, C);
+    add(dl_slot[s], ((const u32x4*)(ring_x + s * d))[v]);
   }
   f32x4* dst = (f32x4*)(dw_r + (int64_t)e * d + v * 8);
   dst[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
