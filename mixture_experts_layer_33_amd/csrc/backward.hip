@@ -16,7 +16,8 @@
 //                       SwiGLU backward -> dA|dU (bf16), g*h (bf16), row partials of dg
 //   dgrad_kernel<UP>    [dA|dU] x [W_gate[e]; W_up[e]] (K = 2f rows) -> dX per copy (bf16)
 //   token_kernel        dg, dl per token; dx = sum_j dX[copy] + dl_j W_r[e_j] (bf16)
-//   router_wgrad        dW_r[e] = sum over the segment (last slot first) of dl x  (fp32)
+//   router_wgrad_*      dW_r[e] = sum over the segment (last slot first) of dl x  (fp32),
+//                       per 128-row tile, then over the expert's tiles (last first)
 //   gather_to_ring      dy rows copied into ring order, one per copy (t, j)
 //   wgrad_kernel        dW_down[e] = dY_e^T (g H)_e;  [dW_gate;dW_up][e] = [dA|dU]_e^T X_e
 // The dgrad tiles are 128 x 128 with K in 64-element slices; the weights, whose K
@@ -304,15 +305,24 @@ __global__ __launch_bounds__(256) void token_kernel(const int32_t* __restrict__ 
 }
 
 // dW_r[e][c] = sum over the segment's rows, last slot first, of dl * x  (fp32).
-__global__ __launch_bounds__(128) void router_wgrad_kernel(const int32_t* __restrict__ offset,
-                                                           int64_t head, int64_t C,
-                                                           const bf16_t* __restrict__ ring_x,
-                                                           const float* __restrict__ dl_slot,
-                                                           int d, float* __restrict__ dw_r) {
-  const int e = blockIdx.x;
+// dW_r[e] = sum over the expert's rows, last slot first, of dl x.  Step 1: every
+// 128-row tile of the tile list (expert-major, rows ascending) sums its rows, last
+// first, into an fp32 partial; the expert's first tile records its index.  Step 2
+// sums each expert's partials, last tile first.  A hot expert's rows are thus spread
+// over many workgroups, in a fixed order.
+__global__ __launch_bounds__(128) void router_wgrad_part_kernel(
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles,
+    const int32_t* __restrict__ offset, int64_t head, int64_t C,
+    const bf16_t* __restrict__ ring_x, const float* __restrict__ dl_slot, int d,
+    float* __restrict__ part, int32_t* __restrict__ first_tile) {
+  const int mt = blockIdx.x;
+  if (mt >= *ntiles) return;
+  const int e = tiles[2 * mt], row0 = tiles[2 * mt + 1];
   const int v = blockIdx.y * 128 + threadIdx.x;   // 8 columns per thread
+  if (row0 == 0 && blockIdx.y == 0 && threadIdx.x == 0) first_tile[e] = mt;
   if (v * 8 >= d) return;
-  const int32_t seg = offset[e], n = offset[e + 1] - seg;
+  const int32_t seg = offset[e];
+  const int rows = min(BT, offset[e + 1] - seg - row0);
   float acc[8] = {};
   auto add = [&](float l, const u32x4& w) __attribute__((always_inline)) {
 #pragma unroll
@@ -321,16 +331,15 @@ __global__ __launch_bounds__(128) void router_wgrad_kernel(const int32_t* __rest
       acc[2 * q + 1] = fmaf(l, hi_bf(w[q]), acc[2 * q + 1]);
     }
   };
-  // rows last slot first; the loads of RB rows are issued together, then added in
-  // that same order (a hot expert has over a thousand rows)
+  // the loads of RB rows are issued together, then added in the same order
   constexpr int RB = 16;
-  int i = n - 1;
+  int i = rows - 1;
   for (; i >= RB - 1; i -= RB) {
     float l[RB];
     u32x4 w[RB];
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
-      const int64_t s = ring_slot(head, seg, i - u, C);
+      const int64_t s = ring_slot(head, seg, row0 + i - u, C);
       l[u] = dl_slot[s];
       w[u] = ((const u32x4*)(ring_x + s * d))[v];
     }
@@ -338,12 +347,28 @@ __global__ __launch_bounds__(128) void router_wgrad_kernel(const int32_t* __rest
     for (int u = 0; u < RB; ++u) add(l[u], w[u]);
   }
   for (; i >= 0; --i) {
-    const int64_t s = ring_slot(head, seg, i, C);
+    const int64_t s = ring_slot(head, seg, row0 + i, C);
     add(dl_slot[s], ((const u32x4*)(ring_x + s * d))[v]);
   }
-  f32x4* dst = (f32x4*)(dw_r + (int64_t)e * d + v * 8);
+  f32x4* dst = (f32x4*)(part + (int64_t)mt * d + v * 8);
   dst[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
   dst[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+}
+
+__global__ __launch_bounds__(256) void router_wgrad_sum_kernel(
+    const int32_t* __restrict__ offset, const int32_t* __restrict__ first_tile,
+    const float* __restrict__ part, int d, float* __restrict__ dw_r) {
+  const int e = blockIdx.x;
+  const int v = blockIdx.y * 256 + threadIdx.x;   // 4 columns per thread
+  if (v * 4 >= d) return;
+  const int n = offset[e + 1] - offset[e];
+  const int nt = (n + BT - 1) / BT;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (nt > 0) {
+    const int t0 = first_tile[e];
+    for (int c = nt - 1; c >= 0; --c) acc += *(const f32x4*)(part + (int64_t)(t0 + c) * d + v * 4);
+  }
+  *(f32x4*)(dw_r + (int64_t)e * d + v * 4) = acc;
 }
 
 // ----------------------------------------------------------------------------- wgrad
@@ -586,7 +611,7 @@ __global__ __launch_bounds__(256) void gather_to_ring_kernel(const bf16_t* __res
 static int bwd_max_tiles(int64_t n, int E) { return (int)((n + BT - 1) / BT) + E; }
 
 struct BwdLayout {
-  size_t tiles, dau, gh, dgpart, dxc, dl, zero, rdy, total;
+  size_t tiles, dau, gh, dgpart, dxc, dl, zero, rdy, rpart, rfirst, total;
 };
 
 static BwdLayout bwd_layout(int64_t T, int64_t C, int d, int E, int k, int f) {
@@ -599,6 +624,8 @@ static BwdLayout bwd_layout(int64_t T, int64_t C, int d, int E, int k, int f) {
   L.dgpart = o; o += al((size_t)C * (f / BT) * 4);
   L.dxc = o;   o += al((size_t)C * d * 2);
   L.dl = o;    o += al((size_t)C * 4);
+  L.rpart = o; o += al((size_t)bwd_max_tiles(T * k, E) * d * 4);   // router-gradient tile partials
+  L.rfirst = o; o += al((size_t)E * 4);
   L.zero = o;  o += 1024;   // a zero row for the weight-gradient stages
   L.rdy = o;   o += al((size_t)C * d * 2);   // dy in ring order
   L.total = o;
@@ -686,8 +713,12 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
   dgrad_kernel<false><<<dim3(d / BT, max_tiles), 256, 0, st>>>(b);
   token_kernel<<<(unsigned)T, 256, 0, st>>>(copy_slot, topk_idx, topk_gate, dgpart, f / BT, dxc,
                                             w_r, d, k, dl, (bf16_t*)dx);
-  router_wgrad_kernel<<<dim3(E, (d / 8 + 127) / 128), 128, 0, st>>>(
-      expert_offset, head, C, (const bf16_t*)ring_x, dl, d, dw_r);
+  float* rpart = (float*)(w + L.rpart);
+  int32_t* rfirst = (int32_t*)(w + L.rfirst);
+  router_wgrad_part_kernel<<<dim3(max_tiles, (d / 8 + 127) / 128), 128, 0, st>>>(
+      tiles, ntiles, expert_offset, head, C, (const bf16_t*)ring_x, dl, d, rpart, rfirst);
+  router_wgrad_sum_kernel<<<dim3(E, (d / 4 + 255) / 256), 256, 0, st>>>(expert_offset, rfirst,
+                                                                        rpart, d, dw_r);
   zero_fill_kernel<<<1, 256, 0, st>>>((uint32_t*)(w + L.zero), 256);
   bf16_t* rdy = (bf16_t*)(w + L.rdy);
   gather_to_ring_kernel<<<(unsigned)T, 256, 0, st>>>((const bf16_t*)dy, copy_slot, k, d, rdy);
