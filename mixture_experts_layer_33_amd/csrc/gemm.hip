@@ -95,6 +95,7 @@ struct GemmArgs {
   uint8_t* out;            // SWIGLU: H (bf16 [C, f], or MX codes [C, f]); else ring_y bf16 [C, N]
   uint8_t* out_scale;      // SWIGLU + MX: H scales [C, f/32]
   uint16_t* saved_au;      // SWIGLU + bf16: [C, 2f] or null
+  int rotate;              // 1: tile L starts its K loop at step L mod (K steps), see kstart_rotates
 };
 
 // Tile order.  The grid is 1-D; workgroup b runs on XCD b % 8 (round-robin
@@ -232,9 +233,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
       bsc_off[i] = (uint32_t)min(n0 + rr, p.N - 1) * Ks;
     }
   }
-  // Copy c (0 <= c < L) of this wave for K step kt, into ring buffer kt % S.
-  auto issue_one = [&](int kt, int c) __attribute__((always_inline)) {
-    const uint32_t st = lds0 + (uint32_t)(kt % S) * SL::SIZE;
+  // K steps are taken in the order s0, s0 + 1, ..., KT - 1, 0, ..., s0 - 1: with
+  // rotation, tiles that run at the same time read different K slices of their
+  // weight rows (a fixed order per tile, so results stay deterministic).
+  const int KT = (int)(Kb / KB);
+  const int s0 = p.rotate ? (int)(((int64_t)mt * nt_cols + ct) % KT) : 0;
+  // Copy c (0 <= c < L) of this wave for the i-th K step of the loop, into ring
+  // buffer i % S.
+  auto issue_one = [&](int i_, int c) __attribute__((always_inline)) {
+    const uint32_t st = lds0 + (uint32_t)(i_ % S) * SL::SIZE;
+    const int kt = i_ + s0 >= KT ? i_ + s0 - KT : i_ + s0;
     if (c < NA) {
       dma16(p.A + (size_t)kt * KB, a_off[c], __builtin_amdgcn_readfirstlane(st + SL::A + (NW * c + wave) * 1024));
     } else if (c < NA + NB) {
@@ -354,7 +362,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   // One barrier per stage: it publishes stage kt (every wave waited for its own
   // copies) and retires the buffer of stage kt-1, which the copies of stage kt+S-1
   // then overwrite.
-  const int KT = (int)(Kb / KB);
   for (int s = 0; s < S - 1 && s < KT; ++s) issue(s);
   if constexpr (S < 4) {
     // Barrier at the start of each stage; the stage's copies (K step kt + S - 1)
@@ -577,6 +584,26 @@ static bool use_big(int dtype, int64_t n, int E) {
   return dtype == 1 && n >= (int64_t)BIG_ROWS_MIN * E;
 }
 
+// Rotation of the K loop's starting step per tile (measured on gfx950, gate/up | down
+// GEMM in ms without -> with):
+//  * many row tiles per expert (the per-GPU share shapes, where every weight panel is
+//    re-read by each row tile and the stage rate through L2 bounds the kernel): tiles
+//    that run together read different K slices, bf16 1.042 -> 1.007 | 0.503 -> 0.503,
+//    MX 0.923 -> 0.873 | 0.435 -> 0.423;
+//  * the bf16 down GEMM with one row tile per expert: a tile's copies of one K step
+//    read 128 bytes from each of 256 weight rows 4 KB (2 KB) apart, all at the same
+//    offset inside a 4 KB page, which crowds them onto a subset of the HBM channels;
+//    rotation spreads them: 2,048 tokens 1.504 -> 1.421, skewed 8,192 tokens 1.517 ->
+//    1.484 (a bare copy of that pattern: 5.4 -> 6.1 TB/s);
+//  * the gate/up GEMM with one row tile per expert loses (2.582 -> 2.605 at 2,048 tokens,
+//    2.218 -> 2.298 skewed): the column tiles of a row tile then no longer read the same
+//    token-row slices at the same time, so those rows are held in L2 longer; the MX
+//    down GEMM there is unchanged within noise (0.907 -> 0.918), so it is not rotated.
+static int kstart_rotates(bool swiglu, int dtype, int64_t n, int E, int BM) {
+  if (n >= 2 * (int64_t)BM * E) return 1;
+  return (!swiglu && dtype == 1) ? 1 : 0;
+}
+
 static int max_tiles_for(int64_t n, int E, int BM) { return (int)((n + BM - 1) / BM) + E; }
 
 size_t ffn_workspace_bytes(int64_t n, int64_t C, int d, int E, int f, int dtype) {
@@ -649,6 +676,8 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
   g2.out = (uint8_t*)ring_y;
   g2.out_scale = nullptr;
   g2.saved_au = nullptr;
+  g1.rotate = kstart_rotates(true, dtype, n, E, BM);
+  g2.rotate = kstart_rotates(false, dtype, n, E, BM);
   if (big) err = run_mfma<MFMA_BM_BIG, 256, 4, 2, 128, true, false, 2>(g1, max_tiles, st);
   else if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, 128, true, false, 3>(g1, max_tiles, st);
   else err = run_mfma<MFMA_BM, 256, 2, 2, 128, true, true, 3>(g1, max_tiles, st);
@@ -656,6 +685,7 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
   if (big) err = run_mfma<MFMA_BM_BIG, 256, 4, 2, 128, false, false, 2>(g2, max_tiles, st);
   else if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, 128, false, false, 3>(g2, max_tiles, st);
   else err = run_mfma<MFMA_BM, 256, 2, 2, 128, false, true, 3>(g2, max_tiles, st);
+#undef G2
   if (err != hipSuccess) return err;
   return mark(2);
 }
