@@ -38,7 +38,10 @@ __global__ __launch_bounds__(64) void dispatch_hist_kernel(const int32_t* __rest
   }
 }
 
-// One workgroup of 1024 threads, one expert per thread (E <= 1024).
+// One workgroup of 1024 threads, one expert per thread (E <= 1024).  A thread walks
+// its expert's column of chunk counts twice (totals, then bases), issuing the loads of
+// 16 chunks at a time so that one memory latency covers 16 chunks.
+constexpr int SCAN_BATCH = 16;
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ hist, int nch,
                                                              int E,
                                                              int32_t* __restrict__ expert_offset) {
@@ -46,10 +49,12 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
   const int e = threadIdx.x;
   int32_t run = 0;
   if (e < E)
-    for (int c = 0; c < nch; ++c) {
-      const int32_t h = hist[(int64_t)c * E + e];
-      hist[(int64_t)c * E + e] = run;
-      run += h;
+    for (int c0 = 0; c0 < nch; c0 += SCAN_BATCH) {
+      int32_t h[SCAN_BATCH];
+#pragma unroll
+      for (int i = 0; i < SCAN_BATCH; ++i) h[i] = c0 + i < nch ? hist[(int64_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < SCAN_BATCH; ++i) run += h[i];
     }
   sc[e] = e < E ? run : 0;
   __syncthreads();
@@ -63,7 +68,19 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
   const int32_t off = sc[e] - run;  // exclusive
   if (e < E) {
     expert_offset[e] = off;
-    for (int c = 0; c < nch; ++c) hist[(int64_t)c * E + e] += off;
+    // base[c][e] = off + copies of expert e in chunks before c
+    int32_t acc = off;
+    for (int c0 = 0; c0 < nch; c0 += SCAN_BATCH) {
+      int32_t h[SCAN_BATCH];
+#pragma unroll
+      for (int i = 0; i < SCAN_BATCH; ++i) h[i] = c0 + i < nch ? hist[(int64_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < SCAN_BATCH; ++i)
+        if (c0 + i < nch) {
+          hist[(int64_t)(c0 + i) * E + e] = acc;
+          acc += h[i];
+        }
+    }
   }
   if (e == E - 1) expert_offset[E] = sc[e];
 }

@@ -4,21 +4,23 @@
 // (dzen.guru page, "Что именно тормозило обучение MoE-моделей?").  The rule
 // (softmax over E, top-k, renormalise the k gates to sum 1) is the layer's
 // workload definition.  Everything here is fp32; bf16 tokens are widened exactly.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
 // ----------------------------------------------------------------------------
-// logits[t, e] = sum_i x[t, i] W_r[e, i] (+ b[e]).  64x64 output tile per
+// logits[t, e] = sum_i x[t, i] W_r[e, i] (the bias is added by the top-k kernel).  64x64 output tile per
 // workgroup, 256 threads, 4x4 outputs per thread, K staged through LDS in
 // steps of 32.  The K order is fixed, so the result is bitwise reproducible.
 constexpr int RT_M = 64, RT_N = 64, RT_K = 32;
 
 template <bool X_F32>
 __global__ __launch_bounds__(256) void router_logits_kernel(
-    const void* __restrict__ xv, const float* __restrict__ w, const float* __restrict__ bias,
-    float* __restrict__ logits, int64_t T, int d, int E) {
+    const void* __restrict__ xv, const float* __restrict__ w, float* __restrict__ logits,
+    int64_t T, int d, int E) {
   __shared__ float xs[RT_K][RT_M + 4];
   __shared__ float ws[RT_K][RT_N + 4];
   const int tid = threadIdx.x;
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = e0 + tx * 4 + j;
-      if (e < E) logits[t * E + e] = acc[i][j] + (bias ? bias[e] : 0.f);
+      if (e < E) logits[t * E + e] = acc[i][j];
     }
   }
 }
@@ -97,15 +99,19 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
 
 // BM tokens x 64 experts per workgroup; waves (BM/32) x 2, each a 32 x 32 tile
 // with one accumulator per plane; K in 64-element slices through double-buffered,
-// XOR-swizzled LDS.  logit = (acc_hi + acc_mid) + acc_lo (+ b).
+// XOR-swizzled LDS.  The K range is split over gridDim.z workgroups: split z sums
+// slices [z KT / KS, (z + 1) KT / KS) and writes partial plane z of the logits,
+// (acc_hi + acc_mid) + acc_lo; the top-k kernel adds the planes in order z = 0, 1, ...
+// and then the bias.  Two K slices are in flight while one is multiplied: slice
+// kt + 1 (requested during the previous slice) and kt + 2, in two register sets.
 constexpr int RM_K = 128;   // bytes of K per row per stage
 
 __device__ __forceinline__ int rswz(int r, int c) { return r * RM_K + ((c ^ (r & 7)) << 4); }
 
 template <int BM>
 __global__ __launch_bounds__(BM * 4) void router_mfma_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w3, const float* __restrict__ bias,
-    float* __restrict__ logits, int64_t T, int d, int E) {
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w3, float* __restrict__ logits,
+    int64_t T, int d, int E) {
   constexpr int NT = BM * 4, BNR = 192;          // threads; B rows = 3 planes x 64 experts
   constexpr int A_LD = BM * 8 / NT, B_LD = BNR * 8 / NT;
   __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * RM_K];
@@ -115,51 +121,46 @@ __global__ __launch_bounds__(BM * 4) void router_mfma_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lg = lane >> 5;
   const int64_t n = (int64_t)E * d;
+  const int KS = gridDim.z, z = blockIdx.z, KA = d / 64;
+  const int kb = (int)((int64_t)KA * z / KS);
+  const int KT = (int)((int64_t)KA * (z + 1) / KS) - kb;
   const bf16_t* a_src[A_LD];
   const bf16_t* b_src[B_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     const int q = tid + NT * i;
     const int64_t t = min(t0 + q / 8, T - 1);
-    a_src[i] = x + t * d + (q % 8) * 8;
+    a_src[i] = x + t * d + (int64_t)kb * 64 + (q % 8) * 8;
   }
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
     const int q = tid + NT * i, r = q / 8;
     const int e = min(e0 + r % 64, E - 1);
-    b_src[i] = w3 + (r / 64) * n + (int64_t)e * d + (q % 8) * 8;
+    b_src[i] = w3 + (r / 64) * n + (int64_t)e * d + (int64_t)kb * 64 + (q % 8) * 8;
   }
-  u32x4 ra[A_LD], rb[B_LD];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = *(const u32x4*)(a_src[i] + kt * 64);
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) rb[i] = *(const u32x4*)(b_src[i] + kt * 64);
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int q = tid + NT * i;
-      *(u32x4*)(As[buf] + rswz(q / 8, q % 8)) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int q = tid + NT * i;
-      *(u32x4*)(Bs[buf] + rswz(q / 8, q % 8)) = rb[i];
-    }
-  };
+  u32x4 ra0[A_LD], rb0[B_LD], ra1[A_LD], rb1[B_LD];
+#define R_LOAD(kt, RA, RB)                                                                   \
+  {                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) RA[i] = *(const u32x4*)(a_src[i] + (kt) * 64); \
+    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) RB[i] = *(const u32x4*)(b_src[i] + (kt) * 64); \
+  }
+#define R_STORE(buf, RA, RB)                                                                 \
+  {                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) {                                      \
+      const int q = tid + NT * i;                                                            \
+      *(u32x4*)(As[buf] + rswz(q / 8, q % 8)) = RA[i];                                       \
+    }                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) {                                      \
+      const int q = tid + NT * i;                                                            \
+      *(u32x4*)(Bs[buf] + rswz(q / 8, q % 8)) = RB[i];                                       \
+    }                                                                                        \
+  }
   f32x16 acc[3];
 #pragma unroll
   for (int p = 0; p < 3; ++p)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[p][r] = 0.f;
-  const int KT = d / 64;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
+  auto compute = [&](int cur) __attribute__((always_inline)) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int c = kk * 2 + lg;
@@ -171,17 +172,44 @@ __global__ __launch_bounds__(BM * 4) void router_mfma_kernel(
         acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[p], 0, 0, 0);
       }
     }
-    if (kt + 1 < KT) sstore(cur ^ 1);
+  };
+  R_LOAD(0, ra0, rb0);
+  if (KT > 1) R_LOAD(1, ra1, rb1);
+  R_STORE(0, ra0, rb0);
+  __syncthreads();
+  // LDS buffer 0 holds even slices, buffer 1 odd ones; each buffer is rewritten only
+  // after the barrier that follows its last read.
+  for (int kt = 0; kt < KT; kt += 2) {
+    if (kt + 2 < KT) R_LOAD(kt + 2, ra0, rb0);
+    compute(0);
+    if (kt + 1 >= KT) break;
+    R_STORE(1, ra1, rb1);
+    __syncthreads();
+    if (kt + 3 < KT) R_LOAD(kt + 3, ra1, rb1);
+    compute(1);
+    if (kt + 2 >= KT) break;
+    R_STORE(0, ra0, rb0);
     __syncthreads();
   }
+#undef R_LOAD
+#undef R_STORE
   const int e = e0 + wn * 32 + lr;
   if (e >= E) return;
-  const float be = bias ? bias[e] : 0.f;
+  float* out = logits + (int64_t)z * T * E;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int64_t t = t0 + wm * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-    if (t < T) logits[t * E + e] = (acc[0][r] + acc[1][r]) + acc[2][r] + be;
+    if (t < T) out[t * E + e] = (acc[0][r] + acc[1][r]) + acc[2][r];
   }
+}
+
+// Number of K splits of the bf16 router: enough workgroups (two fit per CU) to give
+// every CU two, keeping at least 8 K slices per split.
+static int router_ksplit(int64_t T, int E, int d) {
+  const int64_t tiles = ((T + 63) / 64) * ((E + 63) / 64);
+  int ks = (int)std::min<int64_t>(8, std::max<int64_t>(1, 512 / std::max<int64_t>(tiles, 1)));
+  while (ks > 1 && d / 64 / ks < 8) --ks;
+  return ks;
 }
 
 // ----------------------------------------------------------------------------
@@ -189,14 +217,23 @@ __global__ __launch_bounds__(BM * 4) void router_mfma_kernel(
 // ascending-id output order, renormalised gates.
 template <int VPL>
 __global__ __launch_bounds__(256) void router_topk_kernel(
-    const float* __restrict__ logits, int64_t T, int E, int k,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
+    const float* __restrict__ logits, int KS, const float* __restrict__ bias, int64_t T, int E,
+    int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  // logit = ((plane 0 + plane 1) + ...) + bias, every lane for its experts lane + 64 i
+  float lv[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = min(lane + 64 * i, E - 1);
+    float v = logits[t * E + e];
+    for (int zz = 1; zz < KS; ++zz) v += logits[((int64_t)zz * T + t) * E + e];
+    lv[i] = v + (bias ? bias[e] : 0.f);
+  }
   int choice, rank;
   float gate;
-  wave_route_row<VPL>(logits + t * E, E, k, choice, rank, gate);
+  wave_route_row_f<VPL>([&](int e) { return lv[(e - lane) >> 6]; }, E, k, choice, rank, gate);
   if (lane < k) {
     topk_idx[t * k + rank] = choice;
     topk_gate[t * k + rank] = gate;
@@ -212,43 +249,54 @@ __global__ __launch_bounds__(1024) void expert_count_kernel(const int32_t* __res
   extern __shared__ int32_t hist[];
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
-  for (int64_t c = threadIdx.x; c < n; c += blockDim.x) atomicAdd(&hist[idx[c]], 1);
+  // eight independent loads per thread before their atomics: one latency per 8 copies
+  for (int64_t c0 = threadIdx.x; c0 < n; c0 += 8 * (int64_t)blockDim.x) {
+    int32_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t c = c0 + (int64_t)i * blockDim.x;
+      v[i] = c < n ? idx[c] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (v[i] >= 0) atomicAdd(&hist[v[i]], 1);
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) count[e] = hist[e];
 }
 
-// workspace: logits [T, E] f32, then the three bf16 planes of W_r [3, E, d] (bf16 tokens)
+// workspace: KS partial planes of the logits [KS, T, E] f32, then the three bf16
+// planes of W_r [3, E, d] (bf16 tokens)
+static size_t logits_bytes(int64_t T, int E, int d) {
+  return ((size_t)router_ksplit(T, E, d) * T * E * sizeof(float) + 255) & ~(size_t)255;
+}
 size_t route_workspace_bytes(int64_t T, int E, int d) {
-  return (((size_t)T * E * sizeof(float) + 255) & ~(size_t)255) + (size_t)3 * E * d * 2;
+  return logits_bytes(T, E, d) + (size_t)3 * E * d * 2;
 }
 
 hipError_t launch_route(const void* x, bool x_f32, const float* w_r, const float* b_r, int64_t T,
                         int d, int E, int k, float* logits, int32_t* topk_idx, float* topk_gate,
                         int32_t* expert_count, hipStream_t st) {
+  int ks = 1;
   if (x_f32) {
     dim3 g1((E + RT_N - 1) / RT_N, (unsigned)((T + RT_M - 1) / RT_M));
-    router_logits_kernel<true><<<g1, 256, 0, st>>>(x, w_r, b_r, logits, T, d, E);
+    router_logits_kernel<true><<<g1, 256, 0, st>>>(x, w_r, logits, T, d, E);
   } else {
     // d % 64 == 0 for bf16 layers
-    bf16_t* w3 = (bf16_t*)((uint8_t*)logits + (((size_t)T * E * sizeof(float) + 255) & ~(size_t)255));
+    bf16_t* w3 = (bf16_t*)((uint8_t*)logits + logits_bytes(T, E, d));
     const int64_t n = (int64_t)E * d;
     router_split_kernel<<<(unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096), 256, 0, st>>>(w_r, n, w3);
-    const unsigned ge = (unsigned)((E + 63) / 64);
-    // 64-token tiles when that still gives every CU a workgroup, else 32-token tiles
-    if (((T + 63) / 64) * ge >= 256)
-      router_mfma_kernel<64><<<dim3(ge, (unsigned)((T + 63) / 64)), 256, 0, st>>>(
-          (const bf16_t*)x, w3, b_r, logits, T, d, E);
-    else
-      router_mfma_kernel<32><<<dim3(ge, (unsigned)((T + 31) / 32)), 128, 0, st>>>(
-          (const bf16_t*)x, w3, b_r, logits, T, d, E);
+    ks = router_ksplit(T, E, d);
+    router_mfma_kernel<64><<<dim3((unsigned)((E + 63) / 64), (unsigned)((T + 63) / 64), (unsigned)ks), 256, 0, st>>>(
+        (const bf16_t*)x, w3, logits, T, d, E);
   }
   const unsigned g2 = (unsigned)((T + 3) / 4);
   const int vpl = (E + 63) / 64;
-  if (vpl <= 1) router_topk_kernel<1><<<g2, 256, 0, st>>>(logits, T, E, k, topk_idx, topk_gate);
-  else if (vpl <= 2) router_topk_kernel<2><<<g2, 256, 0, st>>>(logits, T, E, k, topk_idx, topk_gate);
-  else if (vpl <= 4) router_topk_kernel<4><<<g2, 256, 0, st>>>(logits, T, E, k, topk_idx, topk_gate);
-  else if (vpl <= 8) router_topk_kernel<8><<<g2, 256, 0, st>>>(logits, T, E, k, topk_idx, topk_gate);
-  else router_topk_kernel<16><<<g2, 256, 0, st>>>(logits, T, E, k, topk_idx, topk_gate);
+  if (vpl <= 1) router_topk_kernel<1><<<g2, 256, 0, st>>>(logits, ks, b_r, T, E, k, topk_idx, topk_gate);
+  else if (vpl <= 2) router_topk_kernel<2><<<g2, 256, 0, st>>>(logits, ks, b_r, T, E, k, topk_idx, topk_gate);
+  else if (vpl <= 4) router_topk_kernel<4><<<g2, 256, 0, st>>>(logits, ks, b_r, T, E, k, topk_idx, topk_gate);
+  else if (vpl <= 8) router_topk_kernel<8><<<g2, 256, 0, st>>>(logits, ks, b_r, T, E, k, topk_idx, topk_gate);
+  else router_topk_kernel<16><<<g2, 256, 0, st>>>(logits, ks, b_r, T, E, k, topk_idx, topk_gate);
   expert_count_kernel<<<1, 1024, E * sizeof(int32_t), st>>>(topk_idx, T * k, E, expert_count);
   return hipGetLastError();
 }
