@@ -12,7 +12,7 @@
 //   dl_j = g_j (dg_j - sum_i g_i dg_i);  dW_r[e_j] += dl_j x_t;  dx_t += dl_j W_r[e_j]
 //
 // Kernels:
-//   dgrad_kernel<DOWN>  ring rows of dy (gathered) x W_down[e] (K = d rows), epilogue:
+//   dgrad_kernel<DOWN>  ring rows of dy x W_down[e] (K = d rows), epilogue:
 //                       SwiGLU backward -> dA|dU (bf16), g*h (bf16), row partials of dg
 //   dgrad_kernel<UP>    [dA|dU] x [W_gate[e]; W_up[e]] (K = 2f rows) -> dX per copy (bf16)
 //   token_kernel        dg, dl per token; dx = sum_j dX[copy] + dl_j W_r[e_j] (bf16)
@@ -20,43 +20,21 @@
 //                       per 128-row tile, then over the expert's tiles (last first)
 //   gather_to_ring      dy rows copied into ring order, one per copy (t, j)
 //   wgrad_kernel        dW_down[e] = dY_e^T (g H)_e;  [dW_gate;dW_up][e] = [dA|dU]_e^T X_e
-// The dgrad tiles are 128 x 128 with K in 64-element slices; the weights, whose K
-// index is their row index, are transposed 8 x 8 in registers on the way into LDS.  The
-// weight gradients read both operands row-major through DMA and transposing LDS
-// reads (see the wgrad section).  No floating-point atomics: every sum has one
-// fixed order.
+// The dgrad tiles are 128 x 128 with K in 32-element stages filled by global -> LDS
+// copies; the weights, whose K index is their row index, are staged row-major and
+// read as MFMA fragments with transposing LDS reads, as are both operands of the
+// weight gradients.  No floating-point atomics: every sum has one fixed order.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int BT = 128;            // tile rows and columns
-constexpr int BKB = 128;           // K bytes per stage (64 bf16)
-constexpr int BCH = BKB / 16;      // 16-byte chunks per row slice
-
-__device__ __forceinline__ int bswz(int r, int c) { return r * BKB + ((c ^ (r & 7)) << 4); }
-
-// 8 rows (K) x 8 bf16 (M or N) in, 8 vectors of 8 bf16 along K out.
-__device__ __forceinline__ void transpose8x8(const u32x4 (&r)[8], u32x4 (&o)[8]) {
-#pragma unroll
-  for (int m = 0; m < 8; ++m)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = r[2 * q][m >> 1], hi = r[2 * q + 1][m >> 1];
-      o[m][q] = (m & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-    }
-}
-
-__device__ __forceinline__ int64_t tok_of_slot(const int32_t* slot_copy, int64_t s, int k) {
-  return slot_copy[s] / k;
-}
-
+constexpr int BT = 128;            // dgrad tile rows and columns
 // Output tiles are staged row-major in LDS (BT rows of BT bf16, rows padded by 16
 // bytes) and written as whole 16-byte pieces of rows instead of 2-byte stores
 // scattered over rows.
 constexpr int SRS = BT * 2 + 16;            // staged row stride in bytes
 constexpr int STAGE_BYTES = BT * SRS;       // 34,816
-constexpr int SMEM_BYTES = 4 * BT * BKB;    // the two double-buffered operand tiles: 65,536
 
 __device__ __forceinline__ void stage_put(uint8_t* stg, int m, int n, float v) {
   *(uint16_t*)(stg + m * SRS + n * 2) = f2bf(v);
@@ -78,7 +56,7 @@ __device__ __forceinline__ void stage_flush(const uint8_t* stg, int rows, RowF d
 
 // ----------------------------------------------------------------------------- dgrad
 struct DgradArgs {
-  const bf16_t* A;          // DOWN: dy [T, d] (gathered through slot_copy); UP: dAU [C, 2f]
+  const bf16_t* A;          // ring-ordered rows: DOWN dy [C, d] (gathered into ring order); UP dAU [C, 2f]
   const bf16_t* B0;         // DOWN: W_down [E, d, f]; UP: W_gate [E, f, d]
   const bf16_t* B1;         // UP: W_up [E, f, d]
   int K, N;                 // DOWN: K = d, N = f; UP: K = 2f, N = d
@@ -97,11 +75,43 @@ struct DgradArgs {
   bf16_t* dxc;              // UP out: [C, d]
 };
 
+// Global -> LDS copy of 16 bytes per lane from a per-lane address (the wave's 64
+// lanes fill 1 KB of LDS at m0 + lane * 16), and a wait for this wave's copies.
+__device__ __forceinline__ void dma16_at(const void* addr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               ::"v"(addr), "s"(lds) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void bwait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ int wsw(int r, int c) { return c ^ ((r & 3) << 2); }
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i16_t ds_tr16(const uint8_t* lds_ptr) {
+  typedef __attribute__((address_space(3))) v4i16_t lds_v4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4*)((__attribute__((address_space(3))) uint8_t*)lds_ptr));
+}
+
+// dgrad stages: DK = 32 K elements.  A: BT ring rows x 64 bytes, 16-byte chunks
+// XOR-swizzled by (row >> 2) & 3 (a 128-bit fragment read is served 16 lanes = 16 rows
+// at a time, which then hit 16 distinct chunk positions of the 256-byte bank line).
+// B: DK weight rows (K) x BT columns (256 bytes), chunks swizzled by (row & 3) << 2,
+// read as MFMA fragments with transposing reads: lane l receives column l % 32 at K
+// rows 8 (l / 32) .. 8 (l / 32) + 7 of a 16-row sub-step, in two reads of 4 rows.
+// Both tiles are filled by global -> LDS copies (no register staging) through a ring
+// of DWS stages, DWS - 1 of them in flight while one is multiplied.
+constexpr int DK = 32, DWS = 4;
+constexpr int DA_BYTES = BT * DK * 2, DB_BYTES = DK * BT * 2, DSTAGE = DA_BYTES + DB_BYTES;
+constexpr int DG_LDS = DWS * DSTAGE;   // 64 KB; the epilogue staging (34,816 bytes) reuses it
+constexpr int DL = (DA_BYTES + DB_BYTES) / 4096;   // 1 KB copies per wave per stage
+
+__device__ __forceinline__ int aswz(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
 template <bool DOWN>
-__global__ __launch_bounds__(256) void dgrad_kernel(DgradArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_BYTES];
-  uint8_t(*As)[BT * BKB] = (uint8_t(*)[BT * BKB])smem;
-  uint8_t(*Bs)[BT * BKB] = (uint8_t(*)[BT * BKB])(smem + 2 * BT * BKB);
+__global__ __launch_bounds__(256, 2) void dgrad_kernel(DgradArgs p) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   __shared__ float red[2][BT];
   const int mt = blockIdx.y;
   if (mt >= *p.ntiles) return;
@@ -109,51 +119,55 @@ __global__ __launch_bounds__(256) void dgrad_kernel(DgradArgs p) {
   const int32_t seg = p.offset[e];
   const int rows = min(BT, p.offset[e + 1] - seg - row0);
   const int n0 = blockIdx.x * BT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lg = lane >> 5;
-  const int lda = DOWN ? p.K : p.K;   // row length of A in elements
 
-  // A: 4 chunks per thread, rows (tid + 256 i) / 8
-  const bf16_t* a_src[4];
+  // Copy i (0, 1) of this wave fills LDS kilobyte wave + 4 i of the A tile, rows
+  // 16 (wave + 4 i) .. + 15, and of the B tile, K rows 4 (wave + 4 i) .. + 3.
+  const uint8_t* a_addr[2];
+  int b_row[2], b_col[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = tid + 256 * i, r = q / BCH;
-    const int64_t s = ring_slot(p.head, seg, row0 + min(r, rows - 1), p.C);
-    const int64_t arow = DOWN ? tok_of_slot(p.slot_copy, s, p.k) : s;
-    a_src[i] = p.A + arow * lda + (q % BCH) * 8;
+  for (int i = 0; i < 2; ++i) {
+    const int j = wave + 4 * i;
+    const int r = j * 16 + (lane >> 2), slot = lane & 3, c = slot ^ ((r >> 2) & 3);
+    const int64_t sl = ring_slot(p.head, seg, row0 + min(r, rows - 1), p.C);
+    a_addr[i] = (const uint8_t*)p.A + (sl * p.K) * 2 + c * 16;
+    const int rb = j * 4 + (lane >> 4), sb = lane & 15;
+    b_row[i] = rb;
+    b_col[i] = (n0 + wsw(rb, sb) * 8) * 2;
   }
-  // B: threads 0..127 load one 8 (K) x 8 (N) block each: K rows kb*8.., columns nb*8..
-  const int kb = (tid & 127) >> 4, nb = tid & 15;
-  const bool bload = tid < 128;
-  auto brow_ptr = [&](int kk) -> const bf16_t* {   // K row kk of the stacked B
-    if (DOWN) return p.B0 + ((int64_t)e * p.K + kk) * p.N;
-    return kk < p.f ? p.B0 + ((int64_t)e * p.f + kk) * p.N
-                    : p.B1 + ((int64_t)e * p.f + (kk - p.f)) * p.N;
+  auto brow_ptr = [&](int kk) -> const uint8_t* {   // K row kk of the stacked B
+    if (DOWN) return (const uint8_t*)(p.B0 + ((int64_t)e * p.K + kk) * p.N);
+    return (const uint8_t*)(kk < p.f ? p.B0 + ((int64_t)e * p.f + kk) * p.N
+                                     : p.B1 + ((int64_t)e * p.f + (kk - p.f)) * p.N);
   };
-
-  u32x4 ra[4], rb[8];
-  auto gload = [&](int kt) {
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    const uint32_t st = lds0 + (uint32_t)(kt % DWS) * DSTAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = *(const u32x4*)(a_src[i] + kt * 64);
-    if (bload) {
-      const int col = min(n0 + nb * 8, p.N - 8);
+    for (int i = 0; i < 2; ++i)
+      dma16_at(a_addr[i] + kt * (DK * 2), __builtin_amdgcn_readfirstlane(st + (wave + 4 * i) * 1024));
 #pragma unroll
-      for (int q = 0; q < 8; ++q) rb[q] = *(const u32x4*)(brow_ptr(kt * 64 + kb * 8 + q) + col);
-    }
+    for (int i = 0; i < 2; ++i)
+      dma16_at(brow_ptr(kt * DK + b_row[i]) + b_col[i],
+               __builtin_amdgcn_readfirstlane(st + DA_BYTES + (wave + 4 * i) * 1024));
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i;
-      *(u32x4*)(As[buf] + bswz(q / BCH, q % BCH)) = ra[i];
-    }
-    if (bload) {
-      u32x4 o[8];
-      transpose8x8(rb, o);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) *(u32x4*)(Bs[buf] + bswz(nb * 8 + m, kb)) = o[m];
-    }
+  auto wait_stage = [&](int later) __attribute__((always_inline)) {
+    if (later <= 0) bwait_vm<0>();
+    else if (later == 1) bwait_vm<DL>();
+    else bwait_vm<2 * DL>();
   };
+  // this lane's first transposing read of B fragment j (tile columns wn*64 + 32j ..)
+  int boff[2];
+  {
+    const int g = lane >> 4, gi = lane & 15, qq = gi >> 2, ss = gi & 3;
+    const int r0 = 8 * (g >> 1) + qq;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int col = wn * 64 + jj * 32 + 16 * (g & 1) + 4 * ss;
+      boff[jj] = DA_BYTES + r0 * (BT * 2) + wsw(r0, col >> 3) * 16 + (col & 7) * 2;
+    }
+  }
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -163,32 +177,33 @@ __global__ __launch_bounds__(256) void dgrad_kernel(DgradArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = p.K / 64;
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  const int KT = p.K / DK;
+  for (int s = 0; s < DWS - 1 && s < KT; ++s) issue(s);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
+    wait_stage(min(DWS - 2, KT - 1 - kt));
+    __syncthreads();   // stage kt published; the buffer of stage kt - 1 is free
+    if (kt + DWS - 1 < KT) issue(kt + DWS - 1);
+    const uint8_t* sb = smem + (kt % DWS) * DSTAGE;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int c = kk * 2 + lg;
+    for (int kk = 0; kk < DK / 16; ++kk) {
       bf16x8 af[2], bfr[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(As[cur] + bswz(wm * 64 + i * 32 + lr, c)));
+        af[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sb + aswz(wm * 64 + i * 32 + lr, kk * 2 + lg)));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bs[cur] + bswz(wn * 64 + j * 32 + lr, c)));
+      for (int j = 0; j < 2; ++j) {
+        const uint8_t* b = sb + boff[j] + kk * 16 * (BT * 2);
+        const v4i16_t lo = ds_tr16(b), hi = ds_tr16(b + 4 * (BT * 2));
+        bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < KT) sstore(cur ^ 1);
-    __syncthreads();
   }
+  __syncthreads();   // every wave is done with the stages: the epilogue reuses them
 
   // the loop ended with a barrier: the operand tiles are free for staging
   uint8_t* stg = smem;
@@ -406,16 +421,6 @@ struct WgShape {
   static constexpr int L = LA + LB;
 };
 
-__device__ __forceinline__ int wsw(int r, int c) { return c ^ ((r & 3) << 2); }
-
-__device__ __forceinline__ void dma16_at(const void* addr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               ::"v"(addr), "s"(lds) : "memory", "m0");
-}
-template <int N>
-__device__ __forceinline__ void bwait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 template <typename T>
 __device__ __forceinline__ T bld_meta(const T* q) {   // scalar load of data written by earlier kernels
   return *(const __attribute__((address_space(4))) T*)q;
@@ -426,13 +431,6 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
-}
-
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ v4i16_t ds_tr16(const uint8_t* lds_ptr) {
-  typedef __attribute__((address_space(3))) v4i16_t lds_v4;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_v4*)((__attribute__((address_space(3))) uint8_t*)lds_ptr));
 }
 
 struct WgradArgs {
@@ -684,8 +682,20 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
 
   hipError_t err = launch_build_tiles(expert_offset, E, BT, tiles, ntiles, st);
   if (err != hipSuccess) return err;
+  zero_fill_kernel<<<1, 256, 0, st>>>((uint32_t*)(w + L.zero), 256);
+  bf16_t* rdy = (bf16_t*)(w + L.rdy);
+  gather_to_ring_kernel<<<(unsigned)T, 256, 0, st>>>((const bf16_t*)dy, copy_slot, k, d, rdy);
+  static bool lds_opt_in = false;   // the 64 KB stage ring plus the static reduction buffer
+  if (!lds_opt_in) {
+    if ((err = hipFuncSetAttribute((const void*)dgrad_kernel<true>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, DG_LDS)) != hipSuccess ||
+        (err = hipFuncSetAttribute((const void*)dgrad_kernel<false>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, DG_LDS)) != hipSuccess)
+      return err;
+    lds_opt_in = true;
+  }
   DgradArgs a{};
-  a.A = (const bf16_t*)dy;
+  a.A = rdy;
   a.B0 = (const bf16_t*)w_down;
   a.K = d;
   a.N = f;
@@ -702,7 +712,7 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
   a.dau = dau;
   a.gh = gh;
   a.dgpart = dgpart;
-  dgrad_kernel<true><<<dim3(f / BT, max_tiles), 256, 0, st>>>(a);
+  dgrad_kernel<true><<<dim3(f / BT, max_tiles), 256, DG_LDS, st>>>(a);
   DgradArgs b = a;
   b.A = dau;
   b.B0 = (const bf16_t*)w_gate;
@@ -710,7 +720,7 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
   b.K = 2 * f;
   b.N = d;
   b.dxc = dxc;
-  dgrad_kernel<false><<<dim3(d / BT, max_tiles), 256, 0, st>>>(b);
+  dgrad_kernel<false><<<dim3(d / BT, max_tiles), 256, DG_LDS, st>>>(b);
   token_kernel<<<(unsigned)T, 256, 0, st>>>(copy_slot, topk_idx, topk_gate, dgpart, f / BT, dxc,
                                             w_r, d, k, dl, (bf16_t*)dx);
   float* rpart = (float*)(w + L.rpart);
@@ -719,9 +729,6 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
       tiles, ntiles, expert_offset, head, C, (const bf16_t*)ring_x, dl, d, rpart, rfirst);
   router_wgrad_sum_kernel<<<dim3(E, (d / 4 + 255) / 256), 256, 0, st>>>(expert_offset, rfirst,
                                                                         rpart, d, dw_r);
-  zero_fill_kernel<<<1, 256, 0, st>>>((uint32_t*)(w + L.zero), 256);
-  bf16_t* rdy = (bf16_t*)(w + L.rdy);
-  gather_to_ring_kernel<<<(unsigned)T, 256, 0, st>>>((const bf16_t*)dy, copy_slot, k, d, rdy);
   WgradArgs wd{};
   wd.A = rdy;
   wd.B = gh;
