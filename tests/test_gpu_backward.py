@@ -23,6 +23,11 @@ MEDIUM = [
     # 400 copies over 64 experts with a strong skew: several experts receive nothing
     LayerConfig("bwd_sparse", T=200, d=128, E=64, k=2, f=128, zipf_s=1.1, hot_ratio=12.0,
                 backward=True, cid=52),
+    # 142-163 rows per expert: every expert spans a full and a ragged 128-row tile
+    LayerConfig("bwd_tall", T=600, d=256, E=8, k=2, f=128, backward=True, cid=53),
+    # skewed loads from 87 to 767 rows: the hottest expert spans six tiles, the last ragged
+    LayerConfig("bwd_tall_skew", T=1024, d=256, E=8, k=2, f=128, zipf_s=1.1, hot_ratio=3.0,
+                backward=True, cid=54),
 ]
 
 

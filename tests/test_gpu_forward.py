@@ -38,6 +38,9 @@ MEDIUM = [
     # at least 256 rows per expert on average: the bf16 256 x 256 tile with 64-byte K
     # slices; ragged in rows, columns and K
     LayerConfig("med_bf16_big256", T=1100, d=320, E=8, k=2, f=192, cid=38),
+    # d = 1984 = 31 K slices of 64 and only 4 token tiles: the bf16 router splits K over
+    # 3 workgroups (10, 10 and 11 slices) whose partial logit planes are added in order
+    LayerConfig("med_bf16_ksplit", T=200, d=1984, E=40, k=4, f=128, cid=39),
 ]
 
 
