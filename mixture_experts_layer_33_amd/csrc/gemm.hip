@@ -123,6 +123,11 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
+// The same copy with the non-temporal cache policy (see gemm_policy).
+__device__ __forceinline__ void dma16nt(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                ::"v"(voff), "s"(base), "s"(lds) : "memory", "m0");
@@ -155,7 +160,9 @@ struct EpiLayout {
   static constexpr int SIZE = BM * RS;
 };
 
-template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S>
+// POL: bit 0 = weight (B) copies with the non-temporal policy, bit 1 = output rows
+// stored with the non-temporal policy (see gemm_policy).
+template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S, int POL>
 __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   constexpr int EB = MX ? 1 : 2;                 // element bytes
   constexpr int WTM = BM / WM, WTN = BN / WN;    // wave tile
@@ -247,7 +254,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
       dma16(p.A + (size_t)kt * KB, a_off[c], __builtin_amdgcn_readfirstlane(st + SL::A + (NW * c + wave) * 1024));
     } else if (c < NA + NB) {
       const int i = c - NA;
-      dma16(b_base[i] + (size_t)kt * KB, b_off[i], __builtin_amdgcn_readfirstlane(st + SL::B + (NW * i + wave) * 1024));
+      if (POL & 1) dma16nt(b_base[i] + (size_t)kt * KB, b_off[i], __builtin_amdgcn_readfirstlane(st + SL::B + (NW * i + wave) * 1024));
+      else dma16(b_base[i] + (size_t)kt * KB, b_off[i], __builtin_amdgcn_readfirstlane(st + SL::B + (NW * i + wave) * 1024));
     } else if (c < NA + NB + NASC) {
       const int i = c - NA - NB;
       dma4(p.A_scale + (size_t)kt * 4, asc_off[i],
@@ -418,7 +426,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
       const int m = q / EL::CPR, cb = (q % EL::CPR) * 16;
       if (m < rows && col0b + cb < rowb) {
         const int64_t sl = ring_slot(p.head, seg, row0 + m, p.C);
-        *(u32x4*)(dst + sl * pitch + col0b + cb) = *(const u32x4*)(stg + m * EL::RS + cb);
+        const u32x4 v = *(const u32x4*)(stg + m * EL::RS + cb);
+        if (POL & 2) __builtin_nontemporal_store(v, (u32x4*)(dst + sl * pitch + col0b + cb));
+        else *(u32x4*)(dst + sl * pitch + col0b + cb) = v;
       }
     }
     __syncthreads();
@@ -474,12 +484,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S>
+template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S, int POL>
 static hipError_t run_mfma(const GemmArgs& a, int max_tiles, hipStream_t st) {
   const int nt = SWIGLU ? (a.N + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
   const size_t lds = std::max<size_t>((size_t)S * StageLayout<BM, BN, KB, MX>::SIZE,
                                       EpiLayout<BM, BN, SWIGLU, MX>::SIZE);
-  auto kern = gg_mfma_kernel<BM, BN, WM, WN, KB, SWIGLU, MX, S>;
+  auto kern = gg_mfma_kernel<BM, BN, WM, WN, KB, SWIGLU, MX, S, POL>;
   static bool attr_set = false;   // opt in to more than 64 KB of LDS once per process
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute((const void*)kern,
@@ -604,6 +614,23 @@ static int kstart_rotates(bool swiglu, int dtype, int64_t n, int E, int BM) {
   return (!swiglu && dtype == 1) ? 1 : 0;
 }
 
+// Cache policy of the copies and stores (measured on gfx950, in one process, ms for
+// default | non-temporal stores | non-temporal stores and weight copies):
+//  * output rows (H, saved A|U, ring_y) are written once and read once by a later
+//    kernel: non-temporal stores never lost and sometimes won (share MX down GEMM
+//    0.422 | 0.399; 2,048-token bf16 down GEMM 1.434 | 1.415), whole forward included;
+//  * non-temporal weight copies pay only where every weight panel is read once, i.e.
+//    one row tile per expert, and then only in the down GEMM (2,048 tokens bf16 1.434 |
+//    1.415 | 1.292, MX 0.907 | 0.876 | 0.859); the gate/up GEMM loses there (2.583 |
+//    2.578 | 2.728) and so does every GEMM whose panels several row tiles share (skewed
+//    gate/up 2.273 | 2.252 | 2.628, share bf16 1.006 | 0.992 | 1.165).
+// A bare copy of the gate/up pattern with a per-tile store behaves the same way: 2.54 ms
+// with default stores whichever the load policy, 2.29 ms with both non-temporal.
+// Whole 2,048-token bf16 forward: 4.205 -> 4.093 ms.
+static int gemm_policy(bool swiglu, int64_t n, int E, int BM) {
+  return (!swiglu && n <= (int64_t)BM * E) ? 3 : 2;
+}
+
 static int max_tiles_for(int64_t n, int E, int BM) { return (int)((n + BM - 1) / BM) + E; }
 
 size_t ffn_workspace_bytes(int64_t n, int64_t C, int d, int E, int f, int dtype) {
@@ -678,14 +705,18 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
   g2.saved_au = nullptr;
   g1.rotate = kstart_rotates(true, dtype, n, E, BM);
   g2.rotate = kstart_rotates(false, dtype, n, E, BM);
-  if (big) err = run_mfma<MFMA_BM_BIG, 256, 4, 2, 128, true, false, 2>(g1, max_tiles, st);
-  else if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, 128, true, false, 3>(g1, max_tiles, st);
-  else err = run_mfma<MFMA_BM, 256, 2, 2, 128, true, true, 3>(g1, max_tiles, st);
+  const int pol1 = gemm_policy(true, n, E, BM), pol2 = gemm_policy(false, n, E, BM);
+#define RUN_POL(P, G, ...)                                                 \
+  err = (P) == 3 ? run_mfma<__VA_ARGS__, 3>(G, max_tiles, st)              \
+                 : run_mfma<__VA_ARGS__, 2>(G, max_tiles, st);
+  if (big) { RUN_POL(pol1, g1, MFMA_BM_BIG, 256, 4, 2, 128, true, false, 2) }
+  else if (dtype == 1) { RUN_POL(pol1, g1, MFMA_BM, 256, 2, 2, 128, true, false, 3) }
+  else { RUN_POL(pol1, g1, MFMA_BM, 256, 2, 2, 128, true, true, 3) }
   if (err != hipSuccess || (err = mark(1)) != hipSuccess) return err;
-  if (big) err = run_mfma<MFMA_BM_BIG, 256, 4, 2, 128, false, false, 2>(g2, max_tiles, st);
-  else if (dtype == 1) err = run_mfma<MFMA_BM, 256, 2, 2, 128, false, false, 3>(g2, max_tiles, st);
-  else err = run_mfma<MFMA_BM, 256, 2, 2, 128, false, true, 3>(g2, max_tiles, st);
-#undef G2
+  if (big) { RUN_POL(pol2, g2, MFMA_BM_BIG, 256, 4, 2, 128, false, false, 2) }
+  else if (dtype == 1) { RUN_POL(pol2, g2, MFMA_BM, 256, 2, 2, 128, false, false, 3) }
+  else { RUN_POL(pol2, g2, MFMA_BM, 256, 2, 2, 128, false, true, 3) }
+#undef RUN_POL
   if (err != hipSuccess) return err;
   return mark(2);
 }
