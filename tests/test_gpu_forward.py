@@ -41,6 +41,10 @@ MEDIUM = [
     # d = 1984 = 31 K slices of 64 and only 4 token tiles: the bf16 router splits K over
     # 3 workgroups (10, 10 and 11 slices) whose partial logit planes are added in order
     LayerConfig("med_bf16_ksplit", T=200, d=1984, E=40, k=4, f=128, cid=39),
+    # at least two row tiles per expert (the regime of the per-GPU share shapes: K-start
+    # rotation on in both GEMMs); bf16 256-row tiles, then MX 128-row tiles
+    LayerConfig("med_bf16_tail", T=2600, d=320, E=4, k=2, f=192, cid=40),
+    LayerConfig("med_mx_tail", T=1500, d=256, E=4, k=2, f=256, dtype="mxfp8", cid=41),
 ]
 
 
