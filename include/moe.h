@@ -35,7 +35,10 @@
  *   - The caller owns every buffer.  The library allocates nothing, keeps no
  *     pointer after return, and only enqueues work on `stream`: there is no
  *     host synchronisation and no device-to-host copy inside any call.
- *   - Outputs are fully overwritten; read-only inputs are never written.
+ *   - Outputs are fully overwritten; read-only inputs are never written.  With
+ *     tokens = 0 the per-expert outputs are zeros (expert_count, expert_offset,
+ *     every weight gradient) and per-token outputs are empty; per-token arrays
+ *     (x, dy, y, dx, topk_idx, topk_gate, copy_slot) may then be NULL.
  *   - Results are bitwise reproducible run to run (fixed reduction orders,
  *     no floating-point atomics).
  *   - Errors: arguments are validated on the host from `shape` before any

@@ -15,6 +15,24 @@ constexpr int MAX_K = 32;
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// A per-token array (x, dy, y, dx, topk_idx, topk_gate, copy_slot) may be NULL when
+// the call has no tokens, like any zero-length array.
+bool missing_tok(const void* p, int64_t T) { return p == nullptr && T > 0; }
+
+// Zero `words` 32-bit words (a fill kernel rather than hipMemsetAsync, so that a call
+// stays safe to capture in a graph).  Used for the outputs of calls with no tokens.
+__global__ void zero_words_kernel(uint32_t* __restrict__ p, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+hipError_t zero_words(void* p, size_t words, hipStream_t st) {
+  if (words == 0) return hipSuccess;
+  const size_t blocks = (words + 255) / 256;
+  zero_words_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, st>>>((uint32_t*)p, words);
+  return hipGetLastError();
+}
+
 bool bad_dtype(int dt) { return dt != MOE_F32 && dt != MOE_BF16 && dt != MOE_MXFP8; }
 
 // Shape checks common to the forward calls.  K-dimension multiples follow the
@@ -78,10 +96,12 @@ int moe_route(const moe_shape* s, const void* x, const float* w_router, const fl
   try {
     int st = check_shape(s);
     if (st) return st;
-    if (!x || !w_router || !topk_idx || !topk_gate || !expert_count || !workspace)
+    const int64_t T = s->tokens;
+    if (missing_tok(x, T) || !w_router || missing_tok(topk_idx, T) || missing_tok(topk_gate, T) ||
+        !expert_count || !workspace)
       return MOE_ERR_NULL;
     if (workspace_bytes < moe_workspace_bytes(s, MOE_OP_ROUTE)) return MOE_ERR_WORKSPACE;
-    if (s->tokens == 0) return MOE_OK;
+    if (s->tokens == 0) return hip_status(zero_words(expert_count, (size_t)s->experts, stream));
     return hip_status(moe::launch_route(x, s->dtype == MOE_F32, w_router, b_router, s->tokens,
                                         s->hidden, s->experts, s->top_k, (float*)workspace,
                                         topk_idx, topk_gate, expert_count, stream));
@@ -96,12 +116,15 @@ int moe_dispatch(const moe_shape* s, const void* x, const int32_t* topk_idx, int
   try {
     int st = check_shape(s);
     if (st) return st;
-    if (!x || !topk_idx || !ring_x || !expert_offset || !copy_slot || !slot_copy || !workspace)
+    const int64_t T = s->tokens;
+    if (missing_tok(x, T) || missing_tok(topk_idx, T) || !ring_x || !expert_offset ||
+        missing_tok(copy_slot, T) || !slot_copy || !workspace)
       return MOE_ERR_NULL;
     if (s->dtype == MOE_MXFP8 && !ring_x_scale) return MOE_ERR_NULL;
     if (ring_head < 0 || ring_head >= s->capacity) return MOE_ERR_SHAPE;
     if (workspace_bytes < moe_workspace_bytes(s, MOE_OP_DISPATCH)) return MOE_ERR_WORKSPACE;
-    if (s->tokens == 0) return MOE_OK;
+    if (s->tokens == 0)   // no copies: every expert's segment is empty
+      return hip_status(zero_words(expert_offset, (size_t)s->experts + 1, stream));
     return hip_status(moe::launch_dispatch(
         x, s->dtype == MOE_F32 ? 4 : 2, s->dtype == MOE_MXFP8, topk_idx, s->tokens, s->hidden,
         s->experts, s->top_k, ring_head, s->capacity, ring_x, ring_x_scale, expert_offset,
@@ -153,7 +176,9 @@ int moe_combine(const moe_shape* s, const void* ring_y, const int32_t* copy_slot
   try {
     int st = check_shape(s);
     if (st) return st;
-    if (!ring_y || !copy_slot || !topk_gate || !y) return MOE_ERR_NULL;
+    const int64_t T = s->tokens;
+    if (!ring_y || missing_tok(copy_slot, T) || missing_tok(topk_gate, T) || missing_tok(y, T))
+      return MOE_ERR_NULL;
     return hip_status(moe::launch_combine(s->dtype == MOE_F32, ring_y, copy_slot, topk_gate,
                                           s->tokens, s->hidden, s->top_k, y, stream));
   } catch (...) {
@@ -198,12 +223,23 @@ int moe_backward(const moe_shape* s, const void* dy, const void* x, const float*
     if (st) return st;
     if (s->dtype != MOE_BF16) return MOE_ERR_DTYPE;
     if (s->hidden % 128 || s->ffn % 128) return MOE_ERR_SHAPE;   // 128 x 128 gradient tiles
-    if (!dy || !x || !w_router || !topk_idx || !topk_gate || !ring_x || !expert_offset ||
-        !copy_slot || !slot_copy || !saved_au || !w_gate || !w_up || !w_down || !dx || !dw_gate ||
+    const int64_t T = s->tokens;
+    if (missing_tok(dy, T) || missing_tok(x, T) || !w_router || missing_tok(topk_idx, T) ||
+        missing_tok(topk_gate, T) || !ring_x || !expert_offset ||
+        missing_tok(copy_slot, T) || !slot_copy || !saved_au || !w_gate || !w_up || !w_down ||
+        missing_tok(dx, T) || !dw_gate ||
         !dw_up || !dw_down || !dw_router || !workspace)
       return MOE_ERR_NULL;
     if (ring_head < 0 || ring_head >= s->capacity) return MOE_ERR_SHAPE;
     if (workspace_bytes < moe_workspace_bytes(s, MOE_OP_BACKWARD)) return MOE_ERR_WORKSPACE;
+    if (s->tokens == 0) {   // no tokens: every weight gradient is zero (dx is empty)
+      const size_t wbytes = (size_t)s->experts * s->ffn * s->hidden * 2;   // bf16, even count
+      hipError_t err = zero_words(dw_gate, wbytes / 4, stream);
+      if (err == hipSuccess) err = zero_words(dw_up, wbytes / 4, stream);
+      if (err == hipSuccess) err = zero_words(dw_down, wbytes / 4, stream);
+      if (err == hipSuccess) err = zero_words(dw_router, (size_t)s->experts * s->hidden, stream);
+      return hip_status(err);
+    }
     return hip_status(moe::launch_backward(
         dy, x, w_router, topk_idx, topk_gate, ring_x, expert_offset, copy_slot, slot_copy,
         ring_head, s->capacity, saved_au, w_gate, w_up, w_down, s->tokens, s->hidden, s->experts,

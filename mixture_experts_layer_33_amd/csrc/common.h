@@ -117,11 +117,6 @@ __device__ __forceinline__ void wave_route_row_f(LogitF logit, int E, int k, int
   gate = p / ps;
 }
 
-template <int VPL>
-__device__ __forceinline__ void wave_route_row(const float* __restrict__ l, int E, int k,
-                                               int& choice, int& rank, float& gate) {
-  wave_route_row_f<VPL>([&](int e) { return l[e]; }, E, k, choice, rank, gate);
-}
 
 // ---------------------------------------------------------------- MX / E4M3
 // Block exponent of the OCP MX rule: X = floor(log2 amax) - 8, clamped to
