@@ -319,7 +319,6 @@ __global__ __launch_bounds__(256) void token_kernel(const int32_t* __restrict__ 
   }
 }
 
-// dW_r[e][c] = sum over the segment's rows, last slot first, of dl * x  (fp32).
 // dW_r[e] = sum over the expert's rows, last slot first, of dl x.  Step 1: every
 // 128-row tile of the tile list (expert-major, rows ascending) sums its rows, last
 // first, into an fp32 partial; the expert's first tile records its index.  Step 2
