@@ -31,7 +31,11 @@
  *   - "act" tensors are fp32 when shape->dtype == MOE_F32, otherwise bf16
  *     (raw 16-bit patterns).  With MOE_MXFP8 the router and the tokens x stay
  *     bf16; ring_x, H and the expert weights are E4M3 codes (uint8) with one
- *     E8M0 scale byte per 32 elements along the reduction dimension.
+ *     E8M0 scale byte per 32 elements along the reduction dimension.  Every MX
+ *     scale tensor of a matrix [rows, cols] is laid out [cols/128][rows][4]: for each
+ *     group of 128 columns one 32-bit word per row holding that row's 4 block scales
+ *     in column order (cols % 128 == 0), so that the scales a GEMM stage needs for
+ *     consecutive rows are consecutive words.
  *   - The caller owns every buffer.  The library allocates nothing, keeps no
  *     pointer after return, and only enqueues work on `stream`: there is no
  *     host synchronisation and no device-to-host copy inside any call.
@@ -110,7 +114,7 @@ int moe_route(const moe_shape* shape, const void* x, const float* w_router,
  * In:  x [T,d] act (bf16 for MOE_MXFP8), topk_idx [T,k], ring_head in [0, C).
  * Out: ring_x [C,d] act (MOE_MXFP8: E4M3 codes, each row MX-quantised along d)
  *        — only the T*k used slots are written;
- *      ring_x_scale [C, d/32] E8M0 bytes (MOE_MXFP8 only, else NULL);
+ *      ring_x_scale [d/128][C][4] E8M0 bytes (MOE_MXFP8 only, else NULL);
  *      expert_offset [E+1] int32, segment starts relative to the head (offset[E] = T*k);
  *      copy_slot [T,k] int32 absolute slot of each copy;
  *      slot_copy [C] int32 copy id t*k+j held by each used slot (other slots untouched).
@@ -128,8 +132,9 @@ int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
  *   [A|U] = X_e [W_gate[e]; W_up[e]]^T,  H = silu(A) * U,  Y_e = H W_down[e]^T.
  * H is bf16 (fp32 for MOE_F32; MX along f for MOE_MXFP8) and lives in the workspace.
  * In:  ring_x (+ ring_x_scale), expert_offset, ring_head; w_gate, w_up [E,f,d] and
- *      w_down [E,d,f] act, or E4M3 codes with w_gate_scale/w_up_scale [E,f,d/32]
- *      and w_down_scale [E,d,f/32] for MOE_MXFP8 (NULL otherwise).
+ *      w_down [E,d,f] act, or E4M3 codes with w_gate_scale/w_up_scale [d/128][E*f][4]
+ *      and w_down_scale [f/128][E*d][4] for MOE_MXFP8 (NULL otherwise), as
+ *      moe_quantize_mx writes them for the [E*f, d] and [E*d, f] matrices.
  * Out: ring_y [C,d] (bf16; fp32 for MOE_F32) at the segment slots;
  *      saved_au [C,2f] bf16 (A then U per slot) when not NULL — the backward's input
  *      (MOE_BF16 only; must be NULL otherwise).
@@ -220,10 +225,11 @@ size_t moe_workspace_bytes(const moe_shape* shape, int op);
 const char* moe_status_string(int status);
 
 /*
- * moe_quantize_mx: MX-quantise a bf16 matrix [rows, cols] along cols (cols % 32 == 0):
+ * moe_quantize_mx: MX-quantise a bf16 matrix [rows, cols] along cols (cols % 128 == 0):
  * per block of 32, X = floor(log2 amax) - 8 clamped to [-127, 127] (-127 for a zero
  * block), code = RNE_E4M3(clamp(v / 2^X, +-448)), scale = X + 127.
- * Out: codes [rows, cols] uint8, scales [rows, cols/32] uint8.  Used for the weights.
+ * Out: codes [rows, cols] uint8, scales [cols/128][rows][4] uint8 (the MX scale
+ * layout above).  Used for the weights.
  */
 int moe_quantize_mx(const void* src_bf16, int64_t rows, int64_t cols, uint8_t* codes,
                     uint8_t* scales, hipStream_t stream);

@@ -121,10 +121,11 @@ def moe_quantize_mx(src, codes, scales, stream=None):
 
 
 def quantize_mx(src: torch.Tensor, stream=None):
-    """(codes uint8, scales uint8) of a bf16 tensor, MX along its last dimension."""
+    """(codes uint8, scales uint8) of a bf16 tensor, MX along its last dimension; the
+    scales in the library's layout [cols/128][rows][4] (rows = all leading dimensions)."""
     codes = torch.empty(src.shape, dtype=torch.uint8, device=src.device)
-    scales = torch.empty(src.shape[:-1] + (src.shape[-1] // 32,), dtype=torch.uint8,
-                         device=src.device)
+    rows = src.numel() // src.shape[-1]
+    scales = torch.empty((src.shape[-1] // 128, rows, 4), dtype=torch.uint8, device=src.device)
     moe_quantize_mx(src, codes, scales, stream)
     return codes, scales
 
@@ -170,7 +171,7 @@ class Layer:
         s = self.shape
         mx = s.dtype == MOE_MXFP8
         ring = self._buf("ring_x", (s.capacity, s.hidden), torch.uint8 if mx else self.act_dtype)
-        rsc = self._buf("ring_x_scale", (s.capacity, s.hidden // 32), torch.uint8) if mx else None
+        rsc = self._buf("ring_x_scale", (s.hidden // 128, s.capacity, 4), torch.uint8) if mx else None
         off = self._buf("expert_offset", (s.experts + 1,), torch.int32)
         cs = self._buf("copy_slot", (s.tokens, s.top_k), torch.int32)
         sc = self._buf("slot_copy", (s.capacity,), torch.int32)

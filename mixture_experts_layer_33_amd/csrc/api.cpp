@@ -253,7 +253,7 @@ int moe_quantize_mx(const void* src_bf16, int64_t rows, int64_t cols, uint8_t* c
                     uint8_t* scales, hipStream_t stream) {
   try {
     if (!src_bf16 || !codes || !scales) return MOE_ERR_NULL;
-    if (rows < 0 || cols <= 0 || cols % 32) return MOE_ERR_SHAPE;
+    if (rows < 0 || cols <= 0 || cols % 128) return MOE_ERR_SHAPE;   // scale groups of 128 columns
     return hip_status(moe::launch_quantize_mx(src_bf16, rows, cols, codes, scales, stream));
   } catch (...) {
     return MOE_ERR_HIP;

@@ -157,7 +157,8 @@ __global__ __launch_bounds__(256) void dispatch_mx_kernel(
     if (ok)
       for (int j = 0; j < k; ++j) {
         *(u32x2*)(ring + slots[j] * d + (int64_t)v * 8) = u32x2{lo, hi};
-        if ((v & 3) == 0) ring_scale[slots[j] * (d / 32) + v / 4] = (uint8_t)(X + 127);
+        if ((v & 3) == 0)   // scale layout [d / 128][C][4]: block v / 4 of ring row slots[j]
+          ring_scale[((int64_t)(v / 16) * C + slots[j]) * 4 + ((v / 4) & 3)] = (uint8_t)(X + 127);
       }
   }
 }

@@ -96,6 +96,8 @@ struct GemmArgs {
   uint8_t* out_scale;      // SWIGLU + MX: H scales [C, f/32]
   uint16_t* saved_au;      // SWIGLU + bf16: [C, 2f] or null
   int rotate;              // 1: tile L starts its K loop at step L mod (K steps), see kstart_rotates
+  int64_t a_rows, b_rows;  // MX: rows of the A scale tensor (C) and of each B scale tensor (E N);
+                           // scale layout [K / 128][rows][4 bytes]
 };
 
 // Tile order.  The grid is 1-D; workgroup b runs on XCD b % 8 (round-robin
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wm = wave / WN, wn = wave % WN;
   const uint32_t Kb = (uint32_t)p.K * EB;                 // row bytes
-  const uint32_t Ks = (uint32_t)p.K / 32;                 // MX scale bytes per row
+
 
   // Copy i of this wave fills 16-byte chunks j = (NW i + wave) * 64 + lane of a tile:
   // row j / CH, slot j % CH, which holds the global chunk whose swizzled slot it is
@@ -236,15 +238,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < NASC; ++i) {          // the waves share the BM scale rows
       const int r = wave * ARW + min(lane, ARW - 1);
-      asc_off[i] = (uint32_t)ring_slot(p.head, seg, row0 + min(r, rows - 1), p.C) * Ks;
+      asc_off[i] = (uint32_t)ring_slot(p.head, seg, row0 + min(r, rows - 1), p.C) * 4;
     }
 #pragma unroll
     for (int i = 0; i < NBSC; ++i) {          // the waves share the BN scale rows
       const int r = (4 * i + wave) * 64 + lane;
       const bool up = SWIGLU && (4 * i + wave) * 64 >= BN / 2;
       const int rr = up ? r - BN / 2 : r;
-      bsc_base[i] = (up ? p.B1_scale : p.B0_scale) + (int64_t)e * p.N * Ks;
-      bsc_off[i] = (uint32_t)min(n0 + rr, p.N - 1) * Ks;
+      bsc_base[i] = (up ? p.B1_scale : p.B0_scale) + (int64_t)e * p.N * 4;
+      bsc_off[i] = (uint32_t)min(n0 + rr, p.N - 1) * 4;
     }
   }
   // K steps are taken in the order s0, s0 + 1, ..., KT - 1, 0, ..., s0 - 1: with
@@ -265,11 +267,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
       else dma16(b_base[i] + (size_t)kt * KB, b_off[i], __builtin_amdgcn_readfirstlane(st + SL::B + (NW * i + wave) * 1024));
     } else if (c < NA + NB + NASC) {
       const int i = c - NA - NB;
-      dma4(p.A_scale + (size_t)kt * 4, asc_off[i],
+      dma4(p.A_scale + (size_t)kt * p.a_rows * 4, asc_off[i],
            __builtin_amdgcn_readfirstlane(st + SL::ASC + wave * 256));
     } else {
       const int i = c - NA - NB - NASC;
-      dma4(bsc_base[i] + (size_t)kt * 4, bsc_off[i],
+      dma4(bsc_base[i] + (size_t)kt * p.b_rows * 4, bsc_off[i],
            __builtin_amdgcn_readfirstlane(st + SL::BSC + (4 * i + wave) * 256));
     }
   };
@@ -464,8 +466,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
               stg[m * EL::RS + cl] = (uint8_t)e4m3_encode(h, X);
               const int col = n0 + cl;
               if (lr == 0 && m < rows && col < p.N)
-                p.out_scale[ring_slot(p.head, seg, row0 + m, p.C) * (p.N / 32) + col / 32] =
-                    (uint8_t)(X + 127);
+                p.out_scale[((int64_t)(col / 128) * p.C + ring_slot(p.head, seg, row0 + m, p.C)) * 4 +
+                            (col / 32) % 4] = (uint8_t)(X + 127);
             } else {
               const float v = plane == 0 ? silu(a) * u : plane == 1 ? a : u;
               *(uint16_t*)(stg + m * EL::RS + cl * 2) = f2bf(v);
@@ -699,6 +701,8 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
   g1.out = H;
   g1.out_scale = dtype == 2 ? H + (size_t)C * f : nullptr;
   g1.saved_au = (uint16_t*)saved_au;
+  g1.a_rows = C;
+  g1.b_rows = (int64_t)E * f;
   GemmArgs g2 = g1;
   g2.A = H;
   g2.A_scale = g1.out_scale;
@@ -711,6 +715,7 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
   g2.out = (uint8_t*)ring_y;
   g2.out_scale = nullptr;
   g2.saved_au = nullptr;
+  g2.b_rows = (int64_t)E * d;
   g1.rotate = kstart_rotates(true, dtype, n, E, BM);
   g2.rotate = kstart_rotates(false, dtype, n, E, BM);
   const int pol1 = gemm_policy(true, n, E, BM), pol2 = gemm_policy(false, n, E, BM);

@@ -4,13 +4,20 @@
 // The MXFP8 format is the one the pages name for the expert kernels (khabar-ai
 // page, @rohanpaul_ai tweet; dzen.guru page, megakernel paragraph); the bits
 // follow the OCP MX v1.0 rule.  4 lanes hold one block (8 bf16 each).
+//
+// Scale layout (every MX scale tensor of the library): [cols / 128][rows][4] bytes, i.e.
+// for each group of 128 columns one dword per row holding its 4 block scales.  A
+// grouped-GEMM stage (128 columns of K) then finds the scales of consecutive rows in
+// consecutive dwords; with the row layout [rows][cols / 32] they sat 4 bytes per row
+// cols / 32 bytes apart, one cache line per row (MX gate/up GEMM 1.83 -> 1.62 ms).
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
 __global__ __launch_bounds__(256) void quantize_mx_kernel(const bf16_t* __restrict__ src,
-                                                          int64_t nvec, uint8_t* __restrict__ codes,
+                                                          int64_t nvec, int64_t rows, int64_t vpr,
+                                                          uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales) {
   // nvec = rows * cols / 8 vectors of 8 bf16; blocks never straddle rows (cols % 32 == 0)
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -34,7 +41,10 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const bf16_t* __restri
     for (int q = 0; q < 4; ++q) hi |= e4m3_encode(f[4 + q], X) << (8 * q);
     if (ok) {
       ((u32x2*)codes)[v] = u32x2{lo, hi};
-      if ((v & 3) == 0) scales[v / 4] = (uint8_t)(X + 127);
+      if ((v & 3) == 0) {   // block cb of row r: vpr = cols / 8 vectors per row
+        const int64_t r = v / vpr, cb = (v - r * vpr) / 4;
+        scales[((cb / 4) * rows + r) * 4 + (cb & 3)] = (uint8_t)(X + 127);
+      }
     }
   }
 }
@@ -45,7 +55,8 @@ hipError_t launch_quantize_mx(const void* src, int64_t rows, int64_t cols, uint8
   if (nvec == 0) return hipSuccess;
   int64_t blocks = (nvec + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  quantize_mx_kernel<<<(unsigned)blocks, 256, 0, st>>>((const bf16_t*)src, nvec, codes, scales);
+  quantize_mx_kernel<<<(unsigned)blocks, 256, 0, st>>>((const bf16_t*)src, nvec, rows, cols / 8,
+                                                        codes, scales);
   return hipGetLastError();
 }
 

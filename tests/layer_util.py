@@ -15,13 +15,22 @@ def to_oracle(t: torch.Tensor) -> np.ndarray:
     return oracle.from_f32(t.detach().float().cpu().numpy())
 
 
+def mx_scale_rows(s: torch.Tensor) -> torch.Tensor:
+    """The library's MX scale layout [cols/128][rows][4] as the row layout [rows, cols/32]
+    the oracle uses (a pure relabelling of bytes)."""
+    g, r, _ = s.shape
+    return s.permute(1, 0, 2).reshape(r, g * 4)
+
+
 class LazyWeights:
     """Oracle weight accessor e -> (W_gate[e], W_up[e], W_down[e]) in fp64, one expert at
     a time from device tensors (MX: decoded by the oracle's own table from codes/scales)."""
 
     def __init__(self, wg, wu, wd, mx_codes=None):
         self.wg, self.wu, self.wd = wg, wu, wd
-        self.mx = mx_codes          # ((cg, sg), (cu, su), (cd, sd)) device tensors or None
+        # ((cg, sg), (cu, su), (cd, sd)) device tensors or None; scales as [E, rows, cols/32]
+        self.mx = None if mx_codes is None else tuple(
+            (c, mx_scale_rows(sc).reshape(c.shape[0], c.shape[1], c.shape[2] // 32)) for c, sc in mx_codes)
         self.cache = {}
 
     def __call__(self, e):

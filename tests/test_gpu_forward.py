@@ -11,7 +11,7 @@ import mixture_experts_layer_33_amd as moe
 import oracle
 from gen import (FWD_BF16, FWD_MXFP8, SHARE_BF16, SHARE_MXFP8, SKEW_BWD, TINY_F32, LayerConfig,
                  make_layer, make_share)
-from layer_util import LazyWeights, rel, to_oracle
+from layer_util import LazyWeights, mx_scale_rows, rel, to_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -83,7 +83,7 @@ def test_forward_parity(cfg):
                      mx_codes=tuple(q) if mx else None)
     if mx:   # the device quantiser matches the oracle's encoder bit for bit
         for e in range(cfg.E):
-            for (c, s), (oc, os_) in zip([(c[e], s[e]) for c, s in q], lw.oracle_mx(e)):
+            for (c, s), (oc, os_) in zip([(c[e], s[e]) for c, s in lw.mx], lw.oracle_mx(e)):
                 np.testing.assert_array_equal(c.cpu().numpy(), oc)
                 np.testing.assert_array_equal(s.cpu().numpy(), os_)
     ref_r = oracle.route(x, w_r, b, cfg.k)
@@ -109,7 +109,7 @@ def test_forward_parity(cfg):
             for j in range(cfg.k):
                 np.testing.assert_array_equal(ring[torch.from_numpy(cs[:, j]).to(DEV)].cpu().numpy(), xc)
                 np.testing.assert_array_equal(
-                    out["ring_x_scale"][torch.from_numpy(cs[:, j]).to(DEV)].cpu().numpy(), xs)
+                    mx_scale_rows(out["ring_x_scale"])[torch.from_numpy(cs[:, j]).to(DEV)].cpu().numpy(), xs)
         else:
             for j in range(cfg.k):
                 got = ring[torch.from_numpy(cs[:, j]).to(DEV)]
@@ -128,7 +128,10 @@ def test_forward_parity(cfg):
         for name, t in first.items():
             if name in ("ring_x", "ring_y", "ring_x_scale"):
                 sl = torch.from_numpy(np.nonzero(oracle.dispatch(ref_r.idx, cfg.E, cfg.C, 0).slot_copy >= 0)[0]).to(DEV)
-                assert torch.equal(t[sl], again[name][sl]), name
+                a, b = t, again[name]
+                if name == "ring_x_scale":   # [d/128][C][4] -> rows [C, d/32] before slot indexing
+                    a, b = mx_scale_rows(a), mx_scale_rows(b)
+                assert torch.equal(a[sl], b[sl]), name
             else:
                 assert torch.equal(t, again[name]), name
 
@@ -163,7 +166,7 @@ def test_forward_full_size_sampled(cfg):
     ring_y = out["ring_y"]
     for e in experts:
         if mx:
-            for (c, s), (oc, os_) in zip([(c[e], s[e]) for c, s in q], lw.oracle_mx(e)):
+            for (c, s), (oc, os_) in zip([(c[e], s[e]) for c, s in lw.mx], lw.oracle_mx(e)):
                 np.testing.assert_array_equal(c.cpu().numpy(), oc)
                 np.testing.assert_array_equal(s.cpu().numpy(), os_)
         slots = oracle.segment_slots(disp, e)
@@ -175,7 +178,7 @@ def test_forward_full_size_sampled(cfg):
             xc, xs = oracle.mx.quantize(x[toks], axis=1)
             sl = torch.from_numpy(slots).to(DEV)
             np.testing.assert_array_equal(layer.bufs["ring_x"][sl].cpu().numpy(), xc)
-            np.testing.assert_array_equal(layer.bufs["ring_x_scale"][sl].cpu().numpy(), xs)
+            np.testing.assert_array_equal(mx_scale_rows(layer.bufs["ring_x_scale"])[sl].cpu().numpy(), xs)
         ref = oracle.swiglu(xe, *lw(e), h_mx=mx)
         got = to_oracle(ring_y[torch.from_numpy(slots).to(DEV)])
         err = rel(got, ref)
