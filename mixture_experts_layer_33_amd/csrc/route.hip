@@ -203,11 +203,115 @@ __global__ __launch_bounds__(BM * 4) void router_mfma_kernel(
   }
 }
 
-// Number of K splits of the bf16 router: enough workgroups (two fit per CU) to give
-// every CU two, keeping at least 8 K slices per split.
+// The same logits with 128 tokens x 128 experts per workgroup: sixteen waves in 4 x 4, each
+// 32 tokens x 32 experts x 3 planes.  Per K slice a workgroup stages 16 KB of tokens and 48 KB of
+// weights for four times the MFMA work of the 64 x 64 tile, halving the L2 traffic per
+// logit; the double buffer (128 KB) is dynamic LDS, one workgroup per CU.  One slice is in
+// flight in registers while the other is multiplied: a second register set would spill.
+constexpr int R2_BM = 128, R2_BN = 128, R2_NT = 1024;
+constexpr int R2_LDS = 2 * (R2_BM + 3 * R2_BN) * RM_K;
+__global__ __launch_bounds__(R2_NT) void router_mfma2_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w3, float* __restrict__ logits,
+    int64_t T, int d, int E) {
+  constexpr int BM = R2_BM, BNE = R2_BN, BNR = 3 * BNE, NT = R2_NT;
+  constexpr int A_LD = BM * 8 / NT, B_LD = BNR * 8 / NT;
+  extern __shared__ __attribute__((aligned(16))) uint8_t r2lds[];
+#define AS2(buf) (r2lds + (buf) * (BM * RM_K))
+#define BS2(buf) (r2lds + 2 * BM * RM_K + (buf) * (BNR * RM_K))
+  const int64_t t0 = (int64_t)blockIdx.y * BM;
+  const int e0 = blockIdx.x * BNE;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3, lr = lane & 31, lg = lane >> 5;
+  const int64_t n = (int64_t)E * d;
+  const int KS = gridDim.z, z = blockIdx.z, KA = d / 64;
+  const int kb = (int)((int64_t)KA * z / KS);
+  const int KT = (int)((int64_t)KA * (z + 1) / KS) - kb;
+  const bf16_t* a_src[A_LD];
+  const bf16_t* b_src[B_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int q = tid + NT * i;
+    const int64_t t = min(t0 + q / 8, T - 1);
+    a_src[i] = x + t * d + (int64_t)kb * 64 + (q % 8) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int q = tid + NT * i, r = q / 8;
+    const int e = min(e0 + r % BNE, E - 1);
+    b_src[i] = w3 + (r / BNE) * n + (int64_t)e * d + (int64_t)kb * 64 + (q % 8) * 8;
+  }
+  u32x4 ra0[A_LD], rb0[B_LD];
+#define R_LOAD(kt, RA, RB)                                                                   \
+  {                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) RA[i] = *(const u32x4*)(a_src[i] + (kt) * 64); \
+    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) RB[i] = *(const u32x4*)(b_src[i] + (kt) * 64); \
+  }
+#define R_STORE(buf, RA, RB)                                                                 \
+  {                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) {                                      \
+      const int q = tid + NT * i;                                                            \
+      *(u32x4*)(AS2(buf) + rswz(q / 8, q % 8)) = RA[i];                                      \
+    }                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) {                                      \
+      const int q = tid + NT * i;                                                            \
+      *(u32x4*)(BS2(buf) + rswz(q / 8, q % 8)) = RB[i];                                      \
+    }                                                                                        \
+  }
+  f32x16 acc[3];
+#pragma unroll
+  for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[pl][r] = 0.f;
+  auto compute = [&](int cur) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int c = kk * 2 + lg;
+      const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(AS2(cur) + rswz(wm * 32 + lr, c)));
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl) {
+        const bf16x8 b = __builtin_bit_cast(
+            bf16x8, *(const u32x4*)(BS2(cur) + rswz(pl * BNE + wn * 32 + lr, c)));
+        acc[pl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[pl], 0, 0, 0);
+      }
+    }
+  };
+  R_LOAD(0, ra0, rb0);
+  R_STORE(0, ra0, rb0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) R_LOAD(kt + 1, ra0, rb0);
+    compute(cur);
+    if (kt + 1 >= KT) break;
+    R_STORE(cur ^ 1, ra0, rb0);
+    __syncthreads();
+  }
+#undef R_LOAD
+#undef R_STORE
+#undef AS2
+#undef BS2
+  float* out = logits + (int64_t)z * T * E;
+  const int e = e0 + wn * 32 + lr;
+  if (e >= E) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t t = t0 + wm * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+    if (t < T) out[t * E + e] = (acc[0][r] + acc[1][r]) + acc[2][r];
+  }
+}
+
+// With 128 or more experts the 128 x 128 tile is taken: its expert tiles are mostly full,
+// and it halves the L2 traffic per logit (60 -> 55 us for 2,048 tokens, d 7168, 256
+// experts; 219 -> 175 us for 8,192 tokens, d 4096, 512 experts).
+static bool router_big(int E) { return E >= 128; }
+
+// Number of K splits of the bf16 router: enough workgroups to give every CU two 64 x 64
+// tiles or one 128 x 128 tile, keeping at least 8 K slices per split.
 static int router_ksplit(int64_t T, int E, int d) {
-  const int64_t tiles = ((T + 63) / 64) * ((E + 63) / 64);
-  int ks = (int)std::min<int64_t>(8, std::max<int64_t>(1, 512 / std::max<int64_t>(tiles, 1)));
+  const bool big = router_big(E);
+  const int64_t tiles = big ? ((T + 127) / 128) * ((E + 127) / 128) : ((T + 63) / 64) * ((E + 63) / 64);
+  const int64_t target = big ? 256 : 512;
+  int ks = (int)std::min<int64_t>(8, std::max<int64_t>(1, target / std::max<int64_t>(tiles, 1)));
   while (ks > 1 && d / 64 / ks < 8) --ks;
   return ks;
 }
@@ -287,8 +391,20 @@ hipError_t launch_route(const void* x, bool x_f32, const float* w_r, const float
     const int64_t n = (int64_t)E * d;
     router_split_kernel<<<(unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096), 256, 0, st>>>(w_r, n, w3);
     ks = router_ksplit(T, E, d);
-    router_mfma_kernel<64><<<dim3((unsigned)((E + 63) / 64), (unsigned)((T + 63) / 64), (unsigned)ks), 256, 0, st>>>(
-        (const bf16_t*)x, w3, logits, T, d, E);
+    if (router_big(E)) {
+      static bool attr = false;
+      if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void*)router_mfma2_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, R2_LDS);
+        if (e != hipSuccess) return e;
+        attr = true;
+      }
+      router_mfma2_kernel<<<dim3((unsigned)((E + 127) / 128), (unsigned)((T + 127) / 128), (unsigned)ks),
+                            R2_NT, R2_LDS, st>>>((const bf16_t*)x, w3, logits, T, d, E);
+    } else {
+      router_mfma_kernel<64><<<dim3((unsigned)((E + 63) / 64), (unsigned)((T + 63) / 64), (unsigned)ks),
+                               256, 0, st>>>((const bf16_t*)x, w3, logits, T, d, E);
+    }
   }
   const unsigned g2 = (unsigned)((T + 3) / 4);
   const int vpl = (E + 63) / 64;

@@ -45,6 +45,9 @@ MEDIUM = [
     # rotation on in both GEMMs); bf16 256-row tiles, then MX 128-row tiles
     LayerConfig("med_bf16_tail", T=2600, d=320, E=4, k=2, f=192, cid=40),
     LayerConfig("med_mx_tail", T=1500, d=256, E=4, k=2, f=256, dtype="mxfp8", cid=41),
+    # 160 experts: the router's 128 x 128 tile, the second expert tile a quarter full, the
+    # last token tile ragged, and K (18 slices of 64) split over 2 workgroups
+    LayerConfig("med_bf16_router128", T=330, d=1152, E=160, k=4, f=128, cid=43),
 ]
 
 
