@@ -140,16 +140,18 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // Stage layout in LDS: A tile [BM][KB] | B tile [BN][KB] | MX: A scale dwords, one
-// 256-byte slot per wave holding BM / 4 rows' dwords in its first half (the copy is a
+// 256-byte slot per wave holding BM / NW rows' dwords in its first half (the copy is a
 // whole-wave instruction; the other lanes write duplicates into the second half) |
-// B scale dwords [BN].  S stages form a ring.
-template <int BM, int BN, int KB, bool MX>
+// B scale dwords [BN], padded to whole-wave copies for every wave (with eight waves and
+// 256 B rows, waves 4-7 fill the padding with clamped duplicates).  S stages form a ring.
+template <int BM, int BN, int KB, bool MX, int NW>
 struct StageLayout {
+  static constexpr int NBSC = MX ? (BN * 4 + NW * 256 - 1) / (NW * 256) : 0;   // B scale copies per wave
   static constexpr int A = 0;
   static constexpr int B = BM * KB;
   static constexpr int ASC = B + BN * KB;
-  static constexpr int BSC = ASC + (MX ? 4 * 256 : 0);
-  static constexpr int SIZE = BSC + (MX ? BN * 4 : 0);
+  static constexpr int BSC = ASC + (MX ? NW * 256 : 0);
+  static constexpr int SIZE = BSC + NBSC * NW * 256;
 };
 
 // Epilogue staging in LDS: the output tile row-major, OUTC columns of OEB bytes,
@@ -173,20 +175,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   constexpr int FM = WTM / 32, FN = WTN / 32;
   constexpr int CH = KB / 16;                    // 16-byte chunks per row slice
   constexpr int RPC = 64 / CH;                   // rows per 1 KB copy
-  using SL = StageLayout<BM, BN, KB, MX>;
   constexpr int NW = WM * WN, NT = NW * 64;      // waves, threads
+  using SL = StageLayout<BM, BN, KB, MX, NW>;
   constexpr int NA = BM * KB / (NW * 1024), NB = BN * KB / (NW * 1024);   // 1 KB copies per wave
   // MX scale copies per wave and stage: one for the A rows (wave w copies rows
-  // w BM / 4 .. (w + 1) BM / 4 - 1 into its slot), BN / 256 for the shared B rows.  One
+  // w BM / NW .. (w + 1) BM / NW - 1 into its slot), and enough for the shared B rows.  One
   // shared A copy instead of a private copy of all BM rows per wave: MX gate/up GEMM
   // 1.863 -> 1.818 ms at 2,048 tokens, 0.861 -> 0.830 ms at the per-GPU share.
-  constexpr int ARW = BM / 4;                    // A scale rows per wave
-  constexpr int NASC = MX ? 1 : 0, NBSC = MX ? BN * 4 / 1024 : 0;
+  constexpr int ARW = BM / NW;                   // A scale rows per wave
+  constexpr int NASC = MX ? 1 : 0, NBSC = SL::NBSC;
   constexpr int L = NA + NB + NASC + NBSC;       // copies per wave per stage
   static_assert(BM * KB % (NW * 1024) == 0 && BN * KB % (NW * 1024) == 0, "tile / wave mismatch");
   static_assert(!MX || KB == 128, "MX stages hold whole 128-element scale groups");
-  static_assert(NW == 4 || (NW == 8 && !MX), "four waves, or eight without scales");
-  static_assert(!MX || (ARW <= 64 && BN * 4 % 1024 == 0), "scale copies");
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(!MX || (ARW <= 64 && BN * 4 % 256 == 0), "scale copies");
   static_assert(!SWIGLU || (FN % 2 == 0), "gate/up fragments come in pairs");
   static_assert(S >= 2 && S <= 4, "stages");
 
@@ -242,8 +244,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
     }
 #pragma unroll
     for (int i = 0; i < NBSC; ++i) {          // the waves share the BN scale rows
-      const int r = (4 * i + wave) * 64 + lane;
-      const bool up = SWIGLU && (4 * i + wave) * 64 >= BN / 2;
+      const int r = (NW * i + wave) * 64 + lane;   // rows past BN: clamped duplicates
+      const bool up = SWIGLU && (NW * i + wave) * 64 >= BN / 2;
       const int rr = up ? r - BN / 2 : r;
       bsc_base[i] = (up ? p.B1_scale : p.B0_scale) + (int64_t)e * p.N * 4;
       bsc_off[i] = (uint32_t)min(n0 + rr, p.N - 1) * 4;
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
     } else {
       const int i = c - NA - NB - NASC;
       dma4(bsc_base[i] + (size_t)kt * p.b_rows * 4, bsc_off[i],
-           __builtin_amdgcn_readfirstlane(st + SL::BSC + (4 * i + wave) * 256));
+           __builtin_amdgcn_readfirstlane(st + SL::BSC + (NW * i + wave) * 256));
     }
   };
   auto issue = [&](int kt) __attribute__((always_inline)) {
@@ -316,6 +318,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   // pipeline while the MFMA executes instead of before all of them.
   constexpr int KK = MX ? KB / 128 * 2 : KB / 32;   // sub-steps per stage
   constexpr int NMF = KK * FM * FN;                  // MFMAs per stage
+  // Fragments of sub-step kk + 1 are read into the second register set during the
+  // MFMAs of sub-step kk, except for MX with eight waves, whose two register sets would
+  // not fit beside the 64 x 128 accumulators: there each sub-step reads its own
+  // fragments first and the SIMD's other wave covers the LDS latency.
+  constexpr bool PF = !(MX && NW == 8);
   using Frag = std::conditional_t<MX, i32x8, bf16x8>;
   Frag af[2][FM], bfr[2][FN];
   int sa[2][FM], sb[2][FN];
@@ -376,6 +383,58 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
     }
   };
 
+  // Without prefetch (MX, eight waves): fragment rows start at multiples of 32, so the
+  // swizzled offset of row rowc + lr, 16-byte chunk 4 kk + 2 h + lg is
+  // rowc * 128 + (l0 ^ ((4 kk + 2 h) << 4)) with the per-lane
+  // l0 = lr * 128 + ((lg ^ ((lr >> 1) & 7)) << 4), and a row's scale dword sits at a
+  // wave-uniform offset + 4 lr.  Both per-lane values pass through an empty asm once
+  // per stage, so the compiler cannot hoist one address per fragment out of the K loop
+  // (those addresses spilled, and each reload waited for every copy in flight).
+  auto read_np = [&](int buf, int kk, int q, uint32_t l0, uint32_t l4) __attribute__((always_inline)) {
+    static_assert(!MX || (KB == 128 && ARW == 32), "fragment addressing");
+    const uint8_t* st = lds + buf * SL::SIZE;
+    const bool isa = q < FM;
+    const int rowc = isa ? wm * WTM + q * 32 : brow(q - FM);
+    const uint8_t* base = st + (isa ? SL::A : SL::B) + rowc * KB;
+    if constexpr (MX) {
+      const u32x4 lo = *(const u32x4*)(base + (l0 ^ ((kk * 4) << 4)));
+      const u32x4 hi = *(const u32x4*)(base + (l0 ^ ((kk * 4 + 2) << 4)));
+      const i32x8 v = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      const uint32_t w = *(const uint32_t*)(st + (isa ? SL::ASC + (rowc / ARW) * 256 : SL::BSC + rowc * 4) + l4);
+      const int sc = (int)((w >> (8 * (kk * 2 + lg))) & 0xffu);
+      if (isa) { af[0][q] = v; sa[0][q] = sc; }
+      else { bfr[0][q - FM] = v; sb[0][q - FM] = sc; }
+    } else {
+      read(buf, kk, q, 0);
+    }
+  };
+  const uint32_t l0_lane = (uint32_t)(lr * KB + ((lg ^ ((lr >> 1) & 7)) << 4)), l4_lane = (uint32_t)lr * 4;
+  // Without prefetch: the FM A fragments of sub-step kk, then per B fragment j its read
+  // followed by its FM MFMAs (one B fragment live at a time); copies spread as above.
+  auto substep_np = [&](int buf, int kk, int next, int c0, int c1, uint32_t l0, uint32_t l4)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < FM; ++q) read_np(buf, kk, q, l0, l4);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      read_np(buf, kk, FM + j, l0, l4);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = j * FM + i;
+        if constexpr (!MX)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[0][i], bfr[0][j], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              af[0][i], bfr[0][j], acc[i][j], 0, 0, 0, sa[0][i], 0, sb[0][j]);
+#pragma unroll
+        for (int c = c0; c < c1; ++c)
+          if ((c - c0) * FM * FN / (c1 - c0) == m && next >= 0) issue_one(next, c);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
   // S-stage ring: stages kt+1 .. kt+S-1 stream in while stage kt is computed.
   // One barrier per stage: it publishes stage kt (every wave waited for its own
   // copies) and retires the buffer of stage kt-1, which the copies of stage kt+S-1
@@ -388,11 +447,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
       wait_stage(min(S - 2, KT - 1 - kt));
       __syncthreads();
       const int buf = kt % S, next = kt + S - 1 < KT ? kt + S - 1 : -1;
+      if constexpr (PF) {
 #pragma unroll
-      for (int q = 0; q < FM + FN; ++q) read(buf, 0, q, 0);
+        for (int q = 0; q < FM + FN; ++q) read(buf, 0, q, 0);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        substep(kk & 1, kk + 1 < KK ? buf : -1, kk + 1, next, kk * L / KK, (kk + 1) * L / KK);
+        for (int kk = 0; kk < KK; ++kk)
+          substep(kk & 1, kk + 1 < KK ? buf : -1, kk + 1, next, kk * L / KK, (kk + 1) * L / KK);
+      } else {
+        uint32_t l0 = l0_lane, l4 = l4_lane;
+        asm volatile("" : "+v"(l0), "+v"(l4));
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) substep_np(buf, kk, next, kk * L / KK, (kk + 1) * L / KK, l0, l4);
+      }
     }
   } else {
     // Barrier before the last sub-step of each stage: the next stage is waited for
@@ -497,7 +563,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
 template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S, int POL>
 static hipError_t run_mfma(const GemmArgs& a, int max_tiles, hipStream_t st) {
   const int nt = SWIGLU ? (a.N + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
-  const size_t lds = std::max<size_t>((size_t)S * StageLayout<BM, BN, KB, MX>::SIZE,
+  const size_t lds = std::max<size_t>((size_t)S * StageLayout<BM, BN, KB, MX, WM * WN>::SIZE,
                                       EpiLayout<BM, BN, SWIGLU, MX>::SIZE);
   auto kern = gg_mfma_kernel<BM, BN, WM, WN, KB, SWIGLU, MX, S, POL>;
   static bool attr_set = false;   // opt in to more than 64 KB of LDS once per process
@@ -584,7 +650,7 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
 }
 
 // ============================================================ launcher
-// Two bf16 MFMA tile shapes.
+// Two MFMA tile shapes (bf16 and MX alike).
 //  * 128 x 256, 128-byte K slices, 3 stages: one row tile holds every row of an
 //    expert with up to 128 rows, so each weight is read from HBM once; the
 //    2,048-token layer (64 rows per expert on average) is bound by that stream.
@@ -596,12 +662,16 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
 //    slices in 4 stages.  Per 64-wide K stage a SIMD runs 64 MFMAs (2048 clocks)
 //    while LDS serves 192 KB of fragment reads and 64 KB of copies (1024 clocks at
 //    256 B/clock).
-// MX keeps the first shape (its stages hold whole 128-element scale groups).
+// MX takes the same two shapes, with 128 K elements per stage.  In the 256 x 256 tile
+// its operand fragments (twice the bf16 size) are not prefetched into a second register
+// set; the fragments of a sub-step are read just before its MFMAs.  Per-GPU share
+// (4 experts, 16,384 rows), MXFP8 gate/up | down in ms, 128 x 256 -> 256 x 256:
+// 0.827 -> 0.585 | 0.391 -> 0.290.
 constexpr int MFMA_BM = 128, MFMA_BM_BIG = 256;
 constexpr int BIG_ROWS_MIN = 256;   // mean rows per expert from which the 256-row tile is used
 
 static bool use_big(int dtype, int64_t n, int E) {
-  return dtype == 1 && n >= (int64_t)BIG_ROWS_MIN * E;
+  return (dtype == 1 || dtype == 2) && n >= (int64_t)BIG_ROWS_MIN * E;
 }
 
 // Rotation of the K loop's starting step per tile (measured on gfx950, gate/up | down
@@ -722,11 +792,13 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
 #define RUN_POL(P, G, ...)                                                 \
   err = (P) == 3 ? run_mfma<__VA_ARGS__, 3>(G, max_tiles, st)              \
                  : run_mfma<__VA_ARGS__, 2>(G, max_tiles, st);
-  if (big) { RUN_POL(pol1, g1, MFMA_BM_BIG, 256, 4, 2, 128, true, false, 2) }
+  if (big && dtype == 2) { RUN_POL(pol1, g1, MFMA_BM_BIG, 256, 4, 2, 128, true, true, 2) }
+  else if (big) { RUN_POL(pol1, g1, MFMA_BM_BIG, 256, 4, 2, 128, true, false, 2) }
   else if (dtype == 1) { RUN_POL(pol1, g1, MFMA_BM, 256, 2, 2, 128, true, false, 3) }
   else { RUN_POL(pol1, g1, MFMA_BM, 256, 2, 2, 128, true, true, 3) }
   if (err != hipSuccess || (err = mark(1)) != hipSuccess) return err;
-  if (big) { RUN_POL(pol2, g2, MFMA_BM_BIG, 256, 4, 2, 128, false, false, 2) }
+  if (big && dtype == 2) { RUN_POL(pol2, g2, MFMA_BM_BIG, 256, 4, 2, 128, false, true, 2) }
+  else if (big) { RUN_POL(pol2, g2, MFMA_BM_BIG, 256, 4, 2, 128, false, false, 2) }
   else if (dtype == 1) { RUN_POL(pol2, g2, MFMA_BM, 256, 2, 2, 128, false, false, 3) }
   else { RUN_POL(pol2, g2, MFMA_BM, 256, 2, 2, 128, false, true, 3) }
 #undef RUN_POL

@@ -48,6 +48,9 @@ MEDIUM = [
     # 160 experts: the router's 128 x 128 tile, the second expert tile a quarter full, the
     # last token tile ragged, and K (18 slices of 64) split over 2 workgroups
     LayerConfig("med_bf16_router128", T=330, d=1152, E=160, k=4, f=128, cid=43),
+    # MX with at least 256 rows per expert: the 256 x 256 eight-wave tile; ragged rows, the
+    # down GEMM's second column tile half full
+    LayerConfig("med_mx_big256", T=1400, d=384, E=4, k=2, f=384, dtype="mxfp8", cid=44),
 ]
 
 
