@@ -405,7 +405,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.d, "experts": cfg.E,
                    "top_k": cfg.k, "ffn": cfg.f, "capacity": cfg.C, "ring_head": 0,
                    "step": "route+dispatch+gate/up GEMM+down GEMM+combine"},
-        "roofline": {"kernel": "gg_mfma_kernel<128,256,2,2,SWIGLU,bf16> (gate/up + SwiGLU)",
+        "roofline": {"kernel": "gg_mfma_kernel<128,256,2,4,SWIGLU,bf16> (gate/up + SwiGLU)",
                      "bound": "hbm", "achieved": round(ach1, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach1 / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("gemm1_swiglu_bf16", alg1),

@@ -322,7 +322,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   // MFMAs of sub-step kk, except for MX with eight waves, whose two register sets would
   // not fit beside the 64 x 128 accumulators: there each sub-step reads its own
   // fragments first and the SIMD's other wave covers the LDS latency.
-  constexpr bool PF = !(MX && NW == 8);
+  constexpr bool PF = !(MX && NW == 8 && FM * FN >= 8);
   using Frag = std::conditional_t<MX, i32x8, bf16x8>;
   Frag af[2][FM], bfr[2][FN];
   int sa[2][FM], sb[2][FN];
@@ -391,7 +391,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   // per stage, so the compiler cannot hoist one address per fragment out of the K loop
   // (those addresses spilled, and each reload waited for every copy in flight).
   auto read_np = [&](int buf, int kk, int q, uint32_t l0, uint32_t l4) __attribute__((always_inline)) {
-    static_assert(!MX || (KB == 128 && ARW == 32), "fragment addressing");
+    static_assert(PF || !MX || (KB == 128 && ARW == 32), "fragment addressing");
     const uint8_t* st = lds + buf * SL::SIZE;
     const bool isa = q < FM;
     const int rowc = isa ? wm * WTM + q * 32 : brow(q - FM);
@@ -651,9 +651,13 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
 
 // ============================================================ launcher
 // Two MFMA tile shapes (bf16 and MX alike).
-//  * 128 x 256, 128-byte K slices, 3 stages: one row tile holds every row of an
-//    expert with up to 128 rows, so each weight is read from HBM once; the
-//    2,048-token layer (64 rows per expert on average) is bound by that stream.
+//  * 128 x 256, 128-byte K slices, 3 stages, eight waves of 64 x 64: one row tile
+//    holds every row of an expert with up to 128 rows, so each weight is read from
+//    HBM once; the 2,048-token layer (64 rows per expert on average) is bound by that
+//    stream.  Eight waves (two per SIMD) instead of four of 64 x 128: while one wave
+//    waits at a stage barrier or on its copies the other's MFMAs run (2,048 tokens,
+//    gate/up | down in ms: bf16 2.547 | 1.309 -> 2.532 | 1.257, MX 1.652 | 0.800 ->
+//    1.491 | 0.755; skewed 8,192 tokens bf16 2.153 | 1.446 -> 2.111 | 1.320).
 //  * 256 x 256, 128-byte K slices, 2 stages (128 KB), eight waves of 64 x 128 (two
 //    per SIMD, so that one wave's MFMAs run while the other waits): with many
 //    rows per expert every row tile re-reads the weights and the kernel is bound
@@ -706,9 +710,14 @@ static int kstart_rotates(bool swiglu, int dtype, int64_t n, int E, int BM) {
 //    gate/up 2.273 | 2.252 | 2.628, share bf16 1.006 | 0.992 | 1.165).
 // A bare copy of the gate/up pattern with a per-tile store behaves the same way: 2.54 ms
 // with default stores whichever the load policy, 2.29 ms with both non-temporal.
-// Whole 2,048-token bf16 forward: 4.205 -> 4.093 ms.
-static int gemm_policy(bool swiglu, int64_t n, int E, int BM) {
-  return (!swiglu && n <= (int64_t)BM * E) ? 3 : 2;
+// Whole 2,048-token bf16 forward: 4.205 -> 4.093 ms.  These figures are for the tile of
+// four waves.  With eight waves the bf16 gate/up GEMM with one row tile per expert
+// gains from non-temporal weight copies too (2.550 | 2.340 ms at 2,048 tokens, whole
+// forward 4.019 -> 3.837 ms); the MX gate/up GEMM still loses (1.485 | 1.553), and so
+// does a gate/up GEMM whose panels several row tiles share (skewed 2.166 | 2.431).
+static int gemm_policy(bool swiglu, int dtype, int64_t n, int E, int BM) {
+  if (n > (int64_t)BM * E) return 2;   // weight panels shared by several row tiles
+  return (!swiglu || dtype == 1) ? 3 : 2;
 }
 
 static int max_tiles_for(int64_t n, int E, int BM) { return (int)((n + BM - 1) / BM) + E; }
@@ -788,19 +797,19 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
   g2.b_rows = (int64_t)E * d;
   g1.rotate = kstart_rotates(true, dtype, n, E, BM);
   g2.rotate = kstart_rotates(false, dtype, n, E, BM);
-  const int pol1 = gemm_policy(true, n, E, BM), pol2 = gemm_policy(false, n, E, BM);
+  const int pol1 = gemm_policy(true, dtype, n, E, BM), pol2 = gemm_policy(false, dtype, n, E, BM);
 #define RUN_POL(P, G, ...)                                                 \
   err = (P) == 3 ? run_mfma<__VA_ARGS__, 3>(G, max_tiles, st)              \
                  : run_mfma<__VA_ARGS__, 2>(G, max_tiles, st);
   if (big && dtype == 2) { RUN_POL(pol1, g1, MFMA_BM_BIG, 256, 4, 2, 128, true, true, 2) }
   else if (big) { RUN_POL(pol1, g1, MFMA_BM_BIG, 256, 4, 2, 128, true, false, 2) }
-  else if (dtype == 1) { RUN_POL(pol1, g1, MFMA_BM, 256, 2, 2, 128, true, false, 3) }
-  else { RUN_POL(pol1, g1, MFMA_BM, 256, 2, 2, 128, true, true, 3) }
+  else if (dtype == 1) { RUN_POL(pol1, g1, MFMA_BM, 256, 2, 4, 128, true, false, 3) }
+  else { RUN_POL(pol1, g1, MFMA_BM, 256, 2, 4, 128, true, true, 3) }
   if (err != hipSuccess || (err = mark(1)) != hipSuccess) return err;
   if (big && dtype == 2) { RUN_POL(pol2, g2, MFMA_BM_BIG, 256, 4, 2, 128, false, true, 2) }
   else if (big) { RUN_POL(pol2, g2, MFMA_BM_BIG, 256, 4, 2, 128, false, false, 2) }
-  else if (dtype == 1) { RUN_POL(pol2, g2, MFMA_BM, 256, 2, 2, 128, false, false, 3) }
-  else { RUN_POL(pol2, g2, MFMA_BM, 256, 2, 2, 128, false, true, 3) }
+  else if (dtype == 1) { RUN_POL(pol2, g2, MFMA_BM, 256, 2, 4, 128, false, false, 3) }
+  else { RUN_POL(pol2, g2, MFMA_BM, 256, 2, 4, 128, false, true, 3) }
 #undef RUN_POL
   if (err != hipSuccess) return err;
   return mark(2);
