@@ -187,7 +187,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   constexpr int L = NA + NB + NASC + NBSC;       // copies per wave per stage
   static_assert(BM * KB % (NW * 1024) == 0 && BN * KB % (NW * 1024) == 0, "tile / wave mismatch");
   static_assert(!MX || KB == 128, "MX stages hold whole 128-element scale groups");
-  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  static_assert(NW == 4 || NW == 8 || (NW == 16 && !MX), "four or eight waves, sixteen without scales");
   static_assert(!MX || (ARW <= 64 && BN * 4 % 256 == 0), "scale copies");
   static_assert(!SWIGLU || (FN % 2 == 0), "gate/up fragments come in pairs");
   static_assert(S >= 2 && S <= 4, "stages");
@@ -381,6 +381,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
         if ((c - c0) * FM * FN / (c1 - c0) == m && next >= 0) issue_one(next, c);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // fewer MFMAs than fragments (a 32-row wave tile): read the rest after them
+#pragma unroll
+    for (int q = FM * FN; q < FM + FN; ++q)
+      if (rbuf >= 0) read(rbuf, rkk, q, set ^ 1);
   };
 
   // Without prefetch (MX, eight waves): fragment rows start at multiples of 32, so the
@@ -658,10 +662,14 @@ __global__ __launch_bounds__(256) void gg_f32_kernel(const float* __restrict__ A
 //    waits at a stage barrier or on its copies the other's MFMAs run (2,048 tokens,
 //    gate/up | down in ms: bf16 2.547 | 1.309 -> 2.532 | 1.257, MX 1.652 | 0.800 ->
 //    1.491 | 0.755; skewed 8,192 tokens bf16 2.153 | 1.446 -> 2.111 | 1.320).
-//  * 256 x 256, 128-byte K slices, 2 stages (128 KB), eight waves of 64 x 128 (two
-//    per SIMD, so that one wave's MFMAs run while the other waits): with many
-//    rows per expert every row tile re-reads the weights and the kernel is bound
-//    inside the CU, by the rate at which L2 serves the stages.  Whole 128-byte
+//  * 256 x 256, 128-byte K slices, 2 stages (128 KB), sixteen waves of 64 x 64 for
+//    bf16 (four per SIMD, so that one wave's MFMAs run while the others wait; eight
+//    waves of 64 x 128 measured 1.534 ms against 1.514 at the per-GPU share; in the
+//    128 x 256 tile sixteen waves of 32 x 64 were slower: down GEMM 1.277 -> 1.353 ms
+//    at 2,048 tokens), eight
+//    waves of 64 x 128 for MX: with many rows per expert every row tile re-reads the
+//    weights and the kernel is bound inside the CU, by the rate at which L2 serves
+//    the stages.  Whole 128-byte
 //    lines per copy and one barrier per 64 K measured ~2 % faster than 64-byte
 //    slices in 4 stages.  Per 64-wide K stage a SIMD runs 64 MFMAs (2048 clocks)
 //    while LDS serves 192 KB of fragment reads and 64 KB of copies (1024 clocks at
@@ -802,12 +810,12 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
   err = (P) == 3 ? run_mfma<__VA_ARGS__, 3>(G, max_tiles, st)              \
                  : run_mfma<__VA_ARGS__, 2>(G, max_tiles, st);
   if (big && dtype == 2) { RUN_POL(pol1, g1, MFMA_BM_BIG, 256, 4, 2, 128, true, true, 2) }
-  else if (big) { RUN_POL(pol1, g1, MFMA_BM_BIG, 256, 4, 2, 128, true, false, 2) }
+  else if (big) { RUN_POL(pol1, g1, MFMA_BM_BIG, 256, 4, 4, 128, true, false, 2) }
   else if (dtype == 1) { RUN_POL(pol1, g1, MFMA_BM, 256, 2, 4, 128, true, false, 3) }
   else { RUN_POL(pol1, g1, MFMA_BM, 256, 2, 4, 128, true, true, 3) }
   if (err != hipSuccess || (err = mark(1)) != hipSuccess) return err;
   if (big && dtype == 2) { RUN_POL(pol2, g2, MFMA_BM_BIG, 256, 4, 2, 128, false, true, 2) }
-  else if (big) { RUN_POL(pol2, g2, MFMA_BM_BIG, 256, 4, 2, 128, false, false, 2) }
+  else if (big) { RUN_POL(pol2, g2, MFMA_BM_BIG, 256, 4, 4, 128, false, false, 2) }
   else if (dtype == 1) { RUN_POL(pol2, g2, MFMA_BM, 256, 2, 4, 128, false, false, 3) }
   else { RUN_POL(pol2, g2, MFMA_BM, 256, 2, 4, 128, false, true, 3) }
 #undef RUN_POL
