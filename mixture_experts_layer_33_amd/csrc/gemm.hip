@@ -139,19 +139,19 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Stage layout in LDS: A tile [BM][KB] | B tile [BN][KB] | MX: A scale dwords, one
-// 256-byte slot per wave holding BM / NW rows' dwords in its first half (the copy is a
-// whole-wave instruction; the other lanes write duplicates into the second half) |
-// B scale dwords [BN], padded to whole-wave copies for every wave (with eight waves and
-// 256 B rows, waves 4-7 fill the padding with clamped duplicates).  S stages form a ring.
+// Stage layout in LDS: A tile [BM][KB] | B tile [BN][KB] | MX: A scale dwords [BM] |
+// B scale dwords [BN] | padding.  The scale dwords arrive in whole-wave copies of 64 rows
+// each (BM / 64 for A, then BN / 64 for B); the count is padded to a multiple of the
+// wave count with clamped duplicates written past the B dwords, so that every wave
+// issues the same copies.  S stages form a ring.
 template <int BM, int BN, int KB, bool MX, int NW>
 struct StageLayout {
-  static constexpr int NBSC = MX ? (BN * 4 + NW * 256 - 1) / (NW * 256) : 0;   // B scale copies per wave
+  static constexpr int NSC = MX ? (BM / 64 + BN / 64 + NW - 1) / NW : 0;   // scale copies per wave
   static constexpr int A = 0;
   static constexpr int B = BM * KB;
   static constexpr int ASC = B + BN * KB;
-  static constexpr int BSC = ASC + (MX ? NW * 256 : 0);
-  static constexpr int SIZE = BSC + NBSC * NW * 256;
+  static constexpr int BSC = ASC + (MX ? BM * 4 : 0);
+  static constexpr int SIZE = ASC + NSC * NW * 256;
 };
 
 // Epilogue staging in LDS: the output tile row-major, OUTC columns of OEB bytes,
@@ -178,17 +178,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   constexpr int NW = WM * WN, NT = NW * 64;      // waves, threads
   using SL = StageLayout<BM, BN, KB, MX, NW>;
   constexpr int NA = BM * KB / (NW * 1024), NB = BN * KB / (NW * 1024);   // 1 KB copies per wave
-  // MX scale copies per wave and stage: one for the A rows (wave w copies rows
-  // w BM / NW .. (w + 1) BM / NW - 1 into its slot), and enough for the shared B rows.  One
-  // shared A copy instead of a private copy of all BM rows per wave: MX gate/up GEMM
-  // 1.863 -> 1.818 ms at 2,048 tokens, 0.861 -> 0.830 ms at the per-GPU share.
-  constexpr int ARW = BM / NW;                   // A scale rows per wave
-  constexpr int NASC = MX ? 1 : 0, NBSC = SL::NBSC;
-  constexpr int L = NA + NB + NASC + NBSC;       // copies per wave per stage
+  // MX scale copies: copy k of the tile (wave k mod NW) brings 64 rows' dwords, A rows
+  // for k < SCA, then B rows.  Per stage that is BM / 64 + BN / 64 whole-wave copies
+  // (one per wave in both tile shapes) where a copy of A and of B rows per wave took
+  // twice as many: 2,048-token MX gate/up | down 1.486 | 0.746 ms with them, 1.425 |
+  // 0.703 ms with no scale copies at all (a timing probe).
+  constexpr int SCA = MX ? BM / 64 : 0, SCB = MX ? BN / 64 : 0;
+  constexpr int NSC = SL::NSC;
+  constexpr int L = NA + NB + NSC;               // copies per wave per stage
   static_assert(BM * KB % (NW * 1024) == 0 && BN * KB % (NW * 1024) == 0, "tile / wave mismatch");
   static_assert(!MX || KB == 128, "MX stages hold whole 128-element scale groups");
   static_assert(NW == 4 || NW == 8 || (NW == 16 && !MX), "four or eight waves, sixteen without scales");
-  static_assert(!MX || (ARW <= 64 && BN * 4 % 256 == 0), "scale copies");
+  static_assert(!MX || (BM % 64 == 0 && BN % 64 == 0), "scale copies of 64 rows");
   static_assert(!SWIGLU || (FN % 2 == 0), "gate/up fragments come in pairs");
   static_assert(S >= 2 && S <= 4, "stages");
 
@@ -234,21 +235,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
     b_base[i] = (up ? p.B1 : p.B0) + (int64_t)e * p.N * Kb;
     b_off[i] = (uint32_t)min(n0 + rr, p.N - 1) * Kb + c * 16;
   }
-  uint32_t asc_off[NASC > 0 ? NASC : 1], bsc_off[NBSC > 0 ? NBSC : 1];
-  const uint8_t* bsc_base[NBSC > 0 ? NBSC : 1];
+  uint32_t sc_off[NSC > 0 ? NSC : 1];
+  const uint8_t* sc_base[NSC > 0 ? NSC : 1];
+  int64_t sc_rows[NSC > 0 ? NSC : 1];           // rows of the [K/128][rows][4] scale array
   if (MX) {
 #pragma unroll
-    for (int i = 0; i < NASC; ++i) {          // the waves share the BM scale rows
-      const int r = wave * ARW + min(lane, ARW - 1);
-      asc_off[i] = (uint32_t)ring_slot(p.head, seg, row0 + min(r, rows - 1), p.C) * 4;
-    }
-#pragma unroll
-    for (int i = 0; i < NBSC; ++i) {          // the waves share the BN scale rows
-      const int r = (NW * i + wave) * 64 + lane;   // rows past BN: clamped duplicates
-      const bool up = SWIGLU && (NW * i + wave) * 64 >= BN / 2;
-      const int rr = up ? r - BN / 2 : r;
-      bsc_base[i] = (up ? p.B1_scale : p.B0_scale) + (int64_t)e * p.N * 4;
-      bsc_off[i] = (uint32_t)min(n0 + rr, p.N - 1) * 4;
+    for (int i = 0; i < NSC; ++i) {
+      const int k = NW * i + wave;              // the tile's scale copy k (wave-uniform)
+      if (k < SCA) {
+        const int r = 64 * k + lane;
+        sc_base[i] = p.A_scale;
+        sc_rows[i] = p.a_rows;
+        sc_off[i] = (uint32_t)ring_slot(p.head, seg, row0 + min(r, rows - 1), p.C) * 4;
+      } else {
+        const int kb = k < SCA + SCB ? k - SCA : 0;   // padding copies repeat B copy 0
+        const int r = 64 * kb + lane;
+        const bool up = SWIGLU && 64 * kb >= BN / 2;
+        const int rr = up ? r - BN / 2 : r;
+        sc_base[i] = (up ? p.B1_scale : p.B0_scale) + (int64_t)e * p.N * 4;
+        sc_rows[i] = p.b_rows;
+        sc_off[i] = (uint32_t)min(n0 + rr, p.N - 1) * 4;
+      }
     }
   }
   // K steps are taken in the order s0, s0 + 1, ..., KT - 1, 0, ..., s0 - 1: with
@@ -267,14 +274,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
       const int i = c - NA;
       if (POL & 1) dma16nt(b_base[i] + (size_t)kt * KB, b_off[i], __builtin_amdgcn_readfirstlane(st + SL::B + (NW * i + wave) * 1024));
       else dma16(b_base[i] + (size_t)kt * KB, b_off[i], __builtin_amdgcn_readfirstlane(st + SL::B + (NW * i + wave) * 1024));
-    } else if (c < NA + NB + NASC) {
-      const int i = c - NA - NB;
-      dma4(p.A_scale + (size_t)kt * p.a_rows * 4, asc_off[i],
-           __builtin_amdgcn_readfirstlane(st + SL::ASC + wave * 256));
     } else {
-      const int i = c - NA - NB - NASC;
-      dma4(bsc_base[i] + (size_t)kt * p.b_rows * 4, bsc_off[i],
-           __builtin_amdgcn_readfirstlane(st + SL::BSC + (NW * i + wave) * 256));
+      const int i = c - NA - NB;
+      dma4(sc_base[i] + (size_t)kt * sc_rows[i] * 4, sc_off[i],
+           __builtin_amdgcn_readfirstlane(st + SL::ASC + (NW * i + wave) * 256));
     }
   };
   auto issue = [&](int kt) __attribute__((always_inline)) {
@@ -356,7 +359,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
       const u32x4 hi = *(const u32x4*)(base + swz<KB>(r, cb));
       const i32x8 v = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      const int ri = isa ? (r / ARW) * 64 + r % ARW : r;   // A row r sits in slot r / ARW
+      const int ri = r;                          // row r's dword (A rows and B rows alike)
       const int sc = (int)(((isa ? asc : bsc)[ri] >> (8 * blk)) & 0xffu);
       if (isa) { af[set][q] = v; sa[set][q] = sc; }
       else { bfr[set][q - FM] = v; sb[set][q - FM] = sc; }
@@ -395,7 +398,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   // per stage, so the compiler cannot hoist one address per fragment out of the K loop
   // (those addresses spilled, and each reload waited for every copy in flight).
   auto read_np = [&](int buf, int kk, int q, uint32_t l0, uint32_t l4) __attribute__((always_inline)) {
-    static_assert(PF || !MX || (KB == 128 && ARW == 32), "fragment addressing");
+    static_assert(PF || KB == 128, "fragment addressing");
     const uint8_t* st = lds + buf * SL::SIZE;
     const bool isa = q < FM;
     const int rowc = isa ? wm * WTM + q * 32 : brow(q - FM);
@@ -405,7 +408,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
       const u32x4 hi = *(const u32x4*)(base + (l0 ^ ((kk * 4 + 2) << 4)));
       const i32x8 v = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                             (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      const uint32_t w = *(const uint32_t*)(st + (isa ? SL::ASC + (rowc / ARW) * 256 : SL::BSC + rowc * 4) + l4);
+      const uint32_t w = *(const uint32_t*)(st + (isa ? SL::ASC : SL::BSC) + rowc * 4 + l4);
       const int sc = (int)((w >> (8 * (kk * 2 + lg))) & 0xffu);
       if (isa) { af[0][q] = v; sa[0][q] = sc; }
       else { bfr[0][q - FM] = v; sb[0][q - FM] = sc; }
