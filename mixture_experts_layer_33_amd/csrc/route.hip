@@ -305,13 +305,15 @@ __global__ __launch_bounds__(R2_NT) void router_mfma2_kernel(
 // experts; 219 -> 175 us for 8,192 tokens, d 4096, 512 experts).
 static bool router_big(int E) { return E >= 128; }
 
+constexpr int RT_MAX_KS = 8;   // most K splits of the bf16 router (partial logit planes)
+
 // Number of K splits of the bf16 router: enough workgroups to give every CU two 64 x 64
 // tiles or one 128 x 128 tile, keeping at least 8 K slices per split.
 static int router_ksplit(int64_t T, int E, int d) {
   const bool big = router_big(E);
   const int64_t tiles = big ? ((T + 127) / 128) * ((E + 127) / 128) : ((T + 63) / 64) * ((E + 63) / 64);
   const int64_t target = big ? 256 : 512;
-  int ks = (int)std::min<int64_t>(8, std::max<int64_t>(1, target / std::max<int64_t>(tiles, 1)));
+  int ks = (int)std::min<int64_t>(RT_MAX_KS, std::max<int64_t>(1, target / std::max<int64_t>(tiles, 1)));
   while (ks > 1 && d / 64 / ks < 8) --ks;
   return ks;
 }
@@ -319,21 +321,39 @@ static int router_ksplit(int64_t T, int E, int d) {
 // ----------------------------------------------------------------------------
 // One wavefront per token: softmax statistics, top-k (ties to the lower id),
 // ascending-id output order, renormalised gates.
-template <int VPL>
+template <int VPL, bool SPLIT>
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float* __restrict__ logits, int KS, const float* __restrict__ bias, int64_t T, int E,
     int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  // logit = ((plane 0 + plane 1) + ...) + bias, every lane for its experts lane + 64 i
+  // logit = ((plane 0 + plane 1) + ...) + bias, every lane for its experts lane + 64 i.
+  // With K split (SPLIT, KS <= RT_MAX_KS planes), all planes' loads are issued before
+  // the first addition: a loop over the runtime plane count waited for each load in turn
+  // (2,048 tokens, 8 planes: 20.4 -> 17.1 us).  A separate instantiation, so that the
+  // single-plane launches keep their few registers and their occupancy.
   float lv[VPL];
+  if constexpr (!SPLIT) {
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int e = min(lane + 64 * i, E - 1);
-    float v = logits[t * E + e];
-    for (int zz = 1; zz < KS; ++zz) v += logits[((int64_t)zz * T + t) * E + e];
-    lv[i] = v + (bias ? bias[e] : 0.f);
+    for (int i = 0; i < VPL; ++i) {
+      const int e = min(lane + 64 * i, E - 1);
+      lv[i] = logits[t * E + e] + (bias ? bias[e] : 0.f);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int e = min(lane + 64 * i, E - 1);
+      float part[RT_MAX_KS];
+#pragma unroll
+      for (int zz = 0; zz < RT_MAX_KS; ++zz)
+        part[zz] = zz < KS ? logits[((int64_t)zz * T + t) * E + e] : 0.f;
+      float v = part[0];
+#pragma unroll
+      for (int zz = 1; zz < RT_MAX_KS; ++zz)
+        if (zz < KS) v += part[zz];
+      lv[i] = v + (bias ? bias[e] : 0.f);
+    }
   }
   int choice, rank;
   float gate;
@@ -408,11 +428,17 @@ hipError_t launch_route(const void* x, bool x_f32, const float* w_r, const float
   }
   const unsigned g2 = (unsigned)((T + 3) / 4);
   const int vpl = (E + 63) / 64;
-  if (vpl <= 1) router_topk_kernel<1><<<g2, 256, 0, st>>>(logits, ks, b_r, T, E, k, topk_idx, topk_gate);
-  else if (vpl <= 2) router_topk_kernel<2><<<g2, 256, 0, st>>>(logits, ks, b_r, T, E, k, topk_idx, topk_gate);
-  else if (vpl <= 4) router_topk_kernel<4><<<g2, 256, 0, st>>>(logits, ks, b_r, T, E, k, topk_idx, topk_gate);
-  else if (vpl <= 8) router_topk_kernel<8><<<g2, 256, 0, st>>>(logits, ks, b_r, T, E, k, topk_idx, topk_gate);
-  else router_topk_kernel<16><<<g2, 256, 0, st>>>(logits, ks, b_r, T, E, k, topk_idx, topk_gate);
+#define TOPK(V)                                                                                   \
+  {                                                                                               \
+    if (ks > 1) router_topk_kernel<V, true><<<g2, 256, 0, st>>>(logits, ks, b_r, T, E, k, topk_idx, topk_gate); \
+    else router_topk_kernel<V, false><<<g2, 256, 0, st>>>(logits, ks, b_r, T, E, k, topk_idx, topk_gate);      \
+  }
+  if (vpl <= 1) TOPK(1)
+  else if (vpl <= 2) TOPK(2)
+  else if (vpl <= 4) TOPK(4)
+  else if (vpl <= 8) TOPK(8)
+  else TOPK(16)
+#undef TOPK
   expert_count_kernel<<<1, 1024, E * sizeof(int32_t), st>>>(topk_idx, T * k, E, expert_count);
   return hipGetLastError();
 }
