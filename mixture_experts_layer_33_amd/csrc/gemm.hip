@@ -59,8 +59,8 @@ hipError_t launch_build_tiles(const int32_t* expert_offset, int E, int BM, int32
 
 // ============================================================ bf16 / MX MFMA GEMM
 // Workgroup tile BM x BN, K staged in KB-byte row slices (KB = 128: 64 bf16 or
-// 128 fp8; KB = 64: 32 bf16) through an S-stage LDS ring.  4 waves in a WM x WN
-// grid; each wave owns FM x FN 32x32 fragments.
+// 128 fp8; KB = 64: 32 bf16) through an S-stage LDS ring.  WM x WN waves (4, 8 or
+// 16); each wave owns FM x FN 32x32 fragments.
 //
 // SWIGLU: the B tile stacks BN/2 rows of W_gate over the same BN/2 rows of
 // W_up, and every wave holds matching gate and up fragments, so the epilogue
@@ -322,9 +322,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   constexpr int KK = MX ? KB / 128 * 2 : KB / 32;   // sub-steps per stage
   constexpr int NMF = KK * FM * FN;                  // MFMAs per stage
   // Fragments of sub-step kk + 1 are read into the second register set during the
-  // MFMAs of sub-step kk, except for MX with eight waves, whose two register sets would
-  // not fit beside the 64 x 128 accumulators: there each sub-step reads its own
-  // fragments first and the SIMD's other wave covers the LDS latency.
+  // MFMAs of sub-step kk, except for MX waves of 64 x 128 (eight waves in 256 x 256),
+  // whose two register sets would not fit beside the accumulators: there each sub-step
+  // reads its own fragments first and the SIMD's other wave covers the LDS latency.
   constexpr bool PF = !(MX && NW == 8 && FM * FN >= 8);
   using Frag = std::conditional_t<MX, i32x8, bf16x8>;
   Frag af[2][FM], bfr[2][FN];
@@ -704,6 +704,8 @@ static bool use_big(int dtype, int64_t n, int E) {
 //    2.218 -> 2.298 skewed): the column tiles of a row tile then no longer read the same
 //    token-row slices at the same time, so those rows are held in L2 longer; the MX
 //    down GEMM there is unchanged within noise (0.907 -> 0.918), so it is not rotated.
+// Re-measured with the eight-wave 128 x 256 tile (2,048 tokens, without -> with): bf16
+// down 1.472 -> 1.279, gate/up 2.307 -> 2.336; MX down 0.733 -> 0.756; the rules stand.
 static int kstart_rotates(bool swiglu, int dtype, int64_t n, int E, int BM) {
   if (n >= 2 * (int64_t)BM * E) return 1;
   return (!swiglu && dtype == 1) ? 1 : 0;
