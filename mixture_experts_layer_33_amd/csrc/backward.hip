@@ -100,16 +100,20 @@ __device__ __forceinline__ v4i16_t ds_tr16(const uint8_t* lds_ptr) {
 // read as MFMA fragments with transposing reads: lane l receives column l % 32 at K
 // rows 8 (l / 32) .. 8 (l / 32) + 7 of a 16-row sub-step, in two reads of 4 rows.
 // Both tiles are filled by global -> LDS copies (no register staging) through a ring
-// of DWS stages, DWS - 1 of them in flight while one is multiplied.
-constexpr int DK = 32, DWS = 4;
+// of DWS stages, DWS - 1 of them in flight while one is multiplied.  Three stages
+// (48 KB), so three workgroups share a CU: skewed 8,192-token backward 9.92 -> 9.79 ms
+// against four stages and two workgroups; five stages and two workgroups 10.9 ms, two
+// stages and four workgroups 9.76 ms.
+constexpr int DK = 32, DWS = 3;
 constexpr int DA_BYTES = BT * DK * 2, DB_BYTES = DK * BT * 2, DSTAGE = DA_BYTES + DB_BYTES;
-constexpr int DG_LDS = DWS * DSTAGE;   // 64 KB; the epilogue staging (34,816 bytes) reuses it
+constexpr int DG_LDS = DWS * DSTAGE > STAGE_BYTES ? DWS * DSTAGE : STAGE_BYTES;   // the epilogue staging (34,816 bytes) reuses it
+static_assert(DG_LDS >= STAGE_BYTES && DG_LDS >= DWS * DSTAGE, "dgrad LDS holds the ring and the epilogue staging");
 constexpr int DL = (DA_BYTES + DB_BYTES) / 4096;   // 1 KB copies per wave per stage
 
 __device__ __forceinline__ int aswz(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
 template <bool DOWN>
-__global__ __launch_bounds__(256, 2) void dgrad_kernel(DgradArgs p) {
+__global__ __launch_bounds__(256, 3) void dgrad_kernel(DgradArgs p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   __shared__ float red[2][BT];
