@@ -244,13 +244,22 @@ def forward_tokens(tokens: Sequence[int], x: np.ndarray, routing: Routing, weigh
 
 
 def brute_force(x: np.ndarray, w_r: np.ndarray, b: Optional[np.ndarray], k: int,
-                weights: Weights) -> np.ndarray:
+                weights: Weights,
+                shared: Optional[Tuple[np.ndarray, np.ndarray, np.ndarray]] = None) -> np.ndarray:
     """Per-token loop, every expert evaluated densely, no sort, no segment, no ring.
-    Only for tiny shapes."""
+    Only for tiny shapes.  shared: an always-on expert (W_gate, W_up, W_down) whose
+    output joins every token's sum with weight 1, outside the softmax."""
     T, _ = x.shape
     E = w_r.shape[0]
     y = np.zeros_like(x)
     for t in range(T):
+        if shared is not None:
+            sg, su, sd = shared
+            hs = []
+            for i in range(sg.shape[0]):
+                a_i = float(np.dot(sg[i], x[t]))
+                hs.append(a_i / (1.0 + np.exp(-a_i)) * float(np.dot(su[i], x[t])))
+            y[t] += sd @ np.array(hs)
         lt = [float(np.dot(w_r[e], x[t])) + (0.0 if b is None else float(b[e])) for e in range(E)]
         outs = []
         for e in range(E):

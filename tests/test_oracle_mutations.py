@@ -93,7 +93,20 @@ def check_autograd(mod):
         np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-10, atol=1e-12)
 
 
-MOE_CHECKS = [check_brute, check_dispatch, check_closed_forms, check_autograd]
+def check_mx_wiring(mod):
+    from test_oracle_pins import mx_golden_check, torch_mx_check
+    mx_golden_check(mod)
+    torch_mx_check(mod)
+
+
+def check_shared(mod):
+    from test_oracle_pins import shared_brute_check, shared_golden_check
+    shared_golden_check(mod)
+    shared_brute_check(mod)
+
+
+MOE_CHECKS = [check_brute, check_dispatch, check_closed_forms, check_autograd, check_mx_wiring,
+              check_shared]
 
 MOE_MUTATIONS = [
     ("silu sign", "H = A * sigmoid(A) * U", "H = A * sigmoid(-A) * U"),
@@ -111,6 +124,16 @@ MOE_MUTATIONS = [
     ("gate dropped in dW_down", "(g[:, None] * dy[ts]).T @ H", "dy[ts].T @ H"),
     ("W_down rows reversed in dgrad", "dHraw = dy[ts] @ wd", "dHraw = dy[ts] @ wd[::-1]"),
     ("router term missing in dx", "dx += dl[:, j, None] * w_r[routing.idx[:, j]]", "pass"),
+    ("H not quantised", "H = mx.fake_quant(H, axis=1)", "H = H"),
+    ("H quantised along rows", "H = mx.fake_quant(H, axis=1)", "H = mx.fake_quant(H, axis=0)"),
+    ("x not quantised in forward", "rows = mx.fake_quant(x, axis=1) if mx_path else x", "rows = x"),
+    ("x quantised along tokens in forward", "rows = mx.fake_quant(x, axis=1) if mx_path else x",
+     "rows = mx.fake_quant(x, axis=0) if mx_path else x"),
+    ("x not quantised in forward_tokens", "xq = mx.fake_quant(xs, axis=1) if mx_path else xs", "xq = xs"),
+    ("shared expert dropped in forward", "y = y + swiglu(x, *shared)", "y = y"),
+    ("shared expert gated in forward", "y = y + swiglu(x, *shared)", "y = y + r.gate[:, :1] * swiglu(x, *shared)"),
+    ("shared expert halved in forward_tokens", "y += swiglu(xs, *shared)", "y += 0.5 * swiglu(xs, *shared)"),
+    ("shared expert dropped in forward_tokens", "y += swiglu(xs, *shared)", "pass"),
 ]
 
 

@@ -408,3 +408,153 @@ def test_redraw_margin_and_zipf_skew():
     assert abs(t[0] / t.mean() - 8.0) < 1e-9 and abs(t.sum() - cfg.n) < 1e-6
     cnt = np.bincount(np.argsort(-l, axis=1)[:, :cfg.k].ravel(), minlength=cfg.E)
     assert 4.0 < cnt.max() / cnt.mean() < 12.0
+
+
+# ----------------------------------------------------------------- MX wiring and the shared expert
+
+
+def load_mx_shared():
+    with open(os.path.join(GOLDEN, "mx_shared_cases.json")) as fh:
+        return json.load(fh)
+
+
+def _vec(n, nonzero):
+    v = np.zeros(n)
+    for i, val in nonzero.items():
+        v[int(i)] = val
+    return v
+
+
+def _unit_rows(n_rows, n_cols, rows):
+    """A matrix whose row r is the unit vector e_c for every r -> c in `rows`, zero elsewhere."""
+    m = np.zeros((n_rows, n_cols))
+    for r, c in rows.items():
+        m[int(r), c] = 1.0
+    return m
+
+
+def mx_golden_check(mod):
+    """The hand-derived MX case: x quantised along d, H along f (tests/golden/mx_shared_cases.json)."""
+    for c in load_mx_shared()["mx_cases"]:
+        d, f = c["d"], c["f"]
+        x = _vec(d, c["x_nonzero"])[None, :]
+        w_r = _vec(d, c["w_router_nonzero"])[None, :]
+        wg = _unit_rows(f, d, c["w_gate_rows"])[None]
+        wu = _unit_rows(f, d, c["w_up_rows"])[None]
+        wd = _unit_rows(d, f, c["w_down_rows"])[None]
+        W = mod.weights_from_arrays(wg, wu, wd)
+        fw = mod.forward(x, w_r, None, c["k"], W, C=1, mx_path=True)
+        np.testing.assert_array_equal(fw.ring_x[0], _vec(d, c["ring_x_nonzero"]))
+        np.testing.assert_array_equal(fw.y[0], _vec(d, c["y_nonzero"]))
+        got = mod.forward_tokens([0], x, fw.routing, W, mx_path=True)
+        np.testing.assert_array_equal(got[0], _vec(d, c["y_nonzero"]))
+
+
+def shared_golden_check(mod):
+    """The hand-derived shared-expert case through forward and forward_tokens."""
+    data = load_mx_shared()
+    base = {b["name"]: b for b in load_cases()}
+    for c in data["shared_cases"]:
+        b = base[c["base_case"]]
+        x, w_r = np.array(b["x"]), np.array(b["w_router"])
+        W = mod.weights_from_arrays(np.array(b["w_gate"]), np.array(b["w_up"]), np.array(b["w_down"]))
+        sh = tuple(np.array(c[n]) for n in ("ws_gate", "ws_up", "ws_down"))
+        fw = mod.forward(x, w_r, None, b["k"], W, C=x.shape[0] * b["k"], shared=sh)
+        np.testing.assert_allclose(fw.y, c["y"], rtol=0, atol=1e-15)
+        got = mod.forward_tokens(range(x.shape[0]), x, fw.routing, W, shared=sh)
+        np.testing.assert_allclose(got, c["y"], rtol=0, atol=1e-15)
+
+
+def torch_mx_fake_quant(v, axis):
+    """An MX round trip built on torch's own E4M3 cast (round to nearest even inside
+    +-448), independent of oracle/mx.py: X = floor(log2 amax) - 8 per 32 elements from
+    torch.frexp, v 2^-X clamped to +-448, cast, and scaled back."""
+    t = torch.from_numpy(np.moveaxis(np.asarray(v, dtype=np.float64), axis, -1).copy())
+    blk = t.reshape(t.shape[:-1] + (t.shape[-1] // 32, 32))
+    amax = blk.abs().amax(dim=-1, keepdim=True)
+    _, e = torch.frexp(amax)
+    X = torch.where(amax > 0, e.to(torch.float64) - 1 - 8, torch.full_like(amax, -127.0)).clamp(-127, 127)
+    s = torch.clamp(blk * torch.exp2(-X), -448.0, 448.0)
+    q = s.to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64) * torch.exp2(X)
+    return np.moveaxis(q.reshape(t.shape).numpy(), -1, axis)
+
+
+def torch_mx_layer(x, w_r, b, k, wg, wu, wd):
+    """Dense per-token MX layer: y_t = sum_{e in S_t} g_e W_d[e] Q_f(silu(W_g[e] Q_d(x_t)) * W_u[e] Q_d(x_t)),
+    with Q the torch-cast MX round trip above, routing on the unquantised x."""
+    l = x @ w_r.T + (0 if b is None else b)
+    xq = torch_mx_fake_quant(x, axis=1)
+    y = np.zeros_like(x)
+    for t in range(x.shape[0]):
+        S = np.argsort(-l[t], kind="stable")[:k]
+        z = np.exp(l[t, S] - l[t, S].max())
+        g = z / z.sum()
+        for gi, e in zip(g, S):
+            a = wg[e] @ xq[t]
+            u = wu[e] @ xq[t]
+            h = torch.nn.functional.silu(torch.from_numpy(a)).numpy() * u
+            y[t] += gi * (wd[e] @ torch_mx_fake_quant(h[None, :], axis=1)[0])
+    return y
+
+
+def torch_mx_check(mod):
+    """The MX layer of the oracle against the torch-cast formulation: a few experts with
+    ragged loads, and one expert of 64 rows (so that a block along the wrong axis exists)."""
+    for seed, (T, d, E, k, f) in ((14, (12, 64, 4, 2, 96)), (15, (64, 64, 1, 1, 64))):
+        rng = np.random.default_rng(seed)
+        x, w_r, b, wg, wu, wd = rand_layer(rng, T, d, E, k, f, bias=E > 1)
+        wg, wu = torch_mx_fake_quant(wg, axis=2), torch_mx_fake_quant(wu, axis=2)
+        wd = torch_mx_fake_quant(wd, axis=2)
+        W = mod.weights_from_arrays(wg, wu, wd)
+        ref = torch_mx_layer(x, w_r, b, k, wg, wu, wd)
+        fw = mod.forward(x, w_r, b, k, W, C=T * k + 3, head=2, mx_path=True)
+        np.testing.assert_allclose(fw.y, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+        got = mod.forward_tokens(range(T), x, fw.routing, W, mx_path=True)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+def shared_brute_check(mod):
+    """forward / forward_tokens with a shared expert against the per-token brute force."""
+    rng = np.random.default_rng(16)
+    T, d, E, k, f = 9, 16, 5, 2, 12
+    x, w_r, b, wg, wu, wd = rand_layer(rng, T, d, E, k, f, bias=True)
+    sh = (rng.standard_normal((f, d)) / 4, rng.standard_normal((f, d)) / 4, rng.standard_normal((d, f)) / 3)
+    W = mod.weights_from_arrays(wg, wu, wd)
+    bf = oracle.brute_force(x, w_r, b, k, oracle.weights_from_arrays(wg, wu, wd), shared=sh)
+    fw = mod.forward(x, w_r, b, k, W, C=T * k, shared=sh)
+    np.testing.assert_allclose(fw.y, bf, rtol=0, atol=1e-12 * np.abs(bf).max())
+    got = mod.forward_tokens(range(T), x, fw.routing, W, shared=sh)
+    np.testing.assert_allclose(got, bf, rtol=0, atol=1e-12 * np.abs(bf).max())
+
+
+def test_mx_golden_case():
+    mx_golden_check(oracle.moe)
+    c = load_mx_shared()["mx_cases"][0]
+    codes, scales = mx.quantize(_vec(c["d"], c["x_nonzero"])[None, :], axis=1)
+    assert scales.tolist() == [[c["x_scale_byte"]]]
+    np.testing.assert_array_equal(codes[0], _vec(c["d"], {i: int(h, 16) for i, h in c["x_codes_nonzero"].items()}))
+    h = np.zeros(c["f"])
+    h[0] = 1.125 / (1 + math.exp(-1.125)) * 1.25
+    h[1] = 9.0 / (1 + math.exp(-3.0))
+    codes, scales = mx.quantize(h[None, :], axis=1)
+    assert scales.tolist() == [[c["h_scale_byte"]]]
+    np.testing.assert_array_equal(codes[0], _vec(c["f"], {i: int(v, 16) for i, v in c["h_codes_nonzero"].items()}))
+
+
+def test_shared_expert_golden_case():
+    shared_golden_check(oracle.moe)
+
+
+def test_shared_expert_against_brute_force():
+    shared_brute_check(oracle.moe)
+    # the brute force's own shared term against a closed form: one token, E = 1
+    x = np.array([[1.0, 0.0]])
+    y = oracle.brute_force(x, np.array([[1.0, 0.0]]), None, 1,
+                           oracle.weights_from_arrays(np.zeros((1, 1, 2)), np.zeros((1, 1, 2)), np.zeros((1, 2, 1))),
+                           shared=(np.array([[2.0, 0.0]]), np.array([[0.5, 0.0]]), np.array([[1.0], [-2.0]])))
+    s2 = 1.0 / (1.0 + math.exp(-2.0))
+    np.testing.assert_allclose(y, [[s2, -2 * s2]], rtol=0, atol=1e-15)
+
+
+def test_mx_layer_against_torch_float8():
+    torch_mx_check(oracle.moe)
