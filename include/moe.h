@@ -63,7 +63,8 @@ extern "C" {
 enum moe_status {
   MOE_OK = 0,
   MOE_ERR_NULL = 1,       /* a required pointer is NULL */
-  MOE_ERR_SHAPE = 2,      /* non-positive size, k > E, MX length not a multiple of 32, ... */
+  MOE_ERR_SHAPE = 2,      /* non-positive size, k > E, a length outside the kernels'
+                             domain (see each call), a ring array of 4 GiB or more, ... */
   MOE_ERR_CAPACITY = 3,   /* ring capacity below tokens * top_k: tokens would be dropped */
   MOE_ERR_WORKSPACE = 4,  /* workspace smaller than moe_workspace_bytes() */
   MOE_ERR_HIP = 5,        /* a HIP launch or runtime call failed */
@@ -217,6 +218,11 @@ int moe_backward(const moe_shape* shape, const void* dy, const void* x,
                  const void* w_gate, const void* w_up, const void* w_down,
                  void* dx, void* dw_gate, void* dw_up, void* dw_down, float* dw_router,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Validation of `shape` alone, as every call performs it first (MOE_OK or the status
+ * a call would return; includes: every ring array the MFMA GEMMs address, C * d and
+ * C * f elements of bf16 or E4M3, must stay below 4 GiB).  Host only, no GPU call. */
+int moe_check_shape(const moe_shape* shape);
 
 /* Bytes of workspace `op` needs for `shape` (0 if none).  Host only, no GPU call. */
 size_t moe_workspace_bytes(const moe_shape* shape, int op);

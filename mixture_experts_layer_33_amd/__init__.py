@@ -16,7 +16,7 @@ import torch
 from ._lib import (DTYPES, MOE_BF16, MOE_F32, MOE_MXFP8, OP_BACKWARD, OP_COMBINE, OP_DECODE,
                    OP_DISPATCH, OP_EXPERT_FFN, OP_ROUTE, LIB_PATH, MoeError, MoeShape, check, lib)
 
-__all__ = ["make_shape", "workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn",
+__all__ = ["make_shape", "check_shape", "workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn",
            "moe_expert_ffn_timed",
            "moe_combine", "moe_decode", "moe_backward", "moe_quantize_mx", "Layer", "MoeError",
            "LIB_PATH"]
@@ -44,6 +44,11 @@ def _p(t: Optional[torch.Tensor]):
 def _s(stream) -> int:
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
+
+
+def check_shape(shape: MoeShape) -> None:
+    """Raise MoeError if the library would reject `shape` (host-side validation only)."""
+    check("moe_check_shape", lib().moe_check_shape(shape))
 
 
 def workspace_bytes(shape: MoeShape, op: int) -> int:
@@ -253,6 +258,7 @@ class RingStack:
             raise ValueError(f"ring of {C} rows cannot hold {L} layers of {n} copies")
         self.L, self.n = L, n
         self.shape = make_shape(T, d, E, k, f, C)
+        check_shape(self.shape)   # e.g. a ring of 4 GiB or more per array is rejected
         self.device = torch.device(device)
         dev = self.device
         z = lambda *s, dtype=torch.int32: torch.zeros(s, dtype=dtype, device=dev)

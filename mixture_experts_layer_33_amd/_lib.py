@@ -36,6 +36,7 @@ SIGNATURES = {
     "moe_decode": [SHP, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_backward": [SHP, P, P, P, P, P, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_workspace_bytes": [SHP, C.c_int],
+    "moe_check_shape": [SHP],
     "moe_status_string": [C.c_int],
     "moe_quantize_mx": [P, I64, I64, P, P, P],
 }

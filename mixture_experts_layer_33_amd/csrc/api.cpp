@@ -49,6 +49,14 @@ int check_shape(const moe_shape* s) {
   if (s->hidden % q || s->ffn % q) return MOE_ERR_SHAPE;
   if (s->capacity < s->tokens * s->top_k) return MOE_ERR_CAPACITY;
   if (s->capacity > ((int64_t)1 << 31) - 1) return MOE_ERR_SHAPE;
+  // The MFMA grouped GEMM addresses its ring-ordered operand rows (ring_x [C, d] in
+  // GEMM-1, H [C, f] in GEMM-2) with 32-bit byte offsets from the array's start:
+  // each of those arrays must stay below 4 GiB.
+  if (s->dtype != MOE_F32) {
+    const int64_t eb = s->dtype == MOE_BF16 ? 2 : 1;
+    const int64_t row = (s->hidden > s->ffn ? s->hidden : s->ffn) * eb;
+    if (s->capacity * row >= ((int64_t)1 << 32)) return MOE_ERR_SHAPE;
+  }
   return MOE_OK;
 }
 
@@ -76,6 +84,8 @@ size_t moe_workspace_bytes(const moe_shape* s, int op) {
     default: return 0;
   }
 }
+
+int moe_check_shape(const moe_shape* s) { return check_shape(s); }
 
 const char* moe_status_string(int st) {
   switch (st) {

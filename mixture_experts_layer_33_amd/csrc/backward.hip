@@ -648,14 +648,10 @@ constexpr int WG_NJ = 4, WG_WS = 2, WG_OCC = 3;
 static hipError_t run_wgrad(const WgradArgs& a, hipStream_t st) {
   auto kern = wgrad_kernel<WG_NJ, WG_WS, WG_OCC>;
   constexpr int lds = WG_WS * WgShape<WG_NJ>::STAGE;
-  if (lds > 65536) {
-    static bool attr_set = false;   // opt in to more than 64 KB of LDS once per process
-    if (!attr_set) {
-      hipError_t err = hipFuncSetAttribute((const void*)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      if (err != hipSuccess) return err;
-      attr_set = true;
-    }
+  if (lds > 65536) {   // opt in to more than 64 KB of LDS (a host-side call, on every launch)
+    hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
   }
   const int64_t P = (int64_t)((a.M + WM_ - 1) / WM_) * ((a.N + WgShape<WG_NJ>::WN - 1) / WgShape<WG_NJ>::WN);
   kern<<<(unsigned)(8 * ((P + 7) / 8) * a.E), 256, lds, st>>>(a);   // 8 XCDs x the largest chunk
@@ -688,15 +684,13 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
   zero_fill_kernel<<<1, 256, 0, st>>>((uint32_t*)(w + L.zero), 256);
   bf16_t* rdy = (bf16_t*)(w + L.rdy);
   gather_to_ring_kernel<<<(unsigned)T, 256, 0, st>>>((const bf16_t*)dy, copy_slot, k, d, rdy);
-  static bool lds_opt_in = false;   // the 64 KB stage ring plus the static reduction buffer
-  if (!lds_opt_in) {
-    if ((err = hipFuncSetAttribute((const void*)dgrad_kernel<true>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, DG_LDS)) != hipSuccess ||
-        (err = hipFuncSetAttribute((const void*)dgrad_kernel<false>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, DG_LDS)) != hipSuccess)
-      return err;
-    lds_opt_in = true;
-  }
+  // dynamic LDS of the dgrad kernels: the stage ring (or the epilogue staging), asked for
+  // on every call (a host-side attribute, no state kept here)
+  if ((err = hipFuncSetAttribute((const void*)dgrad_kernel<true>,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, DG_LDS)) != hipSuccess ||
+      (err = hipFuncSetAttribute((const void*)dgrad_kernel<false>,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, DG_LDS)) != hipSuccess)
+    return err;
   DgradArgs a{};
   a.A = rdy;
   a.B0 = (const bf16_t*)w_down;

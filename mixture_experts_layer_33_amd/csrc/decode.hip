@@ -397,14 +397,11 @@ hipError_t launch_decode(const void* x, const float* w_r, const float* b_r, cons
   if (err != hipSuccess) return err;
   err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
-  static bool lds_opt_in[17] = {};   // per d / 512: the largest LDS any call may need
-  if (!lds_opt_in[d / 512]) {
-    err = hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)((size_t)DEC_BMAX * d * 2 + (2 * DEC_BMAX * DEC_KMAX + 1) * 4 +
-                                    (1024 / 32) * 4));
-    if (err != hipSuccess) return err;
-    lds_opt_in[d / 512] = true;
-  }
+  // the largest LDS any call of this d may need, asked for on every call (host side only)
+  err = hipFuncSetAttribute(k1, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)((size_t)DEC_BMAX * d * 2 + (2 * DEC_BMAX * DEC_KMAX + 1) * 4 +
+                                  (1024 / 32) * 4));
+  if (err != hipSuccess) return err;
   err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k1, DEC_THREADS, lds);
   if (err != hipSuccess) return err;
   if (per_cu < 1) return hipErrorInvalidConfiguration;

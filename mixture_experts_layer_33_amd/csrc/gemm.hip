@@ -573,13 +573,11 @@ static hipError_t run_mfma(const GemmArgs& a, int max_tiles, hipStream_t st) {
   const size_t lds = std::max<size_t>((size_t)S * StageLayout<BM, BN, KB, MX, WM * WN>::SIZE,
                                       EpiLayout<BM, BN, SWIGLU, MX>::SIZE);
   auto kern = gg_mfma_kernel<BM, BN, WM, WN, KB, SWIGLU, MX, S, POL>;
-  static bool attr_set = false;   // opt in to more than 64 KB of LDS once per process
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute((const void*)kern,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  // opt in to more than 64 KB of LDS: a host-side attribute, set on every launch so that
+  // nothing is kept between calls
+  hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
   const int64_t vmax = (int64_t)max_tiles * nt;          // bound on live tiles
   const int64_t grid = 8 * ((vmax + 7) / 8);
   kern<<<(unsigned)grid, WM * WN * 64, lds, st>>>(a);

@@ -412,13 +412,9 @@ hipError_t launch_route(const void* x, bool x_f32, const float* w_r, const float
     router_split_kernel<<<(unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096), 256, 0, st>>>(w_r, n, w3);
     ks = router_ksplit(T, E, d);
     if (router_big(E)) {
-      static bool attr = false;
-      if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)router_mfma2_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, R2_LDS);
-        if (e != hipSuccess) return e;
-        attr = true;
-      }
+      hipError_t e = hipFuncSetAttribute((const void*)router_mfma2_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, R2_LDS);
+      if (e != hipSuccess) return e;
       router_mfma2_kernel<<<dim3((unsigned)((E + 127) / 128), (unsigned)((T + 127) / 128), (unsigned)ks),
                             R2_NT, R2_LDS, st>>>((const bf16_t*)x, w3, logits, T, d, E);
     } else {

@@ -139,3 +139,26 @@ def test_ring_stack_capacity():
     st = moe.RingStack(3, T=16, d=128, E=8, k=2, f=256, device="cpu")
     assert st.shape.capacity == 3 * 40 and st.n == 32
     assert tuple(st.ring_x.shape) == (120, 128) and tuple(st.saved_au.shape) == (120, 512)
+
+
+def test_rings_of_4_gib_are_rejected():
+    """The grouped GEMM addresses ring_x [C, d] and H [C, f] with 32-bit byte offsets:
+    a shape whose ring array reaches 4 GiB is rejected on the host, before any launch."""
+    L = _lib.lib()
+    d, f = 7168, 2048
+    c_max = ((1 << 32) - 1) // (d * 2)            # the largest bf16 ring below 4 GiB
+    ok = moe.make_shape(2048, d, 256, 8, f, C=c_max)
+    bad = moe.make_shape(2048, d, 256, 8, f, C=c_max + 1)
+    assert L.moe_check_shape(ok) == _lib.MOE_OK
+    assert L.moe_check_shape(bad) == _lib.MOE_ERR_SHAPE
+    assert route(bad) == _lib.MOE_ERR_SHAPE
+    assert L.moe_expert_ffn(bad, FAKE, None, FAKE, 0, FAKE, FAKE, FAKE, None, None, None, FAKE, None,
+                            FAKE, 1 << 40, None) == _lib.MOE_ERR_SHAPE
+    # H decides when f > d; MX rows are one byte per element
+    assert L.moe_check_shape(moe.make_shape(64, 256, 8, 2, 8192, C=(1 << 32) // (8192 * 2))) == _lib.MOE_ERR_SHAPE
+    assert L.moe_check_shape(moe.make_shape(64, 7168, 8, 2, 2048, C=c_max + 1, dtype="mxfp8")) == _lib.MOE_OK
+    assert L.moe_check_shape(moe.make_shape(64, 7168, 8, 2, 2048, C=-(-(1 << 32) // 7168),
+                                            dtype="mxfp8")) == _lib.MOE_ERR_SHAPE
+    # a ring stack of six skewed layers (d 4096, 102,400 rows each) would need 5 GB per array
+    with pytest.raises(moe.MoeError):
+        moe.RingStack(6, T=8192, d=4096, E=512, k=10, f=1024, device="cpu")
