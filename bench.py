@@ -31,6 +31,14 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+# Host threads of the oracle baseline: the CPUs this process may run on, capped by the
+# OpenMP thread count the machine sets for a process's share.  The BLAS pools read these
+# variables when numpy is first imported, so they are pinned here, before any import.
+AFFINITY_CPUS = len(os.sched_getaffinity(0))
+CPU_THREADS = min(AFFINITY_CPUS, int(os.environ.get("OMP_NUM_THREADS") or AFFINITY_CPUS))
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ[_v] = str(CPU_THREADS)
+
 METRIC = "MoE-layer tokens/s at 2048 tok; decode µs/token; % of MFMA/HBM peak"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFS = 2516.6
@@ -44,7 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0,
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle expert work in the CPU baseline sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (reference for counter scaling)")
@@ -80,24 +88,39 @@ def fwd_step_timed(layer, inp, events):
                   events=events)
 
 
+REPEAT_BUFFERS = ("topk_idx", "topk_gate", "expert_count", "expert_offset", "copy_slot", "slot_copy",
+                  "ring_x", "ring_y", "y")
+
+
 def measure_forward(torch, moe, inp, cfg, steps, warmup, scales=(None, None, None), wq=None):
-    """Time `steps` forwards; returns (ms/step, avg GEMM-1 ms, avg GEMM-2 ms, layer)."""
+    """Time `steps` forwards back to back; returns (ms/step, avg GEMM-1 ms, avg GEMM-2 ms,
+    layer, spread) with spread = per-step median / min / p90 (from an event at every step
+    boundary) and whether every output and ring buffer of the last timed step is bitwise
+    equal to the first warm-up step's."""
     layer = moe.Layer.create(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.C, dtype=cfg.dtype)
     wg, wu, wd = wq if wq is not None else (inp.w_gate, inp.w_up, inp.w_down)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for _ in range(warmup):
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    first = None
+    for i in range(max(1, warmup)):
         layer.forward(inp.x, inp.w_router, inp.b_router, wg, wu, wd, scales=scales)
+        if i == 0:
+            first = {n: layer.bufs[n].clone() for n in REPEAT_BUFFERS if n in layer.bufs}
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
+    marks[0].record()
     for i in range(steps):
         layer.forward(inp.x, inp.w_router, inp.b_router, wg, wu, wd, scales=scales, events=evs[i])
-    end.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    ms = marks[0].elapsed_time(marks[steps]) / steps
+    per = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
     g1 = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
     g2 = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
-    return ms, g1, g2, layer
+    same = all(torch.equal(first[n].view(torch.uint8), layer.bufs[n].view(torch.uint8)) for n in first)
+    spread = {"step_ms_median": round(per[len(per) // 2], 4), "step_ms_min": round(per[0], 4),
+              "step_ms_p90": round(per[int(0.9 * (len(per) - 1))], 4),
+              "repeat_bitwise_equal": bool(same), "repeat_buffers": sorted(first)}
+    return ms, g1, g2, layer, spread
 
 
 def expert_bytes(counts, d, f, elem_bytes, scale_bytes_per_elem=0.0):
@@ -108,18 +131,22 @@ def expert_bytes(counts, d, f, elem_bytes, scale_bytes_per_elem=0.0):
 
 def cpu_baseline(inp, cfg, budget_s):
     """The oracle on the host over the whole layer: router, dispatch, ring fill, the expert
-    FFN of every expert (ascending id) and combine.  When one pass is short, each step is
-    repeated `reps` times so that about `budget_s` seconds of oracle work are timed; when it
-    is long, experts are sampled in ascending id until the budget and the expert time is
-    extrapolated by the sampled share of token copies."""
+    FFN of every expert (ascending id) and combine.  Each step is repeated `reps` times so
+    that about `budget_s` seconds of oracle work are timed, reps sized from an untimed
+    warm-up and a timed probe of the first expert; an expert's weights are widened to
+    fp64 once, outside the timed regions.  If one layer alone would exceed the budget, its
+    experts are sampled in ascending id until the budget and the expert time is
+    extrapolated by the sampled share of token copies.  BLAS runs on CPU_THREADS threads,
+    pinned before numpy was imported."""
     import numpy as np
     import oracle
     from gen import bits16
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threadpool_limits(CPU_THREADS)
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
-        threads = 1
+        threads = CPU_THREADS
     x = oracle.from_bf16_bits(bits16(inp.x))
     w_r = oracle.from_f32(inp.w_router.cpu().numpy())
     t0 = time.perf_counter()
@@ -135,11 +162,12 @@ def cpu_baseline(inp, cfg, budget_s):
             continue
         w = tuple(oracle.from_bf16_bits(bits16(t[e])) for t in (inp.w_gate, inp.w_up, inp.w_down))
         if reps is None:   # size the repetition count from the first expert's cost
+            oracle.swiglu(ring[slots], *w)                       # warm-up: thread pools, caches
             t1 = time.perf_counter()
             oracle.swiglu(ring[slots], *w)
-            probe = (time.perf_counter() - t1) * cfg.n / slots.size + t_fixed1
-            reps = int(max(1, min(20, budget_s // max(probe, 1e-9))))
-        if sampled % 8 == 0:
+            probe = (time.perf_counter() - t1) * cfg.n / slots.size + 2 * t_fixed1
+            reps = int(max(1, min(50, math.ceil(budget_s / max(probe, 1e-9)))))
+        if sampled % 32 == 0:
             progress(f"oracle expert {e}: {t_exp:.1f} s of expert work so far ({reps} reps)")
         t1 = time.perf_counter()
         for _ in range(reps):
@@ -147,7 +175,7 @@ def cpu_baseline(inp, cfg, budget_s):
         t_exp += time.perf_counter() - t1
         rows += slots.size
         sampled += 1
-        if t_exp >= budget_s:
+        if t_exp >= budget_s and rows < cfg.n:
             break
     reps = reps or 1
     t2 = time.perf_counter()
@@ -159,11 +187,12 @@ def cpu_baseline(inp, cfg, budget_s):
         oracle.combine(ring_y, disp.copy_slot, r.gate)
     t_fixed = t_fixed1 + time.perf_counter() - t2
     est = t_fixed + t_exp * (cfg.n / rows)
-    return {"value": round(reps * cfg.T / est, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"fp64 numpy oracle, {reps} repetition(s) of each step: router, dispatch, "
-                       f"ring fill and combine over all {cfg.T} tokens ({t_fixed:.2f} s); expert "
-                       f"SwiGLU on {sampled} of {cfg.E} experts ({rows} of {cfg.n} copies, "
-                       f"{t_exp:.2f} s); {reps} full layer(s) "
+    return {"value": round(reps * cfg.T / est, 3), "unit": "tokens/s", "cores": threads,
+            "affinity_cpus": AFFINITY_CPUS, "kind": "oracle",
+            "sample": (f"fp64 numpy oracle on {threads} BLAS threads, {reps} repetition(s) of each "
+                       f"step: router, dispatch, ring fill and combine over all {cfg.T} tokens "
+                       f"({t_fixed:.2f} s); expert SwiGLU on {sampled} of {cfg.E} experts ({rows} of "
+                       f"{cfg.n} copies, {t_exp:.2f} s); {reps} full layer(s) "
                        + ("timed" if rows == cfg.n else "extrapolated by the copy share")
                        + f" in {est:.1f} s")}
 
@@ -349,10 +378,23 @@ def secondary(torch, moe, steps):
     progress(f"forward {cfg.name}")
     inp = make_layer(cfg, "cuda")
     q = [moe.quantize_mx(w) for w in (inp.w_gate, inp.w_up, inp.w_down)]
-    ms, g1, g2, layer = measure_forward(torch, moe, inp, cfg, steps, 3,
-                                        scales=tuple(s for _, s in q), wq=tuple(c for c, _ in q))
+    ms, g1, g2, layer, spread = measure_forward(torch, moe, inp, cfg, steps, 3,
+                                                scales=tuple(s for _, s in q), wq=tuple(c for c, _ in q))
+    # algorithmic bytes: E4M3 codes plus one E8M0 byte per 32 of every MX operand read once
+    counts = layer.bufs["expert_count"].cpu().numpy()
+    used = int((counts > 0).sum())
+    n, d, f = cfg.n, cfg.d, cfg.f
+    mxb = 1 + 1 / 32
+    alg1 = used * 2 * f * d * mxb + n * d * mxb + n * f * mxb       # weights + ring rows + H
+    alg2 = used * d * f * mxb + n * f * mxb + n * d * 2              # weights + H + ring_y bf16
     out["fwd_mxfp8_t2048"] = {"tokens_per_s": round(cfg.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
-                              "gemm1_ms": round(g1, 4), "gemm2_ms": round(g2, 4)}
+                              "gemm1_ms": round(g1, 4), "gemm2_ms": round(g2, 4),
+                              "gemm1_alg_bytes": alg1, "gemm2_alg_bytes": alg2,
+                              "gemm1_hbm_frac": round(alg1 / (g1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "gemm2_hbm_frac": round(alg2 / (g2 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "gemm_hbm_frac": round((alg1 + alg2) / ((g1 + g2) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "gemm_fp8_mfma_frac": round(2.0 * n * d * 3 * f / ((g1 + g2) * 1e-3) / 1e12 / FP8_PEAK_TFS, 4),
+                              **spread}
     return out
 
 
@@ -379,7 +421,7 @@ def main():
     torch.cuda.synchronize()
     progress(f"timing {args.steps} steps after {args.warmup} warm-up steps")
     t0 = time.perf_counter()
-    ms, g1, g2, layer = measure_forward(torch, moe, inp, cfg, args.steps, args.warmup)
+    ms, g1, g2, layer, spread = measure_forward(torch, moe, inp, cfg, args.steps, args.warmup)
     wall = time.perf_counter() - t0
     counts = layer.bufs["expert_count"].cpu().numpy()
     used, w_gu, w_d = expert_bytes(counts, cfg.d, cfg.f, 2)
@@ -420,6 +462,7 @@ def main():
                     "layer_hbm_frac": round((alg1 + alg2) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "timed_wall_s": round(wall, 3),
     }
+    result.update(spread)
     progress(f"forward {ms:.3f} ms/step, gate/up GEMM {g1:.3f} ms, down GEMM {g2:.3f} ms")
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
