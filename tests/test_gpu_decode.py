@@ -55,3 +55,33 @@ def test_decode_full_size(B):
     print(f"\n[case] decode full size B={B}", flush=True)
     check_decode(DECODE(B), reps=3)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cfg", [
+    LayerConfig("dec_vs_prefill_b8", T=8, d=2048, E=64, k=8, f=1024, fs=0, cid=77),
+    DECODE(8).with_(name="decode_b8_routed_only", fs=0),
+], ids=lambda c: c.name)
+def test_decode_error_vs_prefill_path(cfg):
+    """The warp-decode page reports decode output closer to the fp32 reference than the
+    expert-centric path.  On the same tokens and weights (routed experts only), the
+    decode's y (h kept in fp32, one rounding at the end) against the forward path's y (H
+    and ring_y rounded to bf16), both measured against the fp64 oracle."""
+    print(f"\n[case] decode vs prefill error {cfg.name}", flush=True)
+    inp = make_layer(cfg, DEV)
+    dec = moe.Layer.create(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, fs=0, dtype="bf16")
+    y_dec, idx, _ = dec.decode(inp.x, inp.w_router, inp.b_router, inp.w_gate, inp.w_up, inp.w_down)
+    pre = moe.Layer.create(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.C, dtype="bf16")
+    y_pre = pre.forward(inp.x, inp.w_router, inp.b_router, inp.w_gate, inp.w_up, inp.w_down)
+    torch.cuda.synchronize()
+    x = to_oracle(inp.x)
+    r = oracle.route(x, to_oracle(inp.w_router), None, cfg.k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), r.idx)
+    np.testing.assert_array_equal(pre.bufs["topk_idx"].cpu().numpy(), r.idx)
+    ref = oracle.forward_tokens(range(cfg.T), x, r, LazyWeights(inp.w_gate, inp.w_up, inp.w_down))
+    e_dec, e_pre = rel(to_oracle(y_dec), ref), rel(to_oracle(y_pre), ref)
+    print(f"  max-abs-rel to the fp64 oracle: decode {e_dec:.3e}, forward path {e_pre:.3e} "
+          f"(ratio {e_dec / e_pre:.2f})", flush=True)
+    assert e_dec <= 2e-2 and e_pre <= 2e-2
+    assert e_dec <= e_pre
+    del inp, dec, pre
+    torch.cuda.empty_cache()

@@ -51,6 +51,15 @@ MEDIUM = [
     # MX with at least 256 rows per expert: the 256 x 256 eight-wave tile; ragged rows, the
     # down GEMM's second column tile half full
     LayerConfig("med_mx_big256", T=1400, d=384, E=4, k=2, f=384, dtype="mxfp8", cid=44),
+    # the method's degenerate cases: k = 1 (one expert per token, every gate 1), k = E
+    # (every expert selected, gates = the full softmax) and E = 1 (a dense SwiGLU FFN)
+    LayerConfig("med_bf16_k1", T=257, d=256, E=16, k=1, f=128, cid=70),
+    LayerConfig("med_bf16_kE", T=130, d=256, E=6, k=6, f=192, cid=71),
+    LayerConfig("med_bf16_e1", T=190, d=320, E=1, k=1, f=128, cid=72),
+    LayerConfig("med_mx_k1", T=257, d=256, E=16, k=1, f=128, dtype="mxfp8", cid=73),
+    LayerConfig("med_mx_kE", T=100, d=256, E=5, k=5, f=256, dtype="mxfp8", cid=74),
+    LayerConfig("med_mx_e1", T=150, d=384, E=1, k=1, f=256, dtype="mxfp8", cid=75),
+    LayerConfig("med_f32_kE", T=40, d=64, E=4, k=4, f=32, dtype="f32", cid=76),
 ]
 
 
