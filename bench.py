@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle expert work in the CPU baseline sample")
+    ap.add_argument("--only", choices=["decode", "share", "skew", "skew-no-stack", "mxfp8"], default=None,
+                    help="run one secondary workload alone (e.g. under a profiler) and print its JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (reference for counter scaling)")
     return ap.parse_args()
@@ -197,7 +199,7 @@ def cpu_baseline(inp, cfg, budget_s):
                        + f" in {est:.1f} s")}
 
 
-def skew_fwd_bwd(torch, moe, steps):
+def skew_fwd_bwd(torch, moe, steps, stack=True):
     """Forward (saving A|U) and backward of the skewed workload, timed separately.
     Algorithmic bytes: forward = used experts' three matrices + W_r (fp32) + x read twice
     (router, dispatch) + ring written and read + H written and read + saved A|U written +
@@ -246,7 +248,7 @@ def skew_fwd_bwd(torch, moe, steps):
             "bwd_mfma_frac": round(bwd_flops / (bm * 1e-3) / 1e12 / BF16_PEAK_TFS, 4),
             "experts_used": used, "max_load": int(counts.max()), "mean_load": round(float(n / E), 2),
             "max_over_mean": round(float(counts.max() / (n / E)), 2),
-            "ring_stack": ring_stack(torch, moe, inp, layer, steps, fm, bm)}
+            **({"ring_stack": ring_stack(torch, moe, inp, layer, steps, fm, bm)} if stack else {})}
 
 
 def ring_stack(torch, moe, inp, layer, steps, fwd_ms_1, bwd_ms_1, L=4):
@@ -286,11 +288,10 @@ def ring_stack(torch, moe, inp, layer, steps, fwd_ms_1, bwd_ms_1, L=4):
     return out
 
 
-def secondary(torch, moe, steps):
+def part_decode(torch, moe, steps):
+    """Small-batch decode, output-parallel, B = 1, 4, 8."""
     import numpy as np
-    from gen import DECODE, FWD_MXFP8, SHARE_BF16, SHARE_MXFP8, make_layer, make_share
-    out = {}
-    # ---- small-batch decode: two kernels, output-parallel
+    from gen import DECODE, make_layer
     dec, prev = {}, None
     for B in (1, 4, 8):
         cfg = DECODE(B)
@@ -334,10 +335,16 @@ def secondary(torch, moe, steps):
                         "unique_experts": U, "alg_bytes": nbytes,
                         "GBps": round(nbytes / us / 1e3, 1),
                         "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
-    out["decode"] = dec
     del prev, inp, layer
     torch.cuda.empty_cache()
-    # ---- one GPU's expert-parallel share: grouped GEMMs alone, MFMA-bound
+    return dec
+
+
+def part_share(torch, moe, steps):
+    """One GPU's expert-parallel share: the grouped GEMMs alone, MFMA-bound."""
+    import numpy as np
+    from gen import SHARE_BF16, SHARE_MXFP8, make_share
+    out = {}
     for scfg, peak in ((SHARE_BF16, BF16_PEAK_TFS), (SHARE_MXFP8, FP8_PEAK_TFS)):
         progress(f"expert-parallel share {scfg.name}")
         sh = make_share(scfg, "cuda")
@@ -370,10 +377,12 @@ def secondary(torch, moe, steps):
                           "gemm2_mfma_frac": round(f2 / g2 / 1e9 / peak, 4)}
         del sh, ws, ring_y, xq, xs, wargs
         torch.cuda.empty_cache()
-    # ---- skewed forward + backward: 8,192 tokens, d 4096, E 512, k 10, f 1024
-    out["skew_fwd_bwd_t8192"] = skew_fwd_bwd(torch, moe, steps)
-    torch.cuda.empty_cache()
-    # ---- MXFP8 forward at the same 2,048-token shape
+    return out
+
+
+def part_mxfp8(torch, moe, steps):
+    """The MXFP8 forward at the 2,048-token shape."""
+    from gen import FWD_MXFP8, make_layer
     cfg = FWD_MXFP8
     progress(f"forward {cfg.name}")
     inp = make_layer(cfg, "cuda")
@@ -387,7 +396,7 @@ def secondary(torch, moe, steps):
     mxb = 1 + 1 / 32
     alg1 = used * 2 * f * d * mxb + n * d * mxb + n * f * mxb       # weights + ring rows + H
     alg2 = used * d * f * mxb + n * f * mxb + n * d * 2              # weights + H + ring_y bf16
-    out["fwd_mxfp8_t2048"] = {"tokens_per_s": round(cfg.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+    return {"tokens_per_s": round(cfg.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
                               "gemm1_ms": round(g1, 4), "gemm2_ms": round(g2, 4),
                               "gemm1_alg_bytes": alg1, "gemm2_alg_bytes": alg2,
                               "gemm1_hbm_frac": round(alg1 / (g1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -395,7 +404,25 @@ def secondary(torch, moe, steps):
                               "gemm_hbm_frac": round((alg1 + alg2) / ((g1 + g2) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                               "gemm_fp8_mfma_frac": round(2.0 * n * d * 3 * f / ((g1 + g2) * 1e-3) / 1e12 / FP8_PEAK_TFS, 4),
                               **spread}
+
+
+def secondary(torch, moe, steps):
+    out = {"decode": part_decode(torch, moe, steps)}
+    out.update(part_share(torch, moe, steps))
+    out["skew_fwd_bwd_t8192"] = skew_fwd_bwd(torch, moe, steps)
+    torch.cuda.empty_cache()
+    out["fwd_mxfp8_t2048"] = part_mxfp8(torch, moe, steps)
     return out
+
+
+def calibrate_copy(torch, args):
+    """A plain 1 GiB device-to-device copy: the reference for scaling the HBM counters."""
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
 
 def main():
@@ -415,6 +442,19 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.only:
+        calibrate_copy(torch, args)
+        steps = max(2, args.steps)
+        if args.only == "decode":
+            res = part_decode(torch, moe, steps)
+        elif args.only == "share":
+            res = part_share(torch, moe, steps)
+        elif args.only in ("skew", "skew-no-stack"):
+            res = skew_fwd_bwd(torch, moe, steps, stack=args.only == "skew")
+        else:
+            res = part_mxfp8(torch, moe, steps)
+        print(json.dumps({"only": args.only, "steps": steps, **res}), flush=True)
+        return
     cfg = FWD_BF16
     progress(f"drawing inputs of {cfg.name}")
     inp = make_layer(cfg, "cuda")
@@ -464,12 +504,7 @@ def main():
     }
     result.update(spread)
     progress(f"forward {ms:.3f} ms/step, gate/up GEMM {g1:.3f} ms, down GEMM {g2:.3f} ms")
-    if args.calibrate_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calibrate_copy(torch, args)
     if not args.no_secondary:
         result["secondary"] = secondary(torch, moe, max(5, args.steps // 2))
     if not args.no_cpu_baseline:
