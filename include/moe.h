@@ -68,7 +68,8 @@ enum moe_status {
   MOE_ERR_CAPACITY = 3,   /* ring capacity below tokens * top_k: tokens would be dropped */
   MOE_ERR_WORKSPACE = 4,  /* workspace smaller than moe_workspace_bytes() */
   MOE_ERR_HIP = 5,        /* a HIP launch or runtime call failed */
-  MOE_ERR_DTYPE = 6       /* unknown dtype, or a dtype the call does not support */
+  MOE_ERR_DTYPE = 6,      /* unknown dtype, or a dtype the call does not support */
+  MOE_ERR_SCRATCH = 7     /* shape needs more than the static scratch of moe_decode_noalloc */
 };
 
 enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 };
@@ -193,6 +194,26 @@ int moe_decode(const moe_shape* shape, const void* x, const float* w_router,
                const void* w_down, const void* ws_gate, const void* ws_up,
                const void* ws_down, void* y, int32_t* topk_idx, float* topk_gate,
                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_decode_noalloc: moe_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results, bitwise, but the workspace is the library's own static
+ * device array of 1 MiB (one per GPU, held until the process ends), so the caller passes
+ * inputs and outputs only.  Shapes whose decode workspace
+ * (moe_workspace_bytes(shape, MOE_OP_DECODE)) exceeds 1 MiB return MOE_ERR_SCRATCH
+ * before any launch: B = 8, k = 8, f = fs = 2048, E = 256 needs 0.6 MiB, while
+ * B = 8, k = 16, f = 4096 (2.3 MiB) is rejected.
+ * No allocation of any kind happens inside the call.  Every call on one GPU shares that
+ * GPU's array: calls that overlap in time on one GPU (two streams, or two threads) race
+ * and must not be issued.  The array needs no initial contents (every word a call reads
+ * it first writes in the same call).
+ */
+int moe_decode_noalloc(const moe_shape* shape, const void* x, const float* w_router,
+                       const float* b_router, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* ws_gate, const void* ws_up,
+                       const void* ws_down, void* y, int32_t* topk_idx, float* topk_gate,
+                       hipStream_t stream);
 
 /*
  * moe_backward: gradients of L = sum_t <dy_t, y_t> with the routing S held

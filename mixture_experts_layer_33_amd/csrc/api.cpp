@@ -96,6 +96,8 @@ const char* moe_status_string(int st) {
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP launch or runtime error";
     case MOE_ERR_DTYPE: return "unknown or unsupported dtype";
+    case MOE_ERR_SCRATCH:
+      return "shape needs more scratch than the library's static buffer holds (moe_decode_noalloc)";
     default: return "unknown status";
   }
 }
@@ -196,26 +198,61 @@ int moe_combine(const moe_shape* s, const void* ring_y, const int32_t* copy_slot
   }
 }
 
+namespace {
+// Checks of moe_decode and moe_decode_noalloc apart from the workspace.
+int decode_checks(const moe_shape* s, const void* x, const float* w_router, const void* w_gate,
+                  const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
+                  const void* ws_down, const void* y, const int32_t* topk_idx,
+                  const float* topk_gate) {
+  int st = check_shape(s);
+  if (st) return st;
+  if (s->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (s->tokens < 1 || s->tokens > 8 || s->top_k > 16) return MOE_ERR_SHAPE;
+  if (s->hidden % 512 || s->ffn % 512 || s->hidden > 8192 || s->ffn > 4096) return MOE_ERR_SHAPE;
+  if (s->shared_ffn != 0 && s->shared_ffn != s->ffn) return MOE_ERR_SHAPE;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !y || !topk_idx || !topk_gate)
+    return MOE_ERR_NULL;
+  if (s->shared_ffn > 0 && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_NULL;
+  return MOE_OK;
+}
+}  // namespace
+
 int moe_decode(const moe_shape* s, const void* x, const float* w_router, const float* b_router,
                const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
                const void* ws_up, const void* ws_down, void* y, int32_t* topk_idx,
                float* topk_gate, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   try {
-    int st = check_shape(s);
+    int st = decode_checks(s, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
+                           topk_idx, topk_gate);
     if (st) return st;
-    if (s->dtype != MOE_BF16) return MOE_ERR_DTYPE;
-    if (s->tokens < 1 || s->tokens > 8 || s->top_k > 16) return MOE_ERR_SHAPE;
-    if (s->hidden % 512 || s->ffn % 512 || s->hidden > 8192 || s->ffn > 4096) return MOE_ERR_SHAPE;
-    if (s->shared_ffn != 0 && s->shared_ffn != s->ffn) return MOE_ERR_SHAPE;
-    if (!x || !w_router || !w_gate || !w_up || !w_down || !y || !topk_idx || !topk_gate ||
-        !workspace)
-      return MOE_ERR_NULL;
-    if (s->shared_ffn > 0 && (!ws_gate || !ws_up || !ws_down)) return MOE_ERR_NULL;
+    if (!workspace) return MOE_ERR_NULL;
     if (workspace_bytes < moe_workspace_bytes(s, MOE_OP_DECODE)) return MOE_ERR_WORKSPACE;
     return hip_status(moe::launch_decode(x, w_router, b_router, w_gate, w_up, w_down, ws_gate,
                                          ws_up, ws_down, (int)s->tokens, s->hidden, s->experts,
                                          s->top_k, s->ffn, s->shared_ffn, y, topk_idx, topk_gate,
                                          workspace, stream));
+  } catch (...) {
+    return MOE_ERR_HIP;
+  }
+}
+
+int moe_decode_noalloc(const moe_shape* s, const void* x, const float* w_router,
+                       const float* b_router, const void* w_gate, const void* w_up,
+                       const void* w_down, const void* ws_gate, const void* ws_up,
+                       const void* ws_down, void* y, int32_t* topk_idx, float* topk_gate,
+                       hipStream_t stream) {
+  try {
+    int st = decode_checks(s, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
+                           topk_idx, topk_gate);
+    if (st) return st;
+    if (moe_workspace_bytes(s, MOE_OP_DECODE) > moe::DECODE_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    void* scratch = nullptr;
+    hipError_t err = moe::decode_scratch(&scratch);
+    if (err != hipSuccess || !scratch) return MOE_ERR_HIP;
+    return hip_status(moe::launch_decode(x, w_router, b_router, w_gate, w_up, w_down, ws_gate,
+                                         ws_up, ws_down, (int)s->tokens, s->hidden, s->experts,
+                                         s->top_k, s->ffn, s->shared_ffn, y, topk_idx, topk_gate,
+                                         scratch, stream));
   } catch (...) {
     return MOE_ERR_HIP;
   }

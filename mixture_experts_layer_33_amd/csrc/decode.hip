@@ -25,6 +25,8 @@
 // used once per call, and on gfx950 such streaming loads reach a higher HBM rate
 // (a bare 16-byte-per-lane read: about 6.9 against 6.2 TB/s; at B = 1 the call went
 // from 154.6 to 138-141 us) while W_r, x and h keep the default policy.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -354,6 +356,33 @@ __global__ __launch_bounds__(256) void decode_k2(DecodeArgs p) {
 size_t decode_workspace_bytes(int B, int E, int k, int f, int fs) {
   return ((size_t)DEC_RP * B * E + (size_t)B * (fs > 0 ? fs : 1) + (size_t)B * k * f) * sizeof(float) +
          (DEC_BMAX * DEC_KMAX + 1) * sizeof(int32_t);
+}
+
+// Scratch for callers that cannot allocate (moe_decode_noalloc): the decode workspace of
+// the largest shape that variant accepts, in a file-scope device array.  Each GPU the
+// library runs on holds its own copy until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol): the
+// address used is the one hipGetSymbolAddress returns on each device, taken once per
+// device with that device current.
+static __device__ __align__(256) uint8_t scratch[DECODE_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+static std::once_flag scratch_once[SCRATCH_MAX_DEVICES];
+static void* scratch_ptr[SCRATCH_MAX_DEVICES];
+static hipError_t scratch_err[SCRATCH_MAX_DEVICES];
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::call_once(scratch_once[dev], [dev] {
+    void* p = nullptr;
+    scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    scratch_ptr[dev] = scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *ptr = scratch_ptr[dev];
+  return scratch_err[dev];
 }
 
 hipError_t launch_decode(const void* x, const float* w_r, const float* b_r, const void* w_gate,

@@ -44,6 +44,11 @@ hipError_t launch_decode(const void* x, const float* w_r, const float* b_r, cons
                          int f, int fs, void* y, int32_t* topk_idx, float* topk_gate, void* ws,
                          hipStream_t st);
 
+// decode without a caller workspace: the device address of the library's static scratch
+// array on the current device (DECODE_SCRATCH_BYTES), looked up once per device
+constexpr size_t DECODE_SCRATCH_BYTES = (size_t)1 << 20;   // 1 MiB
+hipError_t decode_scratch(void** ptr);
+
 // backward
 size_t backward_workspace_bytes(int64_t T, int64_t C, int d, int E, int k, int f);
 hipError_t launch_backward(const void* dy, const void* x, const float* w_r,

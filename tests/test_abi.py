@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = _lib.lib()
-    for code in range(7):
+    for code in range(8):
         assert L.moe_status_string(code)
     assert b"unknown" in L.moe_status_string(99)
 
@@ -162,3 +162,16 @@ def test_rings_of_4_gib_are_rejected():
     # a ring stack of six skewed layers (d 4096, 102,400 rows each) would need 5 GB per array
     with pytest.raises(moe.MoeError):
         moe.RingStack(6, T=8192, d=4096, E=512, k=10, f=1024, device="cpu")
+
+
+def test_decode_noalloc_validates_on_the_host():
+    """The allocation-free decode rejects, before any HIP call, what moe_decode rejects and
+    shapes whose workspace exceeds its 1 MiB static scratch."""
+    L = _lib.lib()
+    ok = moe.make_shape(8, 7168, 256, 8, 2048, fs=2048)
+    assert moe.workspace_bytes(ok, _lib.OP_DECODE) <= (1 << 20)
+    big = moe.make_shape(8, 1024, 64, 16, 4096, fs=4096)
+    assert L.moe_decode_noalloc(big, *([FAKE] * 12), None) == _lib.MOE_ERR_SCRATCH
+    assert L.moe_decode_noalloc(moe.make_shape(9, 1024, 16, 4, 512), *([FAKE] * 12), None) == _lib.MOE_ERR_SHAPE
+    assert L.moe_decode_noalloc(ok, *([FAKE] * 9), None, FAKE, FAKE, None) == _lib.MOE_ERR_NULL
+    assert b"scratch" in L.moe_status_string(_lib.MOE_ERR_SCRATCH)
