@@ -112,17 +112,56 @@ constexpr int DL = (DA_BYTES + DB_BYTES) / 4096;   // 1 KB copies per wave per s
 
 __device__ __forceinline__ int aswz(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
+// Row tiles per group in the dgrad tile order (below): the down dgrad's copy rows are
+// d wide (1 MB per 128-row tile at d = 4096) and its 8 column tiles all run at once;
+// the gate/up dgrad's are 2f wide (512 KB) against 32 column tiles.
+constexpr int DG_GROUP_DOWN = 8, DG_GROUP_UP = 4;
+
+// Logical tile L of an expert-major list of (row tile, column tile) pairs, nct column
+// tiles per row tile, row tiles in groups of G per expert with the column tile slower
+// than the row tile inside a group.  The expert of L is that of row tile L / nct (the
+// expert's range of L is the same in row-major order); tiles[2 i + 1] / BT is row tile
+// i's index inside its expert.
+__device__ __forceinline__ void grouped_tile(int L, int nct, int G, const int32_t* tiles,
+                                             const int32_t* offset, int& mt, int& ct) {
+  const int mr = L / nct;
+  const int e = tiles[2 * mr];
+  const int t0 = mr - tiles[2 * mr + 1] / BT;                       // the expert's first row tile
+  const int R = (offset[e + 1] - offset[e] + BT - 1) / BT;          // its row tiles
+  const int local = L - t0 * nct;
+  const int g = local / (G * nct);
+  const int rg = min(G, R - g * G);                                 // row tiles in group g
+  const int rem = local - g * G * nct;
+  ct = rem / rg;
+  mt = t0 + g * G + rem % rg;
+}
+
 template <bool DOWN>
 __global__ __launch_bounds__(256, 3) void dgrad_kernel(DgradArgs p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   __shared__ float red[2][BT];
-  const int mt = blockIdx.y;
-  if (mt >= *p.ntiles) return;
+  // Tile order: workgroup b runs on XCD b % 8, and XCD x takes the logical tiles
+  // [x per, (x + 1) per), per = ceil(V / 8) of the V live tiles.  Logical tiles are
+  // expert-major; an expert's row tiles form groups of G, and inside a group the column
+  // tile is slower than the row tile: the group's row tiles read each weight panel
+  // together, through one L2, and the group's copy rows stay there for all its column
+  // tiles.  Fetched at 8,192 skewed tokens (FETCH_SIZE, copy-calibrated), down | gate/up
+  // dgrad: column tile as blockIdx.x (every XCD fetched every row tile's copy rows) 10.8 |
+  // 12.5 GB; row-major contiguous ranges (the gate/up weights re-fetched per row tile)
+  // 7.6 | 15.6 GB; this order 7.0 | 10.8 GB, against 5.3 | 8.9 GB algorithmic.  The
+  // kernel times did not change (1.79 | 2.91 ms): these kernels are bound by their
+  // copy-to-MFMA pipeline, not by HBM traffic.
+  const int nct = p.N / BT;
+  const int V = *p.ntiles * nct, per = (V + 7) / 8;
+  const int li = (int)(blockIdx.x >> 3), L = (int)(blockIdx.x & 7) * per + li;
+  if (li >= per || L >= V) return;
+  int mt, ct;
+  grouped_tile(L, nct, DOWN ? DG_GROUP_DOWN : DG_GROUP_UP, p.tiles, p.offset, mt, ct);
   const int e = p.tiles[2 * mt], row0 = p.tiles[2 * mt + 1];
   const int32_t seg = p.offset[e];
   const int rows = min(BT, p.offset[e + 1] - seg - row0);
-  const int n0 = blockIdx.x * BT;
+  const int n0 = ct * BT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lg = lane >> 5;
@@ -247,7 +286,7 @@ __global__ __launch_bounds__(256, 3) void dgrad_kernel(DgradArgs p) {
     __syncthreads();
     if (tid < rows) {
       const int64_t s = ring_slot(p.head, seg, row0 + tid, p.C);
-      p.dgpart[s * (f / BT) + blockIdx.x] = red[0][tid] + red[1][tid];
+      p.dgpart[s * (f / BT) + n0 / BT] = red[0][tid] + red[1][tid];
     }
   } else {
 #pragma unroll
@@ -457,15 +496,18 @@ __global__ __launch_bounds__(256, OCC) void wgrad_kernel(WgradArgs p) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   const int mtiles = (p.M + WM_ - 1) / WM_, ntiles = (p.N + S::WN - 1) / S::WN;
   const int P = mtiles * ntiles;   // tiles per expert
-  // Workgroup b runs on XCD b % 8.  Each expert's P tiles are dealt to the 8 XCDs in
-  // 8 contiguous chunks, and XCD x walks its chunk of every expert, experts E-1 -> 0:
-  // each XCD gets the same share of every expert's rows, however skewed the loads.
-  // A chunk spans all tiles along the operand with the smaller panel (A when M < N),
-  // so every XCD's L2 reads the whole of that panel but only its slice of the other.
+  // Workgroup b runs on XCD b % 8.  XCD x takes whole experts, those with e % 8 == x,
+  // from the largest id down (experts E-1 -> 0 overall), all P tiles of each: both
+  // operand panels of an expert are then fetched once, into one XCD's L2.  Interleaved
+  // ids spread the hottest experts over the eight XCDs.  Dealing every expert's tiles
+  // over all eight XCDs fetched each panel once per XCD: 2.03 + 3.39 GB (down, gate/up)
+  // against 0.84 + 1.0 GB algorithmic in the skewed 8,192-token backward; this order
+  // fetches 0.93 + 1.80 GB in the same time (1.67 + 3.06 ms: the dW stores bound it).
   const int x = blockIdx.x & 7, li = blockIdx.x >> 3;
-  const int cbase = x * P / 8, cnt = (x + 1) * P / 8 - cbase;
-  if (cnt == 0 || li >= cnt * p.E) return;
-  const int e = p.E - 1 - li / cnt, jt = cbase + li % cnt;
+  if (x >= p.E) return;
+  const int etop = p.E - 1 - ((p.E - 1 - x) & 7);   // the largest expert id = x (mod 8)
+  const int e = etop - 8 * (li / P), jt = li % P;
+  if (e < 0) return;
   const bool nmajor = p.M < p.N;
   const int m0 = (nmajor ? jt % mtiles : jt / ntiles) * WM_;
   const int n0 = (nmajor ? jt / mtiles : jt % ntiles) * S::WN;
@@ -654,7 +696,7 @@ static hipError_t run_wgrad(const WgradArgs& a, hipStream_t st) {
     if (err != hipSuccess) return err;
   }
   const int64_t P = (int64_t)((a.M + WM_ - 1) / WM_) * ((a.N + WgShape<WG_NJ>::WN - 1) / WgShape<WG_NJ>::WN);
-  kern<<<(unsigned)(8 * ((P + 7) / 8) * a.E), 256, lds, st>>>(a);   // 8 XCDs x the largest chunk
+  kern<<<(unsigned)(8 * P * ((a.E + 7) / 8)), 256, lds, st>>>(a);   // 8 XCDs x P x the longest expert list
   return hipGetLastError();
 }
 
@@ -709,7 +751,8 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
   a.dau = dau;
   a.gh = gh;
   a.dgpart = dgpart;
-  dgrad_kernel<true><<<dim3(f / BT, max_tiles), 256, DG_LDS, st>>>(a);
+  // 1-D grids over the bound max_tiles x column tiles (XCD-contiguous tile order inside)
+  dgrad_kernel<true><<<(unsigned)(8 * (((int64_t)max_tiles * (f / BT) + 7) / 8)), 256, DG_LDS, st>>>(a);
   DgradArgs b = a;
   b.A = dau;
   b.B0 = (const bf16_t*)w_gate;
@@ -717,7 +760,7 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
   b.K = 2 * f;
   b.N = d;
   b.dxc = dxc;
-  dgrad_kernel<false><<<dim3(d / BT, max_tiles), 256, DG_LDS, st>>>(b);
+  dgrad_kernel<false><<<(unsigned)(8 * (((int64_t)max_tiles * (d / BT) + 7) / 8)), 256, DG_LDS, st>>>(b);
   token_kernel<<<(unsigned)T, 256, 0, st>>>(copy_slot, topk_idx, topk_gate, dgpart, f / BT, dxc,
                                             w_r, d, k, dl, (bf16_t*)dx);
   float* rpart = (float*)(w + L.rpart);
