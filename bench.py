@@ -125,6 +125,31 @@ def measure_forward(torch, moe, inp, cfg, steps, warmup, scales=(None, None, Non
     return ms, g1, g2, layer, spread
 
 
+def measure_fused(torch, moe, inp, cfg, steps, warmup, chained):
+    """The same forward as one kernel launch (moe_forward): ms per step back to back, the
+    per-step spread, and whether every output and ring buffer equals the chained calls'
+    bit for bit (`chained`: the Layer of the timed chained forward)."""
+    layer = moe.Layer.create(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.C, dtype=cfg.dtype)
+    args = (inp.x, inp.w_router, inp.b_router, inp.w_gate, inp.w_up, inp.w_down)
+    for _ in range(max(1, warmup)):
+        layer.forward_fused(*args)
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record()
+    for i in range(steps):
+        layer.forward_fused(*args)
+        marks[i + 1].record()
+    torch.cuda.synchronize()
+    ms = marks[0].elapsed_time(marks[steps]) / steps
+    per = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    same = all(torch.equal(layer.bufs[n].view(torch.uint8), chained.bufs[n].view(torch.uint8))
+               for n in ("topk_idx", "topk_gate", "expert_count", "expert_offset", "copy_slot", "y"))
+    return {"launches_per_step": 1, "ms_per_step": round(ms, 4), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+            "step_ms_median": round(per[len(per) // 2], 4), "step_ms_min": round(per[0], 4),
+            "step_ms_p90": round(per[int(0.9 * (len(per) - 1))], 4),
+            "barrier_status": layer.forward_status(), "bitwise_equal_to_chained": bool(same)}
+
+
 def expert_bytes(counts, d, f, elem_bytes, scale_bytes_per_elem=0.0):
     used = int((counts > 0).sum())
     per = d * f * (elem_bytes + scale_bytes_per_elem)
@@ -503,6 +528,8 @@ def main():
         "timed_wall_s": round(wall, 3),
     }
     result.update(spread)
+    progress("single-launch forward (moe_forward)")
+    result["fused_forward"] = measure_fused(torch, moe, inp, cfg, args.steps, args.warmup, layer)
     progress(f"forward {ms:.3f} ms/step, gate/up GEMM {g1:.3f} ms, down GEMM {g2:.3f} ms")
     calibrate_copy(torch, args)
     if not args.no_secondary:

@@ -76,7 +76,7 @@ enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 };
 
 enum moe_op {
   MOE_OP_ROUTE = 0, MOE_OP_DISPATCH = 1, MOE_OP_EXPERT_FFN = 2,
-  MOE_OP_COMBINE = 3, MOE_OP_DECODE = 4, MOE_OP_BACKWARD = 5
+  MOE_OP_COMBINE = 3, MOE_OP_DECODE = 4, MOE_OP_BACKWARD = 5, MOE_OP_FORWARD = 6
 };
 
 /* Shape of one layer call (host struct). */
@@ -171,6 +171,37 @@ int moe_expert_ffn_timed(const moe_shape* shape, const void* ring_x, const uint8
  */
 int moe_combine(const moe_shape* shape, const void* ring_y, const int32_t* copy_slot,
                 const float* topk_gate, void* y, hipStream_t stream);
+
+/*
+ * moe_forward: the whole forward (moe_route, moe_dispatch, moe_expert_ffn, moe_combine)
+ * in ONE kernel launch, persistent and deterministic (dzen.guru page, megakernel
+ * paragraph of "Три решения…": one GPU call moves and computes, with one deterministic
+ * result; @cursor_ai tweet on the khabar-ai page: a single, fully deterministic kernel).
+ * Same arguments and outputs as the four calls chained (the router's workspace, the
+ * dispatch's and the FFN's live inside this call's workspace); every output is bitwise
+ * the chained calls' where those run the 128-row GEMM tile (fewer than 256 copies per
+ * expert on average), and equal up to fp32 rounding order otherwise.
+ * In:  x [T,d] bf16, w_router [E,d] f32, b_router [E] f32 or NULL, w_gate/w_up [E,f,d] and
+ *      w_down [E,d,f] bf16, ring_head in [0, C).
+ * Out: topk_idx, topk_gate, expert_count (as moe_route); ring_x, expert_offset, copy_slot,
+ *      slot_copy (as moe_dispatch); ring_y [C,d] bf16 and saved_au [C,2f] bf16 or NULL
+ *      (as moe_expert_ffn); y [T,d] bf16 (as moe_combine).
+ * The kernel is launched cooperatively, one workgroup per CU (a multiple of 8), and its
+ * phases meet at grid barriers kept in the first 256 bytes of the workspace: those bytes
+ * must be zero before the first call on a workspace and are kept consistent by every
+ * call (the rest of the workspace needs no initial contents).  A barrier wait gives up
+ * after spin_limit polls (0: 4,194,304, far beyond any normal wait) and then sets bit 0
+ * of the 32-bit status word at byte offset 8 of the workspace; the results of that call
+ * are then undefined, the bit stays set until the caller clears it, and the first 256
+ * bytes must be zeroed before the next call.  Calls sharing a workspace must not overlap.
+ * workspace: moe_workspace_bytes(shape, MOE_OP_FORWARD) bytes.  MOE_BF16 only.
+ */
+int moe_forward(const moe_shape* shape, const void* x, const float* w_router,
+                const float* b_router, const void* w_gate, const void* w_up, const void* w_down,
+                int64_t ring_head, int32_t* topk_idx, float* topk_gate, int32_t* expert_count,
+                void* ring_x, int32_t* expert_offset, int32_t* copy_slot, int32_t* slot_copy,
+                void* ring_y, void* saved_au, void* y, uint32_t spin_limit, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_decode: small-batch decode parallelised over outputs, in two kernels and

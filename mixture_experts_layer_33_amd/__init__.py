@@ -14,11 +14,13 @@ from typing import Dict, Optional
 import torch
 
 from ._lib import (DTYPES, MOE_BF16, MOE_F32, MOE_MXFP8, OP_BACKWARD, OP_COMBINE, OP_DECODE,
-                   OP_DISPATCH, OP_EXPERT_FFN, OP_ROUTE, LIB_PATH, MoeError, MoeShape, check, lib)
+                   OP_DISPATCH, OP_EXPERT_FFN, OP_FORWARD, OP_ROUTE, LIB_PATH, MoeError, MoeShape,
+                   check, lib)
 
 __all__ = ["make_shape", "check_shape", "workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn",
            "moe_expert_ffn_timed",
-           "moe_combine", "moe_decode", "moe_backward", "moe_quantize_mx", "Layer", "MoeError",
+           "moe_combine", "moe_forward", "moe_decode", "moe_backward", "moe_quantize_mx", "Layer",
+           "MoeError",
            "LIB_PATH"]
 
 
@@ -99,6 +101,17 @@ def moe_expert_ffn_timed(shape, ring_x, ring_x_scale, expert_offset, ring_head, 
 def moe_combine(shape, ring_y, copy_slot, topk_gate, y, stream=None):
     check("moe_combine", lib().moe_combine(shape, _p(ring_y), _p(copy_slot), _p(topk_gate), _p(y),
                                            _s(stream)))
+
+
+def moe_forward(shape, x, w_router, b_router, w_gate, w_up, w_down, ring_head, topk_idx, topk_gate,
+                expert_count, ring_x, expert_offset, copy_slot, slot_copy, ring_y, saved_au, y, ws,
+                spin_limit=0, stream=None):
+    """The whole forward in one cooperative launch (bf16)."""
+    check("moe_forward", lib().moe_forward(
+        shape, _p(x), _p(w_router), _p(b_router), _p(w_gate), _p(w_up), _p(w_down), int(ring_head),
+        _p(topk_idx), _p(topk_gate), _p(expert_count), _p(ring_x), _p(expert_offset), _p(copy_slot),
+        _p(slot_copy), _p(ring_y), _p(saved_au), _p(y), int(spin_limit), _p(ws), ws.numel(),
+        _s(stream)))
 
 
 def moe_decode(shape, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
@@ -212,6 +225,29 @@ class Layer:
                                      events)
         y = self.combine(ring_y, cs, gate)
         return y
+
+    def forward_fused(self, x, w_router, b_router, w_gate, w_up, w_down, head=0, save_au=False,
+                      spin_limit=0):
+        """The forward as one kernel launch (moe_forward), into the same buffers as forward()."""
+        s = self.shape
+        T, k, E, C = s.tokens, s.top_k, s.experts, s.capacity
+        b = {"topk_idx": ((T, k), torch.int32), "topk_gate": ((T, k), torch.float32),
+             "expert_count": ((E,), torch.int32), "ring_x": ((C, s.hidden), torch.bfloat16),
+             "expert_offset": ((E + 1,), torch.int32), "copy_slot": ((T, k), torch.int32),
+             "slot_copy": ((C,), torch.int32), "ring_y": ((C, s.hidden), torch.bfloat16),
+             "y": ((T, s.hidden), torch.bfloat16)}
+        t = {n: self._buf(n, shp, dt) for n, (shp, dt) in b.items()}
+        au = self._buf("saved_au", (C, 2 * s.ffn), torch.bfloat16) if save_au else None
+        moe_forward(s, x, w_router, b_router, w_gate, w_up, w_down, head, t["topk_idx"],
+                    t["topk_gate"], t["expert_count"], t["ring_x"], t["expert_offset"],
+                    t["copy_slot"], t["slot_copy"], t["ring_y"], au, t["y"], self._ws(OP_FORWARD),
+                    spin_limit)
+        return t["y"]
+
+    def forward_status(self) -> int:
+        """The fused forward's status word (bit 0: a grid barrier gave up); a host read."""
+        ws = self.bufs.get(f"ws{OP_FORWARD}")
+        return 0 if ws is None else int(ws[8:12].view(torch.int32).item())
 
     def decode(self, x, w_router, b_router, w_gate, w_up, w_down, ws_gate=None, ws_up=None,
                ws_down=None):

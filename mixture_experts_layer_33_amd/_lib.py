@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 (MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_CAPACITY, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_DTYPE,
  MOE_ERR_SCRATCH) = range(8)
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
-OP_ROUTE, OP_DISPATCH, OP_EXPERT_FFN, OP_COMBINE, OP_DECODE, OP_BACKWARD = range(6)
+OP_ROUTE, OP_DISPATCH, OP_EXPERT_FFN, OP_COMBINE, OP_DECODE, OP_BACKWARD, OP_FORWARD = range(7)
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp8": MOE_MXFP8}
 
@@ -34,6 +34,7 @@ SIGNATURES = {
     "moe_expert_ffn": [SHP, P, P, P, I64, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_expert_ffn_timed": [SHP, P, P, P, I64, P, P, P, P, P, P, P, P, P, SZ, P, P],
     "moe_combine": [SHP, P, P, P, P, P],
+    "moe_forward": [SHP, P, P, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, P, C.c_uint32, P, SZ, P],
     "moe_decode": [SHP, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
     "moe_decode_noalloc": [SHP, P, P, P, P, P, P, P, P, P, P, P, P, P],
     "moe_backward": [SHP, P, P, P, P, P, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, P, SZ, P],

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["api.cpp", "route.hip", "dispatch.hip", "gemm.hip", "combine.hip", "decode.hip",
-           "backward.hip", "mxq.hip"]
+           "backward.hip", "mxq.hip", "fused.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -78,6 +78,10 @@ size_t moe_workspace_bytes(const moe_shape* s, int op) {
     case MOE_OP_DECODE:
       return align256(moe::decode_workspace_bytes((int)T, s->experts, s->top_k, s->ffn,
                                                   s->shared_ffn));
+    case MOE_OP_FORWARD:
+      return s->dtype == MOE_BF16
+                 ? align256(moe::fused_workspace_bytes(T, C, s->hidden, s->experts, s->ffn))
+                 : 0;
     case MOE_OP_BACKWARD:
       return align256(moe::backward_workspace_bytes(T, C, s->hidden, s->experts, s->top_k,
                                                     s->ffn));
@@ -193,6 +197,38 @@ int moe_combine(const moe_shape* s, const void* ring_y, const int32_t* copy_slot
       return MOE_ERR_NULL;
     return hip_status(moe::launch_combine(s->dtype == MOE_F32, ring_y, copy_slot, topk_gate,
                                           s->tokens, s->hidden, s->top_k, y, stream));
+  } catch (...) {
+    return MOE_ERR_HIP;
+  }
+}
+
+int moe_forward(const moe_shape* s, const void* x, const float* w_router, const float* b_router,
+                const void* w_gate, const void* w_up, const void* w_down, int64_t ring_head,
+                int32_t* topk_idx, float* topk_gate, int32_t* expert_count, void* ring_x,
+                int32_t* expert_offset, int32_t* copy_slot, int32_t* slot_copy, void* ring_y,
+                void* saved_au, void* y, uint32_t spin_limit, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  try {
+    int st = check_shape(s);
+    if (st) return st;
+    if (s->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    const int64_t T = s->tokens;
+    if (missing_tok(x, T) || !w_router || !w_gate || !w_up || !w_down ||
+        missing_tok(topk_idx, T) || missing_tok(topk_gate, T) || !expert_count || !ring_x ||
+        !expert_offset || missing_tok(copy_slot, T) || !slot_copy || !ring_y ||
+        missing_tok(y, T) || !workspace)
+      return MOE_ERR_NULL;
+    if (ring_head < 0 || ring_head >= s->capacity) return MOE_ERR_SHAPE;
+    if (workspace_bytes < moe_workspace_bytes(s, MOE_OP_FORWARD)) return MOE_ERR_WORKSPACE;
+    if (T == 0) {   // no copies: every count and segment offset is zero
+      hipError_t err = zero_words(expert_count, (size_t)s->experts, stream);
+      if (err == hipSuccess) err = zero_words(expert_offset, (size_t)s->experts + 1, stream);
+      return hip_status(err);
+    }
+    return hip_status(moe::launch_forward_fused(
+        x, w_router, b_router, w_gate, w_up, w_down, T, s->hidden, s->experts, s->top_k, s->ffn,
+        s->capacity, ring_head, topk_idx, topk_gate, expert_count, ring_x, expert_offset,
+        copy_slot, slot_copy, ring_y, saved_au, y, spin_limit, workspace, stream));
   } catch (...) {
     return MOE_ERR_HIP;
   }

@@ -13,29 +13,17 @@
 //      slot = (head + rank) mod C; the row is read once and written to its k
 //      slots (MX: quantised once, codes and scales written k times).
 #include "common.h"
+#include "dispatch_body.h"
 #include "kernels.h"
 
 namespace moe {
-
-constexpr int DCH = 64;  // tokens per chunk = wavefront width
 
 __global__ __launch_bounds__(64) void dispatch_hist_kernel(const int32_t* __restrict__ idx,
                                                            int64_t T, int k, int E,
                                                            unsigned long long* __restrict__ masks,
                                                            int32_t* __restrict__ hist) {
   extern __shared__ unsigned long long m[];
-  const int lane = threadIdx.x;
-  const int64_t chunk = blockIdx.x;
-  for (int e = lane; e < E; e += 64) m[e] = 0ull;
-  __syncthreads();
-  const int64_t t = chunk * DCH + lane;
-  if (t < T)
-    for (int j = 0; j < k; ++j) atomicOr(&m[idx[t * k + j]], 1ull << lane);
-  __syncthreads();
-  for (int e = lane; e < E; e += 64) {
-    masks[chunk * E + e] = m[e];
-    hist[chunk * E + e] = __popcll(m[e]);
-  }
+  dispatch_hist_chunk(idx, T, k, E, masks, hist, blockIdx.x, m);
 }
 
 // One workgroup of 1024 threads, one expert per thread (E <= 1024).  A thread walks
@@ -85,28 +73,6 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
   if (e == E - 1) expert_offset[E] = sc[e];
 }
 
-__device__ __forceinline__ void copy_slots(const int32_t* __restrict__ idx,
-                                           const unsigned long long* __restrict__ masks,
-                                           const int32_t* __restrict__ base, int64_t t, int k,
-                                           int E, int64_t head, int64_t C,
-                                           int32_t* __restrict__ copy_slot,
-                                           int32_t* __restrict__ slot_copy, int64_t* slots) {
-  const int j = threadIdx.x;
-  if (j < k) {
-    const int64_t chunk = t / DCH;
-    const int lc = (int)(t % DCH);
-    const int e = idx[t * k + j];
-    const unsigned long long mk = masks[chunk * E + e];
-    const int64_t rank = base[chunk * E + e] + __popcll(mk & ((1ull << lc) - 1ull));
-    int64_t s = head + rank;
-    if (s >= C) s -= C;
-    slots[j] = s;
-    copy_slot[t * k + j] = (int32_t)s;
-    slot_copy[s] = (int32_t)(t * k + j);
-  }
-  __syncthreads();
-}
-
 // Plain copy of one token row (row_bytes a multiple of 16) into its k slots, read and
 // written with the non-temporal cache policy (every byte moves once; whole forward at
 // 2,048 tokens 4.081 -> 4.050 ms, skewed 8,192 tokens 4.242 -> 4.184 ms).
@@ -116,14 +82,8 @@ __global__ __launch_bounds__(256) void dispatch_copy_kernel(
     int64_t head, int64_t C, int64_t row_bytes, uint8_t* __restrict__ ring,
     int32_t* __restrict__ copy_slot, int32_t* __restrict__ slot_copy) {
   __shared__ int64_t slots[64];
-  const int64_t t = blockIdx.x;
-  copy_slots(idx, masks, base, t, k, E, head, C, copy_slot, slot_copy, slots);
-  const int64_t nv = row_bytes / 16;
-  const u32x4* src = (const u32x4*)(x + t * row_bytes);
-  for (int64_t v = threadIdx.x; v < nv; v += blockDim.x) {
-    const u32x4 val = __builtin_nontemporal_load(src + v);
-    for (int j = 0; j < k; ++j) __builtin_nontemporal_store(val, (u32x4*)(ring + slots[j] * row_bytes) + v);
-  }
+  dispatch_copy_token(x, idx, masks, base, k, E, head, C, row_bytes, ring, copy_slot, slot_copy,
+                      blockIdx.x, slots);
 }
 
 // MX: each 32-element block is held by 4 consecutive lanes (8 bf16 each).

@@ -44,6 +44,16 @@ hipError_t launch_decode(const void* x, const float* w_r, const float* b_r, cons
                          int f, int fs, void* y, int32_t* topk_idx, float* topk_gate, void* ws,
                          hipStream_t st);
 
+// the whole forward in one cooperative launch (bf16)
+size_t fused_workspace_bytes(int64_t T, int64_t C, int d, int E, int f);
+hipError_t launch_forward_fused(const void* x, const float* w_r, const float* b_r,
+                                const void* w_gate, const void* w_up, const void* w_down,
+                                int64_t T, int d, int E, int k, int f, int64_t C, int64_t head,
+                                int32_t* topk_idx, float* topk_gate, int32_t* expert_count,
+                                void* ring_x, int32_t* expert_offset, int32_t* copy_slot,
+                                int32_t* slot_copy, void* ring_y, void* saved_au, void* y,
+                                uint32_t spin_limit, void* ws, hipStream_t st);
+
 // decode without a caller workspace: the device address of the library's static scratch
 // array on the current device (DECODE_SCRATCH_BYTES), looked up once per device
 constexpr size_t DECODE_SCRATCH_BYTES = (size_t)1 << 20;   // 1 MiB

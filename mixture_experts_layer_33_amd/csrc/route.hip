@@ -8,6 +8,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "route_body.h"
 
 namespace moe {
 
@@ -85,122 +86,17 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 // x * w_plane of a bf16 x is exact in fp32 and the MFMA accumulates in fp32.
 __global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ w,
                                                            int64_t n, bf16_t* __restrict__ w3) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const float v = w[i];
-    const bf16_t hi = f2bf(v);
-    const float r1 = v - bf2f(hi);
-    const bf16_t mid = f2bf(r1);
-    const bf16_t lo = f2bf(r1 - bf2f(mid));
-    w3[i] = hi;
-    w3[n + i] = mid;
-    w3[2 * n + i] = lo;
-  }
+  router_split_range(w, n, w3, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
 }
-
-// BM tokens x 64 experts per workgroup; waves (BM/32) x 2, each a 32 x 32 tile
-// with one accumulator per plane; K in 64-element slices through double-buffered,
-// XOR-swizzled LDS.  The K range is split over gridDim.z workgroups: split z sums
-// slices [z KT / KS, (z + 1) KT / KS) and writes partial plane z of the logits,
-// (acc_hi + acc_mid) + acc_lo; the top-k kernel adds the planes in order z = 0, 1, ...
-// and then the bias.  Two K slices are in flight while one is multiplied: slice
-// kt + 1 (requested during the previous slice) and kt + 2, in two register sets.
-constexpr int RM_K = 128;   // bytes of K per row per stage
-
-__device__ __forceinline__ int rswz(int r, int c) { return r * RM_K + ((c ^ (r & 7)) << 4); }
 
 template <int BM>
 __global__ __launch_bounds__(BM * 4) void router_mfma_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w3, float* __restrict__ logits,
     int64_t T, int d, int E) {
-  constexpr int NT = BM * 4, BNR = 192;          // threads; B rows = 3 planes x 64 experts
-  constexpr int A_LD = BM * 8 / NT, B_LD = BNR * 8 / NT;
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * RM_K];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BNR * RM_K];
-  const int64_t t0 = (int64_t)blockIdx.y * BM;
-  const int e0 = blockIdx.x * 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lg = lane >> 5;
-  const int64_t n = (int64_t)E * d;
-  const int KS = gridDim.z, z = blockIdx.z, KA = d / 64;
-  const int kb = (int)((int64_t)KA * z / KS);
-  const int KT = (int)((int64_t)KA * (z + 1) / KS) - kb;
-  const bf16_t* a_src[A_LD];
-  const bf16_t* b_src[B_LD];
-#pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int q = tid + NT * i;
-    const int64_t t = min(t0 + q / 8, T - 1);
-    a_src[i] = x + t * d + (int64_t)kb * 64 + (q % 8) * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int q = tid + NT * i, r = q / 8;
-    const int e = min(e0 + r % 64, E - 1);
-    b_src[i] = w3 + (r / 64) * n + (int64_t)e * d + (int64_t)kb * 64 + (q % 8) * 8;
-  }
-  u32x4 ra0[A_LD], rb0[B_LD], ra1[A_LD], rb1[B_LD];
-#define R_LOAD(kt, RA, RB)                                                                   \
-  {                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) RA[i] = *(const u32x4*)(a_src[i] + (kt) * 64); \
-    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) RB[i] = *(const u32x4*)(b_src[i] + (kt) * 64); \
-  }
-#define R_STORE(buf, RA, RB)                                                                 \
-  {                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) {                                      \
-      const int q = tid + NT * i;                                                            \
-      *(u32x4*)(As[buf] + rswz(q / 8, q % 8)) = RA[i];                                       \
-    }                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) {                                      \
-      const int q = tid + NT * i;                                                            \
-      *(u32x4*)(Bs[buf] + rswz(q / 8, q % 8)) = RB[i];                                       \
-    }                                                                                        \
-  }
-  f32x16 acc[3];
-#pragma unroll
-  for (int p = 0; p < 3; ++p)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[p][r] = 0.f;
-  auto compute = [&](int cur) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int c = kk * 2 + lg;
-      const bf16x8 a = __builtin_bit_cast(bf16x8, *(const u32x4*)(As[cur] + rswz(wm * 32 + lr, c)));
-#pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        const bf16x8 b =
-            __builtin_bit_cast(bf16x8, *(const u32x4*)(Bs[cur] + rswz(p * 64 + wn * 32 + lr, c)));
-        acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[p], 0, 0, 0);
-      }
-    }
-  };
-  R_LOAD(0, ra0, rb0);
-  if (KT > 1) R_LOAD(1, ra1, rb1);
-  R_STORE(0, ra0, rb0);
-  __syncthreads();
-  // LDS buffer 0 holds even slices, buffer 1 odd ones; each buffer is rewritten only
-  // after the barrier that follows its last read.
-  for (int kt = 0; kt < KT; kt += 2) {
-    if (kt + 2 < KT) R_LOAD(kt + 2, ra0, rb0);
-    compute(0);
-    if (kt + 1 >= KT) break;
-    R_STORE(1, ra1, rb1);
-    __syncthreads();
-    if (kt + 3 < KT) R_LOAD(kt + 3, ra1, rb1);
-    compute(1);
-    if (kt + 2 >= KT) break;
-    R_STORE(0, ra0, rb0);
-    __syncthreads();
-  }
-#undef R_LOAD
-#undef R_STORE
-  const int e = e0 + wn * 32 + lr;
-  if (e >= E) return;
-  float* out = logits + (int64_t)z * T * E;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t t = t0 + wm * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-    if (t < T) out[t * E + e] = (acc[0][r] + acc[1][r]) + acc[2][r];
-  }
+  __shared__ __attribute__((aligned(16))) uint8_t As[2 * BM * RM_K];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2 * 192 * RM_K];
+  router_mfma_body<BM>(x, w3, logits, T, d, E, (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z,
+                       (int)gridDim.z, As, Bs);
 }
 
 // The same logits with 128 tokens x 128 experts per workgroup: sixteen waves in 4 x 4, each
@@ -300,68 +196,13 @@ __global__ __launch_bounds__(R2_NT) void router_mfma2_kernel(
   }
 }
 
-// With 128 or more experts the 128 x 128 tile is taken: its expert tiles are mostly full,
-// and it halves the L2 traffic per logit (60 -> 55 us for 2,048 tokens, d 7168, 256
-// experts; 219 -> 175 us for 8,192 tokens, d 4096, 512 experts).
-static bool router_big(int E) { return E >= 128; }
-
-constexpr int RT_MAX_KS = 8;   // most K splits of the bf16 router (partial logit planes)
-
-// Number of K splits of the bf16 router: enough workgroups to give every CU two 64 x 64
-// tiles or one 128 x 128 tile, keeping at least 8 K slices per split.
-static int router_ksplit(int64_t T, int E, int d) {
-  const bool big = router_big(E);
-  const int64_t tiles = big ? ((T + 127) / 128) * ((E + 127) / 128) : ((T + 63) / 64) * ((E + 63) / 64);
-  const int64_t target = big ? 256 : 512;
-  int ks = (int)std::min<int64_t>(RT_MAX_KS, std::max<int64_t>(1, target / std::max<int64_t>(tiles, 1)));
-  while (ks > 1 && d / 64 / ks < 8) --ks;
-  return ks;
-}
-
-// ----------------------------------------------------------------------------
-// One wavefront per token: softmax statistics, top-k (ties to the lower id),
-// ascending-id output order, renormalised gates.
 template <int VPL, bool SPLIT>
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float* __restrict__ logits, int KS, const float* __restrict__ bias, int64_t T, int E,
     int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate) {
-  const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  // logit = ((plane 0 + plane 1) + ...) + bias, every lane for its experts lane + 64 i.
-  // With K split (SPLIT, KS <= RT_MAX_KS planes), all planes' loads are issued before
-  // the first addition: a loop over the runtime plane count waited for each load in turn
-  // (2,048 tokens, 8 planes: 20.4 -> 17.1 us).  A separate instantiation, so that the
-  // single-plane launches keep their few registers and their occupancy.
-  float lv[VPL];
-  if constexpr (!SPLIT) {
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int e = min(lane + 64 * i, E - 1);
-      lv[i] = logits[t * E + e] + (bias ? bias[e] : 0.f);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int e = min(lane + 64 * i, E - 1);
-      float part[RT_MAX_KS];
-#pragma unroll
-      for (int zz = 0; zz < RT_MAX_KS; ++zz)
-        part[zz] = zz < KS ? logits[((int64_t)zz * T + t) * E + e] : 0.f;
-      float v = part[0];
-#pragma unroll
-      for (int zz = 1; zz < RT_MAX_KS; ++zz)
-        if (zz < KS) v += part[zz];
-      lv[i] = v + (bias ? bias[e] : 0.f);
-    }
-  }
-  int choice, rank;
-  float gate;
-  wave_route_row_f<VPL>([&](int e) { return lv[(e - lane) >> 6]; }, E, k, choice, rank, gate);
-  if (lane < k) {
-    topk_idx[t * k + rank] = choice;
-    topk_gate[t * k + rank] = gate;
-  }
+  route_token<VPL, SPLIT>(logits, KS, bias, T, E, k, t, topk_idx, topk_gate);
 }
 
 // ----------------------------------------------------------------------------
@@ -389,11 +230,6 @@ __global__ __launch_bounds__(1024) void expert_count_kernel(const int32_t* __res
   for (int e = threadIdx.x; e < E; e += blockDim.x) count[e] = hist[e];
 }
 
-// workspace: KS partial planes of the logits [KS, T, E] f32, then the three bf16
-// planes of W_r [3, E, d] (bf16 tokens)
-static size_t logits_bytes(int64_t T, int E, int d) {
-  return ((size_t)router_ksplit(T, E, d) * T * E * sizeof(float) + 255) & ~(size_t)255;
-}
 size_t route_workspace_bytes(int64_t T, int E, int d) {
   return logits_bytes(T, E, d) + (size_t)3 * E * d * 2;
 }
