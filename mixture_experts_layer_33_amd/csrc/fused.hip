@@ -18,6 +18,16 @@
 // same results up to fp32 rounding order).  Nothing is accumulated across workgroups:
 // the result does not depend on the schedule.
 //
+// Measured (2,048 tokens, d 7168, 256 experts, one MI355X, per-phase timestamps of every
+// workgroup): 4.16 ms per call against 3.89 ms for the separate kernels.  The GEMM phases
+// take the time of the separate GEMMs (2.29 | 1.34 ms of work per workgroup); each grid
+// barrier costs about 15 us from the last arrival to the release (the arriving
+// workgroup's L2 write-back, which cross-XCD visibility needs, is on the critical path),
+// eight of them about 0.12 ms.  Earlier forms: an acquire load in the polling loop
+// invalidated the caches at every poll (about 30 us per barrier); a fixed assignment of
+// GEMM tiles to workgroups ended each GEMM phase 0.2 ms after its median workgroup; one
+// token per workgroup in the copy and combine phases was latency-bound (2x slower).
+//
 // Grid barrier: a 64-bit ticket counter in the workspace, never reset.  A workgroup takes
 // ticket i = old value of the counter and waits until the counter reaches
 // (i / G + 1) G (G workgroups), so the counter only grows and is consistent from call to
@@ -68,16 +78,22 @@ struct FusedArgs {
   // the two grouped GEMMs (tile list, H, ring_y and saved A|U inside)
   GemmArgs g1, g2;
   int grid1, grid2;      // workgroup counts the separate GEMM launches would use
-  // grid barrier
+  // grid barrier and the GEMM phases' per-XCD tile counters [2][8]
+  uint32_t* queue;
   unsigned long long* ticket;
   uint32_t* status;
   uint32_t spin_limit;
 };
 
-// Returns false (in every thread of the workgroup) when the wait gave up.
+// Returns false (in every thread of the workgroup) when the wait gave up.  Every wave's
+// stores reach L2 before the workgroup arrives; thread 0's release (an L2 write-back)
+// then publishes them device-wide, and its acquire after the wait (an invalidation of
+// this CU's L1 and the XCD's L2 lines) covers every wave of the workgroup, which all
+// run on this CU.  The wait polls with relaxed loads: an acquire in the loop would
+// invalidate the caches at every poll (about 30 us per barrier, and slower workgroups
+// still computing lose their cached lines).
 __device__ __forceinline__ bool grid_sync(const FusedArgs a, volatile int* ok) {
-  // every thread's stores are made visible device-wide before the arrival
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned long long G = gridDim.x;
@@ -86,21 +102,100 @@ __device__ __forceinline__ bool grid_sync(const FusedArgs a, volatile int* ok) {
     const unsigned long long target = (i / G + 1) * G;
     uint32_t polls = 0;
     int passed = 1;
-    while (__hip_atomic_load(a.ticket, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (__hip_atomic_load(a.ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       if (++polls > a.spin_limit) {
         __hip_atomic_fetch_or(a.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         passed = 0;
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     *ok = passed;
   }
   __syncthreads();
-  const bool pass = *ok != 0;
-  // no thread of this workgroup reads lines cached before the other workgroups' stores
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return pass;
+  return *ok != 0;
+}
+
+// The next place of XCD x (workgroup places x, x + 8, x + 16, ... run there) in a GEMM
+// phase, from the XCD's own counter: tiles go to whichever of the XCD's workgroups is
+// free, in the order the hardware dispatcher hands a separate launch's workgroups to that
+// XCD, so a phase ends when the last tile does rather than when the workgroup with the
+// most work does.  Each tile is still computed by exactly one workgroup with its fixed K
+// order: the results do not depend on the order of claims.
+__device__ __forceinline__ int claim_place(uint32_t* queue, int x, volatile int* slot) {
+  if (threadIdx.x == 0)
+    *slot = (int)__hip_atomic_fetch_add(queue + x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int li = *slot;
+  __syncthreads();
+  return li * 8 + x;
+}
+
+// P5 for one token per wavefront: the copy_slots and row copy of dispatch_copy_token with
+// the k slots held by lanes j < k (shuffled to every lane), the same stores.
+__device__ __forceinline__ void fused_copy_token(const FusedArgs a, int64_t t) {
+  const int lane = threadIdx.x & 63, k = a.k, E = a.E;
+  int64_t s = 0;
+  if (lane < k) {
+    const int64_t chunk = t / DCH;
+    const int lc = (int)(t % DCH);
+    const int e = a.topk_idx[t * k + lane];
+    const unsigned long long mk = a.masks[chunk * E + e];
+    const int64_t rank = a.base[chunk * E + e] + __popcll(mk & ((1ull << lc) - 1ull));
+    s = a.head + rank;
+    if (s >= a.C) s -= a.C;
+    a.copy_slot[t * k + lane] = (int32_t)s;
+    a.slot_copy[s] = (int32_t)(t * k + lane);
+  }
+  const int64_t row_bytes = (int64_t)a.d * 2, nv = row_bytes / 16;
+  const u32x4* src = (const u32x4*)((const uint8_t*)a.x + t * row_bytes);
+  for (int64_t v = lane; v < nv; v += 64) {
+    const u32x4 val = __builtin_nontemporal_load(src + v);
+    for (int j = 0; j < k; ++j) {
+      const int64_t sj = __shfl(s, j, 64);
+      __builtin_nontemporal_store(val, (u32x4*)(a.ring_x + sj * row_bytes) + v);
+    }
+  }
+}
+
+// P8 for one token per wavefront: combine_token's sum, element by element the same
+// operations in the same order (gates and slots of lanes j < k shuffled to every lane).
+__device__ __forceinline__ void fused_combine_token(const FusedArgs a, int64_t t) {
+  const int lane = threadIdx.x & 63, k = a.k, d = a.d;
+  int64_t sl = 0;
+  float gl = 0.f;
+  if (lane < k) {
+    sl = a.copy_slot[t * k + lane];
+    gl = a.topk_gate[t * k + lane];
+  }
+  const bf16_t* ring_y = (const bf16_t*)a.g2.out;
+  for (int v = lane; v < d / 8; v += 64) {
+    float acc[8] = {};
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      u32x4 w[8];
+      float g[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {   // copies past k reload the last row, unused
+        const int j = min(j0 + jj, k - 1);
+        const int64_t s = __shfl(sl, j, 64);
+        g[jj] = __shfl(gl, j, 64);
+        w[jj] = __builtin_nontemporal_load((const u32x4*)(ring_y + s * d) + v);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (j0 + jj >= k) break;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(g[jj], lo_bf(w[jj][q]), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(g[jj], hi_bf(w[jj][q]), acc[2 * q + 1]);
+        }
+      }
+    }
+    ((u32x4*)(a.y + t * d))[v] =
+        u32x4{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3]), pack_bf2(acc[4], acc[5]),
+              pack_bf2(acc[6], acc[7])};
+  }
 }
 
 // P4, workgroup 0 alone: per-expert totals (expert_count), exclusive offsets, the chunk
@@ -188,6 +283,7 @@ __device__ __forceinline__ void fused_scan_tiles(const FusedArgs a, uint8_t* lds
     }
     if (e == 1023) *const_cast<int32_t*>(a.g1.ntiles) = sc[1023];
   }
+  if (tid < 16) a.queue[tid] = 0u;   // the GEMM phases' tile counters, 8 XCDs each
 }
 
 template <bool SPLIT>
@@ -247,36 +343,38 @@ __global__ __launch_bounds__(FU_NT) void fused_forward_kernel(FusedArgs a) {
   if (b == 0) fused_scan_tiles(a, lds);
   if (!grid_sync(a, ok)) return;
 
-  // P5: token rows into their ring slots
-  for (int64_t t = b; t < a.T; t += G) {
-    dispatch_copy_token((const uint8_t*)a.x, a.topk_idx, a.masks, a.base, a.k, a.E, a.head, a.C,
-                        (int64_t)a.d * 2, a.ring_x, a.copy_slot, a.slot_copy, t, (int64_t*)lds);
-    __syncthreads();
+  // P5: token rows into their ring slots, one token per wavefront
+  {
+    const int nw = FU_NT / 64;
+    for (int64_t t = (int64_t)b * nw + (tid >> 6); t < a.T; t += (int64_t)G * nw) fused_copy_token(a, t);
   }
   if (!grid_sync(a, ok)) return;
 
-  // P6, P7: the grouped GEMMs; workgroup b takes the grid places b, b + G, ... of the
-  // separate launch (same XCD, b % 8, since G is a multiple of 8)
-  for (int vb = b; vb < a.grid1; vb += G) {
+  // P6, P7: the grouped GEMMs; workgroup b (on XCD b % 8, G being a multiple of 8) takes
+  // its XCD's next place of the separate launch's grid until they run out
+  __shared__ int place[1];
+  for (int vb = claim_place(a.queue, b & 7, place); vb < a.grid1; vb = claim_place(a.queue, b & 7, place)) {
     gg_mfma_body<FU_BM, 256, 2, 4, 128, true, false, 3, POL>(a.g1, vb, lds);
     __syncthreads();
   }
   if (!grid_sync(a, ok)) return;
-  for (int vb = b; vb < a.grid2; vb += G) {
+  for (int vb = claim_place(a.queue + 8, b & 7, place); vb < a.grid2;
+       vb = claim_place(a.queue + 8, b & 7, place)) {
     gg_mfma_body<FU_BM, 256, 2, 4, 128, false, false, 3, POL>(a.g2, vb, lds);
     __syncthreads();
   }
   if (!grid_sync(a, ok)) return;
 
-  // P8: y[t] = sum_j g[t, j] ring_y[copy_slot[t, j]], ascending expert order
-  for (int64_t t = b; t < a.T; t += G) {
-    combine_token<false>(a.g2.out, a.copy_slot, a.topk_gate, a.d, a.k, a.y, t, (int64_t*)lds,
-                         (float*)(lds + 512));
-    __syncthreads();
+  // P8: y[t] = sum_j g[t, j] ring_y[copy_slot[t, j]], ascending expert order, one token
+  // per wavefront
+  {
+    const int nw = FU_NT / 64;
+    for (int64_t t = (int64_t)b * nw + (tid >> 6); t < a.T; t += (int64_t)G * nw) fused_combine_token(a, t);
   }
 }
 
-// Workspace: [0, 256) ticket counter (8 bytes) and status word (at byte 8) | W_r planes |
+// Workspace: [0, 256) ticket counter (8 bytes), status word (at byte 8), the GEMM phases'
+// tile counters (16 words at byte 64, reset inside every call) | W_r planes |
 // logit planes | chunk masks | chunk counts/bases | tile list | H.
 struct FusedLayout {
   size_t w3, logits, masks, base, tiles, H, total;
@@ -367,6 +465,7 @@ hipError_t launch_forward_fused(const void* x, const float* w_r, const float* b_
   a.grid1 = (int)(8 * (((int64_t)max_tiles * nt1 + 7) / 8));
   a.grid2 = (int)(8 * (((int64_t)max_tiles * nt2 + 7) / 8));
   a.ticket = (unsigned long long*)w;
+  a.queue = (uint32_t*)(w + 64);
   a.status = (uint32_t*)(w + 8);
   a.spin_limit = spin_limit ? spin_limit : (1u << 22);
 
