@@ -419,3 +419,82 @@ def max_abs_rel(got: np.ndarray, ref: np.ndarray) -> float:
     den = np.max(np.abs(ref))
     err = np.max(np.abs(np.asarray(got, dtype=np.float64) - ref)) if ref.size else 0.0
     return float(err / den) if den > 0 else float(err)
+
+
+# --------------------------------------------------------------------------- O6 MXFP8 backward
+#
+# The pages report the layer's MXFP8 backward (dzen.guru page, "Что показали замеры?") without
+# its recipe.  Reading: each backward GEMM takes its two operands MX-quantised (E4M3, one E8M0
+# scale per 32) along that GEMM's own reduction dimension, products accumulated exactly (fp64
+# here), everything elementwise unquantised; the forward's quantisation is the identity in
+# the backward (straight-through), and A, U are the MX forward's:
+#   A = Q_d(X) Q_d(W_gate)^T,  U = Q_d(X) Q_d(W_up)^T,  H = silu(A) U
+#   dH_raw = Q_d(dY) Q_d(W_down)          W_down [d, f] quantised along d (its columns)
+#   dg = <dH_raw, H>;  dA, dU as in the bf16 backward
+#   dX_c = Q_f(dA) Q_f(W_gate) + Q_f(dU) Q_f(W_up)     W_gate, W_up [f, d] along f
+#   dW_down = Q_t(dY)^T Q_t(g H),  dW_gate = Q_t(dA)^T Q_t(X),  dW_up = Q_t(dU)^T Q_t(X)
+# Q_t quantises along the token axis: an expert's copies in ring-segment order (ascending
+# token), in blocks of 32 aligned to the segment's end (the first block is the partial one:
+# the backward walks the ring last slot first).  The router part is the bf16 backward's.
+
+
+def token_quant(M: np.ndarray) -> np.ndarray:
+    """MX round trip of the rows of M (an expert's copies in segment order) along the row
+    axis, blocks of 32 rows aligned to the last row (zero rows pad the first block)."""
+    n = M.shape[0]
+    pad = (-n) % mx.BLOCK
+    P = np.concatenate([np.zeros((pad,) + M.shape[1:]), M], axis=0)
+    return mx.fake_quant(P, axis=0)[pad:]
+
+
+def expert_backward_mx(e: int, x: np.ndarray, dy: np.ndarray, routing: Routing,
+                       weights: Weights, disp: Dispatch) -> ExpertGrad:
+    """Gradients through expert e in the MXFP8 layer (weights: the bf16 weights in fp64)."""
+    k = routing.idx.shape[1]
+    copies = disp.slot_copy[segment_slots(disp, e)]      # ring-segment order
+    ts, js = copies // k, copies % k
+    wg, wu, wd = weights(e)
+    f, d = wg.shape
+    if ts.size == 0:
+        z = np.zeros
+        return ExpertGrad(z((f, d)), z((f, d)), z((d, f)), ts, js, z(0), z((0, d)))
+    X = x[ts]
+    g = routing.gate[ts, js]
+    Xq = mx.fake_quant(X, axis=1)
+    A = Xq @ mx.fake_quant(wg, axis=1).T
+    U = Xq @ mx.fake_quant(wu, axis=1).T
+    s = sigmoid(A)
+    H = A * s * U
+    dY = dy[ts]
+    dHraw = mx.fake_quant(dY, axis=1) @ mx.fake_quant(wd, axis=0)
+    dg = np.sum(dHraw * H, axis=1)
+    dH = g[:, None] * dHraw
+    dA = dH * U * s * (1.0 + A * (1.0 - s))
+    dU = dH * A * s
+    dxc = (mx.fake_quant(dA, axis=1) @ mx.fake_quant(wg, axis=0)
+           + mx.fake_quant(dU, axis=1) @ mx.fake_quant(wu, axis=0))
+    Xt = token_quant(X)
+    return ExpertGrad(token_quant(dA).T @ Xt, token_quant(dU).T @ Xt,
+                      token_quant(dY).T @ token_quant(g[:, None] * H), ts, js, dg, dxc)
+
+
+def backward_mx(x: np.ndarray, w_r: np.ndarray, routing: Routing, weights: Weights,
+                dy: np.ndarray, disp: Dispatch) -> Backward:
+    """The MXFP8 layer's backward of L = sum_t <dy_t, y_t> (S fixed, b a constant)."""
+    T, d = x.shape
+    E, k = w_r.shape[0], routing.idx.shape[1]
+    dx = np.zeros((T, d))
+    dg = np.zeros((T, k))
+    grads = []
+    for e in range(E):
+        eg = expert_backward_mx(e, x, dy, routing, weights, disp)
+        grads.append(eg)
+        dg[eg.tokens, eg.js] = eg.dg
+        np.add.at(dx, eg.tokens, eg.dx)
+    dl = router_logit_grad(routing.gate, dg)
+    dw_r = np.zeros((E, d))
+    for j in range(k):
+        np.add.at(dw_r, routing.idx[:, j], dl[:, j, None] * x)
+        dx += dl[:, j, None] * w_r[routing.idx[:, j]]
+    return Backward(dx, np.stack([g.dw_gate for g in grads]), np.stack([g.dw_up for g in grads]),
+                    np.stack([g.dw_down for g in grads]), dw_r, dg, dl)

@@ -105,8 +105,17 @@ def check_shared(mod):
     shared_brute_check(mod)
 
 
+def check_mx_backward(mod):
+    from test_oracle_pins import mx_backward_check
+    mx_backward_check(mod)
+    M = np.zeros((40, 32))
+    M[:, 0] = 0.0013
+    M[39, 0] = 32.0
+    assert mod.token_quant(M)[8, 0] == 5 * 2.0 ** -12
+
+
 MOE_CHECKS = [check_brute, check_dispatch, check_closed_forms, check_autograd, check_mx_wiring,
-              check_shared]
+              check_shared, check_mx_backward]
 
 MOE_MUTATIONS = [
     ("silu sign", "H = A * sigmoid(A) * U", "H = A * sigmoid(-A) * U"),
@@ -134,6 +143,21 @@ MOE_MUTATIONS = [
     ("shared expert gated in forward", "y = y + swiglu(x, *shared)", "y = y + r.gate[:, :1] * swiglu(x, *shared)"),
     ("shared expert halved in forward_tokens", "y += swiglu(xs, *shared)", "y += 0.5 * swiglu(xs, *shared)"),
     ("shared expert dropped in forward_tokens", "y += swiglu(xs, *shared)", "pass"),
+    ("MX bwd: dY not quantised", "dHraw = mx.fake_quant(dY, axis=1) @", "dHraw = dY @"),
+    ("MX bwd: W_down quantised along f", "@ mx.fake_quant(wd, axis=0)", "@ mx.fake_quant(wd, axis=1)"),
+    ("MX bwd: dA not quantised", "dxc = (mx.fake_quant(dA, axis=1) @", "dxc = (dA @"),
+    ("MX bwd: W_gate quantised along d", "mx.fake_quant(dA, axis=1) @ mx.fake_quant(wg, axis=0)",
+     "mx.fake_quant(dA, axis=1) @ mx.fake_quant(wg, axis=1)"),
+    ("MX bwd: dU paired with W_gate", "+ mx.fake_quant(dU, axis=1) @ mx.fake_quant(wu, axis=0)",
+     "+ mx.fake_quant(dU, axis=1) @ mx.fake_quant(wg, axis=0)"),
+    ("MX bwd: token blocks aligned to the start",
+     "P = np.concatenate([np.zeros((pad,) + M.shape[1:]), M], axis=0)\n    return mx.fake_quant(P, axis=0)[pad:]",
+     "P = np.concatenate([M, np.zeros((pad,) + M.shape[1:])], axis=0)\n    return mx.fake_quant(P, axis=0)[:n]"),
+    ("MX bwd: gH not token-quantised", "token_quant(g[:, None] * H)", "(g[:, None] * H)"),
+    ("MX bwd: X not token-quantised", "Xt = token_quant(X)", "Xt = X"),
+    ("MX bwd: A from unquantised x", "A = Xq @ mx.fake_quant(wg, axis=1).T", "A = X @ mx.fake_quant(wg, axis=1).T"),
+    ("MX bwd: copies in token order, not ring order", "copies = disp.slot_copy[segment_slots(disp, e)]",
+     "copies = np.sort(disp.slot_copy[segment_slots(disp, e)])[::-1]"),
 ]
 
 

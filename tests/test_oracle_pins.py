@@ -558,3 +558,108 @@ def test_shared_expert_against_brute_force():
 
 def test_mx_layer_against_torch_float8():
     torch_mx_check(oracle.moe)
+
+
+# ----------------------------------------------------------------- MXFP8 backward
+
+
+def torch_token_quant(M):
+    """MX round trip along the row axis with blocks aligned to the last row, written as: flip
+    the rows, quantise blocks of 32 from the (new) top with the last block partial, flip back."""
+    t = torch.from_numpy(np.ascontiguousarray(M[::-1]))
+    n = t.shape[0]
+    out = torch.empty_like(t)
+    for r0 in range(0, n, 32):
+        blk = t[r0:r0 + 32]
+        full = torch.zeros((32,) + tuple(blk.shape[1:]), dtype=blk.dtype)
+        full[: blk.shape[0]] = blk
+        out[r0:r0 + 32] = torch.from_numpy(torch_mx_fake_quant(full.numpy(), axis=0))[: blk.shape[0]]
+    return out.numpy()[::-1].copy()
+
+
+def torch_mx_backward(x, w_r, b, k, wg, wu, wd, dy):
+    """The MXFP8 layer's backward written out per token and per expert with torch's E4M3 cast:
+    the routing from a library argsort, each expert's copies listed by scanning tokens."""
+    T, d = x.shape
+    E = w_r.shape[0]
+    l = x @ w_r.T + (0 if b is None else b)
+    S = np.sort(np.argsort(-l, axis=1, kind="stable")[:, :k], axis=1)
+    q = lambda v, ax: torch_mx_fake_quant(v, axis=ax)
+    dx = np.zeros((T, d))
+    dg = np.zeros((T, k))
+    dwg, dwu, dwd = np.zeros_like(wg), np.zeros_like(wu), np.zeros_like(wd)
+    for e in range(E):
+        ts = [t for t in range(T) if e in S[t]]
+        if not ts:
+            continue
+        js = [int(np.nonzero(S[t] == e)[0][0]) for t in ts]
+        rows = {"dA": [], "dU": [], "X": [], "dY": [], "gH": []}
+        for t, j in zip(ts, js):
+            lS = l[t, S[t]]
+            g = np.exp(lS[j] - lS.max()) / np.exp(lS - lS.max()).sum()
+            xq = q(x[t][None, :], 1)[0]
+            a = q(wg[e], 1) @ xq
+            u = q(wu[e], 1) @ xq
+            sg = torch.sigmoid(torch.from_numpy(a)).numpy()
+            h = a * sg * u
+            dhr = q(dy[t][None, :], 1)[0] @ q(wd[e], 0)
+            dg[t, j] = dhr @ h
+            da = g * dhr * u * sg * (1 + a * (1 - sg))
+            du = g * dhr * a * sg
+            dx[t] += q(da[None, :], 1)[0] @ q(wg[e], 0) + q(du[None, :], 1)[0] @ q(wu[e], 0)
+            for nm, v in (("dA", da), ("dU", du), ("X", x[t]), ("dY", dy[t]), ("gH", g * h)):
+                rows[nm].append(v)
+        R = {nm: torch_token_quant(np.array(v)) for nm, v in rows.items()}
+        dwg[e], dwu[e] = R["dA"].T @ R["X"], R["dU"].T @ R["X"]
+        dwd[e] = R["dY"].T @ R["gH"]
+    gate = np.stack([np.exp(l[t, S[t]] - l[t, S[t]].max()) / np.exp(l[t, S[t]] - l[t, S[t]].max()).sum()
+                     for t in range(T)])
+    dl = gate * (dg - (gate * dg).sum(axis=1, keepdims=True))
+    dwr = np.zeros_like(w_r)
+    for t in range(T):
+        for j in range(k):
+            dwr[S[t, j]] += dl[t, j] * x[t]
+            dx[t] += dl[t, j] * w_r[S[t, j]]
+    return dx, dwg, dwu, dwd, dwr
+
+
+def mx_backward_check(mod):
+    """The oracle's MXFP8 backward against the torch formulation: 3 experts with 40-50 copies
+    each (partial first token blocks), a bias, a wrapping ring head."""
+    rng = np.random.default_rng(18)
+    T, d, E, k, f = 70, 64, 3, 2, 64
+    x, w_r, b, wg, wu, wd = rand_layer(rng, T, d, E, k, f, bias=True)
+    dy = rng.standard_normal((T, d))
+    r = mod.route(x, w_r, b, k)
+    C = T * k + 5
+    disp = mod.dispatch(r.idx, E, C, head=C - 9)
+    assert all(n % 32 and n > 32 for n in r.count)
+    bw = mod.backward_mx(x, w_r, r, mod.weights_from_arrays(wg, wu, wd), dy, disp)
+    ref = torch_mx_backward(x, w_r, b, k, wg, wu, wd, dy)
+    for got, want in zip((bw.dx, bw.dw_gate, bw.dw_up, bw.dw_down, bw.dw_router), ref):
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12 * np.abs(want).max())
+
+
+def test_mx_backward_against_torch_float8():
+    mx_backward_check(oracle.moe)
+
+
+def test_token_quant_end_alignment():
+    """Blocks of 32 rows aligned to the last row: with 40 rows, rows 8..39 form one block
+    whose amax is set by row 39 (2^5 -> X = -3), rows 0..7 a partial block (amax 1 -> X = -8)."""
+    M = np.zeros((40, 32))
+    M[:, 0] = 1.1          # not MX-representable at X = -3 (1.1 * 8 = 8.8 -> 9 -> 1.125)
+    M[39, 0] = 32.0
+    Q = oracle.token_quant(M)
+    assert Q[39, 0] == 32.0 and Q[8, 0] == 1.125 and Q[38, 0] == 1.125
+    # the partial first block, amax 1.1: X = -8, 1.1 * 256 = 281.6 -> 288 -> 1.125
+    assert Q[0, 0] == 1.125 and Q[7, 0] == 1.125
+    # a value far below its block's maximum is subnormal there: 0.0013 in the block of 32.0
+    # (X = -3): 0.0013 * 8 = 0.0104 -> 5 steps of 2^-9 -> 5 * 2^-12; in the partial block
+    # of 0.0013 alone (X = floor(log2 0.0013) - 8 = -18): 340.8 -> 352 -> 352 * 2^-18.
+    # Blocks aligned to the start would put row 8 with rows 0..31 (the second value).
+    M[:, 0] = 0.0013
+    M[39, 0] = 32.0
+    Q = oracle.token_quant(M)
+    assert Q[8, 0] == 5 * 2.0 ** -12 and Q[38, 0] == 5 * 2.0 ** -12
+    assert Q[0, 0] == 352 * 2.0 ** -18 and Q[7, 0] == 352 * 2.0 ** -18
