@@ -139,7 +139,8 @@ int moe_dispatch(const moe_shape* shape, const void* x, const int32_t* topk_idx,
  *      moe_quantize_mx writes them for the [E*f, d] and [E*d, f] matrices.
  * Out: ring_y [C,d] (bf16; fp32 for MOE_F32) at the segment slots;
  *      saved_au [C,2f] bf16 (A then U per slot) when not NULL — the backward's input
- *      (MOE_BF16 only; must be NULL otherwise).
+ *      (MOE_BF16 and MOE_MXFP8: the gate/up fp32 accumulations rounded to bf16; NULL for
+ *      MOE_F32).
  * workspace: moe_workspace_bytes(shape, MOE_OP_EXPERT_FFN) bytes.
  */
 int moe_expert_ffn(const moe_shape* shape, const void* ring_x, const uint8_t* ring_x_scale,
@@ -260,8 +261,9 @@ int moe_decode_noalloc(const moe_shape* shape, const void* x, const float* w_rou
  *      moe_expert_ffn; w_gate, w_up, w_down bf16.
  * Out: dx [T,d] bf16; dw_gate, dw_up [E,f,d] bf16; dw_down [E,d,f] bf16 (zero for
  *      experts with no rows); dw_router [E,d] f32.
- * workspace: moe_workspace_bytes(shape, MOE_OP_BACKWARD) bytes.  MOE_BF16 only; d and f
- * must be multiples of 128 (MOE_ERR_SHAPE otherwise).
+ * workspace: moe_workspace_bytes(shape, MOE_OP_BACKWARD) bytes.  MOE_BF16 only (the MXFP8
+ * layer's backward is moe_backward_mx); d and f must be multiples of 128 (MOE_ERR_SHAPE
+ * otherwise).
  */
 int moe_backward(const moe_shape* shape, const void* dy, const void* x,
                  const float* w_router, const int32_t* topk_idx, const float* topk_gate,
@@ -275,6 +277,37 @@ int moe_backward(const moe_shape* shape, const void* dy, const void* x,
  * a call would return; includes: every ring array the MFMA GEMMs address, C * d and
  * C * f elements of bf16 or E4M3, must stay below 4 GiB).  Host only, no GPU call. */
 int moe_check_shape(const moe_shape* shape);
+
+/*
+ * moe_backward_mx: the MXFP8 layer's backward (the MXFP8 backward of the dzen.guru page,
+ * "Что показали замеры?").  The gradients of moe_backward, with every backward GEMM's two
+ * operands MX-quantised (E4M3, one E8M0 scale per 32) along that GEMM's reduction
+ * dimension and fp32 accumulation; the forward's quantisation counts as the identity:
+ *   dh = Q_d(W_down)^T Q_d(dy_t)        (W_down quantised along d, i.e. transposed)
+ *   dx_t += Q_f(W_gate)^T Q_f(da) + Q_f(W_up)^T Q_f(du)   (weights along f)
+ *   dW_down[e] = Q_t(dY_e)^T Q_t(g H_e),  dW_gate[e] = Q_t(dA_e)^T Q_t(X_e),
+ *   dW_up[e] = Q_t(dU_e)^T Q_t(X_e)
+ * Q_t: along the token axis, each expert's copies in ring-segment order in blocks of 32
+ * aligned to the segment's last slot (the first block partial).  dg, da, du, the router
+ * gradient and dx's router term as in moe_backward; saved_au from the MXFP8 forward's
+ * moe_expert_ffn.
+ * In:  dy, x [T,d] bf16; w_router; topk_idx, topk_gate; expert_offset, copy_slot,
+ *      slot_copy, ring_head from moe_dispatch; saved_au [C,2f] bf16;
+ *      w_gu_t [E,d,2f] E4M3 = [W_gate^T | W_up^T] of every expert quantised along f, scales
+ *      w_gu_t_scale [2f/128][E*d][4]; w_down_t [E,f,d] = W_down^T quantised along d,
+ *      scales w_down_t_scale [d/128][E*f][4] (both as moe_quantize_mx_t writes them).
+ * Out: dx [T,d] bf16; dw_gate, dw_up [E,f,d] and dw_down [E,d,f] bf16; dw_router [E,d] f32.
+ * workspace: moe_workspace_bytes(shape with dtype MOE_MXFP8, MOE_OP_BACKWARD) bytes.
+ * MOE_MXFP8 only; d and f multiples of 128.
+ */
+int moe_backward_mx(const moe_shape* shape, const void* dy, const void* x,
+                    const float* w_router, const int32_t* topk_idx, const float* topk_gate,
+                    const int32_t* expert_offset, const int32_t* copy_slot,
+                    const int32_t* slot_copy, int64_t ring_head, const void* saved_au,
+                    const uint8_t* w_gu_t, const uint8_t* w_gu_t_scale, const uint8_t* w_down_t,
+                    const uint8_t* w_down_t_scale, void* dx, void* dw_gate, void* dw_up,
+                    void* dw_down, float* dw_router, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
 
 /* Bytes of workspace `op` needs for `shape` (0 if none).  Host only, no GPU call. */
 size_t moe_workspace_bytes(const moe_shape* shape, int op);
@@ -291,6 +324,18 @@ const char* moe_status_string(int status);
  */
 int moe_quantize_mx(const void* src_bf16, int64_t rows, int64_t cols, uint8_t* codes,
                     uint8_t* scales, hipStream_t stream);
+
+/*
+ * moe_quantize_mx_t: MX-quantise `batch` bf16 matrices [rows, cols] (src [batch, rows, cols])
+ * along their rows and write them transposed: source column c of matrix b becomes row
+ * b*cols + c of a code matrix with rows of ld bytes, its values in columns col0 .. col0 +
+ * rows - 1; scales in that code matrix's layout [ld/128][batch*cols][4].  The MXFP8
+ * backward's weights: W_down [E,d,f] -> (E, d, f, ld = d, col0 = 0); W_gate and W_up [E,f,d]
+ * -> (E, f, d, ld = 2f, col0 = 0 and f).  rows % 32 == 0, ld % 128 == 0, col0 % 32 == 0.
+ */
+int moe_quantize_mx_t(const void* src_bf16, int64_t batch, int64_t rows, int64_t cols,
+                      uint8_t* codes, int64_t ld, int64_t col0, uint8_t* scales,
+                      hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,8 @@ from ._lib import (DTYPES, MOE_BF16, MOE_F32, MOE_MXFP8, OP_BACKWARD, OP_COMBINE
 
 __all__ = ["make_shape", "check_shape", "workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn",
            "moe_expert_ffn_timed",
-           "moe_combine", "moe_forward", "moe_decode", "moe_backward", "moe_quantize_mx", "Layer",
+           "moe_combine", "moe_forward", "moe_decode", "moe_backward", "moe_backward_mx",
+           "moe_quantize_mx", "quantize_mx_t_backward_weights", "Layer",
            "MoeError",
            "LIB_PATH"]
 
@@ -130,6 +131,33 @@ def moe_backward(shape, dy, x, w_router, topk_idx, topk_gate, ring_x, expert_off
         _p(expert_offset), _p(copy_slot), _p(slot_copy), int(ring_head), _p(saved_au),
         _p(w_gate), _p(w_up), _p(w_down), _p(dx), _p(dw_gate), _p(dw_up), _p(dw_down),
         _p(dw_router), _p(ws), ws.numel(), _s(stream)))
+
+
+def moe_backward_mx(shape, dy, x, w_router, topk_idx, topk_gate, expert_offset, copy_slot,
+                    slot_copy, ring_head, saved_au, w_gu_t, w_gu_t_scale, w_down_t, w_down_t_scale,
+                    dx, dw_gate, dw_up, dw_down, dw_router, ws, stream=None):
+    check("moe_backward_mx", lib().moe_backward_mx(
+        shape, _p(dy), _p(x), _p(w_router), _p(topk_idx), _p(topk_gate), _p(expert_offset),
+        _p(copy_slot), _p(slot_copy), int(ring_head), _p(saved_au), _p(w_gu_t), _p(w_gu_t_scale),
+        _p(w_down_t), _p(w_down_t_scale), _p(dx), _p(dw_gate), _p(dw_up), _p(dw_down),
+        _p(dw_router), _p(ws), ws.numel(), _s(stream)))
+
+
+def quantize_mx_t_backward_weights(w_gate, w_up, w_down, stream=None):
+    """The MXFP8 backward's weights from the bf16 ones: (w_gu_t [E,d,2f], its scales,
+    w_down_t [E,f,d], its scales), via moe_quantize_mx_t."""
+    E, f, d = w_gate.shape
+    dev = w_gate.device
+    gu = torch.empty((E, d, 2 * f), dtype=torch.uint8, device=dev)
+    gus = torch.empty((2 * f // 128, E * d, 4), dtype=torch.uint8, device=dev)
+    dn = torch.empty((E, f, d), dtype=torch.uint8, device=dev)
+    dns = torch.empty((d // 128, E * f, 4), dtype=torch.uint8, device=dev)
+    L = lib()
+    s = _s(stream)
+    check("moe_quantize_mx_t", L.moe_quantize_mx_t(_p(w_gate), E, f, d, _p(gu), 2 * f, 0, _p(gus), s))
+    check("moe_quantize_mx_t", L.moe_quantize_mx_t(_p(w_up), E, f, d, _p(gu), 2 * f, f, _p(gus), s))
+    check("moe_quantize_mx_t", L.moe_quantize_mx_t(_p(w_down), E, d, f, _p(dn), d, 0, _p(dns), s))
+    return gu, gus, dn, dns
 
 
 def moe_quantize_mx(src, codes, scales, stream=None):
@@ -258,6 +286,20 @@ class Layer:
         moe_decode(s, x, w_router, b_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y, idx,
                    gate, self._ws(OP_DECODE))
         return y, idx, gate
+
+    def backward_mx(self, dy, x, w_router, w_gu_t, w_gu_t_scale, w_down_t, w_down_t_scale, head=0):
+        """The MXFP8 layer's gradients after forward(..., save_au=True) with the same buffers."""
+        s = self.shape
+        b = self.bufs
+        dx = self._buf("dx", (s.tokens, s.hidden), torch.bfloat16)
+        dwg = self._buf("dw_gate", (s.experts, s.ffn, s.hidden), torch.bfloat16)
+        dwu = self._buf("dw_up", (s.experts, s.ffn, s.hidden), torch.bfloat16)
+        dwd = self._buf("dw_down", (s.experts, s.hidden, s.ffn), torch.bfloat16)
+        dwr = self._buf("dw_router", (s.experts, s.hidden), torch.float32)
+        moe_backward_mx(s, dy, x, w_router, b["topk_idx"], b["topk_gate"], b["expert_offset"],
+                        b["copy_slot"], b["slot_copy"], head, b["saved_au"], w_gu_t, w_gu_t_scale,
+                        w_down_t, w_down_t_scale, dx, dwg, dwu, dwd, dwr, self._ws(OP_BACKWARD))
+        return dx, dwg, dwu, dwd, dwr
 
     def backward(self, dy, x, w_router, w_gate, w_up, w_down, head=0):
         """Gradients after a forward(..., save_au=True) with the same buffers."""

@@ -83,6 +83,9 @@ size_t moe_workspace_bytes(const moe_shape* s, int op) {
                  ? align256(moe::fused_workspace_bytes(T, C, s->hidden, s->experts, s->ffn))
                  : 0;
     case MOE_OP_BACKWARD:
+      if (s->dtype == MOE_MXFP8)
+        return align256(moe::backward_mx_workspace_bytes(T, C, s->hidden, s->experts, s->top_k,
+                                                         s->ffn));
       return align256(moe::backward_workspace_bytes(T, C, s->hidden, s->experts, s->top_k,
                                                     s->ffn));
     default: return 0;
@@ -164,7 +167,7 @@ int moe_expert_ffn_timed(const moe_shape* s, const void* ring_x, const uint8_t* 
     const bool mx = s->dtype == MOE_MXFP8;
     if (mx && (!ring_x_scale || !w_gate_scale || !w_up_scale || !w_down_scale))
       return MOE_ERR_NULL;
-    if (saved_au && s->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (saved_au && s->dtype == MOE_F32) return MOE_ERR_DTYPE;
     if (ring_head < 0 || ring_head >= s->capacity) return MOE_ERR_SHAPE;
     if (workspace_bytes < moe_workspace_bytes(s, MOE_OP_EXPERT_FFN)) return MOE_ERR_WORKSPACE;
     if (s->tokens == 0) return MOE_OK;
@@ -327,6 +330,59 @@ int moe_backward(const moe_shape* s, const void* dy, const void* x, const float*
         dy, x, w_router, topk_idx, topk_gate, ring_x, expert_offset, copy_slot, slot_copy,
         ring_head, s->capacity, saved_au, w_gate, w_up, w_down, s->tokens, s->hidden, s->experts,
         s->top_k, s->ffn, dx, dw_gate, dw_up, dw_down, dw_router, workspace, stream));
+  } catch (...) {
+    return MOE_ERR_HIP;
+  }
+}
+
+int moe_backward_mx(const moe_shape* s, const void* dy, const void* x, const float* w_router,
+                    const int32_t* topk_idx, const float* topk_gate,
+                    const int32_t* expert_offset, const int32_t* copy_slot,
+                    const int32_t* slot_copy, int64_t ring_head, const void* saved_au,
+                    const uint8_t* w_gu_t, const uint8_t* w_gu_t_scale, const uint8_t* w_down_t,
+                    const uint8_t* w_down_t_scale, void* dx, void* dw_gate, void* dw_up,
+                    void* dw_down, float* dw_router, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  try {
+    int st = check_shape(s);
+    if (st) return st;
+    if (s->dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
+    if (s->hidden % 128 || s->ffn % 128) return MOE_ERR_SHAPE;
+    const int64_t T = s->tokens;
+    if (missing_tok(dy, T) || missing_tok(x, T) || !w_router || missing_tok(topk_idx, T) ||
+        missing_tok(topk_gate, T) || !expert_offset || missing_tok(copy_slot, T) || !slot_copy ||
+        !saved_au || !w_gu_t || !w_gu_t_scale || !w_down_t || !w_down_t_scale ||
+        missing_tok(dx, T) || !dw_gate || !dw_up || !dw_down || !dw_router || !workspace)
+      return MOE_ERR_NULL;
+    if (ring_head < 0 || ring_head >= s->capacity) return MOE_ERR_SHAPE;
+    if (workspace_bytes < moe_workspace_bytes(s, MOE_OP_BACKWARD)) return MOE_ERR_WORKSPACE;
+    if (T == 0) {
+      const size_t wbytes = (size_t)s->experts * s->ffn * s->hidden * 2;
+      hipError_t err = zero_words(dw_gate, wbytes / 4, stream);
+      if (err == hipSuccess) err = zero_words(dw_up, wbytes / 4, stream);
+      if (err == hipSuccess) err = zero_words(dw_down, wbytes / 4, stream);
+      if (err == hipSuccess) err = zero_words(dw_router, (size_t)s->experts * s->hidden, stream);
+      return hip_status(err);
+    }
+    return hip_status(moe::launch_backward_mx(
+        dy, x, w_router, topk_idx, topk_gate, expert_offset, copy_slot, slot_copy, ring_head,
+        s->capacity, saved_au, w_gu_t, w_gu_t_scale, w_down_t, w_down_t_scale, T, s->hidden,
+        s->experts, s->top_k, s->ffn, dx, dw_gate, dw_up, dw_down, dw_router, workspace, stream));
+  } catch (...) {
+    return MOE_ERR_HIP;
+  }
+}
+
+int moe_quantize_mx_t(const void* src_bf16, int64_t batch, int64_t rows, int64_t cols,
+                      uint8_t* codes, int64_t ld, int64_t col0, uint8_t* scales,
+                      hipStream_t stream) {
+  try {
+    if (!src_bf16 || !codes || !scales) return MOE_ERR_NULL;
+    if (batch < 0 || rows <= 0 || cols <= 0 || rows % 32 || ld % 128 || col0 < 0 || col0 % 32 ||
+        col0 + rows > ld)
+      return MOE_ERR_SHAPE;
+    return hip_status(moe::launch_quantize_mx_t(src_bf16, batch, rows, cols, codes, ld, col0,
+                                                scales, stream));
   } catch (...) {
     return MOE_ERR_HIP;
   }

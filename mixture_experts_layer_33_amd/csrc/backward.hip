@@ -25,6 +25,7 @@
 // read as MFMA fragments with transposing LDS reads, as are both operands of the
 // weight gradients.  No floating-point atomics: every sum has one fixed order.
 #include "common.h"
+#include "gemm_body.h"
 #include "kernels.h"
 
 namespace moe {
@@ -788,6 +789,348 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
   WgradArgs wu = wd;
   wu.A = dau;
   wu.B = (const bf16_t*)ring_x;
+  wu.M = 2 * f;
+  wu.N = d;
+  wu.msplit = f;
+  wu.lda = 2 * f;
+  wu.ldb = d;
+  wu.out0 = (bf16_t*)dw_gate;
+  wu.out1 = (bf16_t*)dw_up;
+  if ((err = run_wgrad(wu, st)) != hipSuccess) return err;
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- MXFP8 backward
+// The MXFP8 layer's backward: every GEMM takes its two operands MX-quantised (E4M3, one
+// E8M0 scale per 32) along its own reduction dimension, with fp32 accumulation; the
+// SwiGLU backward and the router part are the bf16 backward's.
+//   down dgrad     dH_raw = Q_d(dY) Q_d(W_down)     the MX grouped GEMM (gemm.hip) on dY
+//                  quantised along d into ring order and W_down^T quantised along d
+//                  (moe_quantize_mx_t); dH_raw in fp32
+//   SwiGLU bwd     per copy: dg (one fixed-order sum over f), dA, dU, g H in fp32, and dA|dU
+//                  quantised along f for the next GEMM
+//   gate/up dgrad  dX_c = [Q_f(dA) | Q_f(dU)] [Q_f(W_gate) ; Q_f(W_up)]: the same GEMM
+//                  with K = 2f over [W_gate^T | W_up^T] quantised along f
+//   wgrad          dW = Q_t(.)^T Q_t(.): each expert's ring rows quantised along the token
+//                  axis in blocks of 32 aligned to the segment's end (its last slot, where
+//                  the weight gradients start), decoded to bf16 (every MX value is a bf16
+//                  value), then the bf16 weight-gradient kernel above.  The products
+//                  are those of the MX operands; the token axis is these operands' row
+//                  axis, which the scaled MFMA (K along a lane's registers) cannot stream
+//                  without a transposed copy, and the kernel is bound by writing dW.
+
+// dy[t] MX-quantised along d (blocks of 32, 4 lanes each) into the k ring slots of its
+// copies: codes [C, d], scales [d/128][C][4].
+__global__ __launch_bounds__(256) void gather_mx_kernel(const bf16_t* __restrict__ src,
+                                                        const int32_t* __restrict__ copy_slot,
+                                                        int k, int d, int64_t C,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales) {
+  const int64_t t = blockIdx.x;
+  __shared__ int64_t slots[64];
+  if (threadIdx.x < k) slots[threadIdx.x] = copy_slot[t * k + threadIdx.x];
+  __syncthreads();
+  const int nv = d / 8;
+  const int iters = (nv + 255) / 256;   // uniform trip count: all lanes join the shuffles
+  for (int it = 0; it < iters; ++it) {
+    const int v = it * 256 + threadIdx.x;
+    const bool ok = v < nv;
+    const u32x4 w = ok ? ((const u32x4*)(src + t * d))[v] : u32x4{0, 0, 0, 0};
+    float fv[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { fv[2 * q] = lo_bf(w[q]); fv[2 * q + 1] = hi_bf(w[q]); }
+    float am = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(fv[q]));
+    am = group_max<4>(am);
+    const int X = mx_block_exp(am);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lo |= e4m3_encode(fv[q], X) << (8 * q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hi |= e4m3_encode(fv[4 + q], X) << (8 * q);
+    if (ok)
+      for (int j = 0; j < k; ++j) {
+        *(u32x2*)(codes + slots[j] * d + (int64_t)v * 8) = u32x2{lo, hi};
+        if ((v & 3) == 0)
+          scales[((int64_t)(v / 16) * C + slots[j]) * 4 + ((v / 4) & 3)] = (uint8_t)(X + 127);
+      }
+  }
+}
+
+// The SwiGLU backward per copy from dH_raw (fp32 [C, f]) and the saved A|U, one row per
+// wavefront: dg = sum_i dH_raw_i h_i (lane partials in column order, then the wavefront's
+// fixed butterfly), dA|dU (fp32 [C, 2f], and MX along f: codes [C, 2f], scales
+// [2f/128][C][4]) and g h (fp32 [C, f]).  Every value that a later step MX-quantises stays
+// in fp32 up to its quantisation: a bf16 rounding in between moves values across E4M3
+// rounding boundaries (skewed workload, hottest expert's dW_up: 6.1e-2 from the oracle
+// with bf16 dH_raw, g h and dA|dU).  Workgroup = one 128-row tile of the tile list.
+__global__ __launch_bounds__(256) void swiglu_bwd_mx_kernel(
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles,
+    const int32_t* __restrict__ offset, int64_t head, int64_t C, int f,
+    const float* __restrict__ dhr, const bf16_t* __restrict__ saved_au,
+    const int32_t* __restrict__ slot_copy, const float* __restrict__ gate,
+    float* __restrict__ dau, uint8_t* __restrict__ dau_q, uint8_t* __restrict__ dau_s,
+    float* __restrict__ gh, float* __restrict__ dg_out) {
+  const int mt = blockIdx.x;
+  if (mt >= *ntiles) return;
+  const int e = tiles[2 * mt], row0 = tiles[2 * mt + 1];
+  const int32_t seg = offset[e];
+  const int rows = min(BT, offset[e + 1] - seg - row0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nv = f / 8, iters = (nv + 63) / 64;
+  for (int r = wave; r < rows; r += 4) {
+    const int64_t s = ring_slot(head, seg, row0 + r, C);
+    const float g = gate[slot_copy[s]];
+    float dgp = 0.f;
+    for (int it = 0; it < iters; ++it) {
+      const int v = it * 64 + lane;
+      const bool ok = v < nv;
+      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 wd0 = ok ? ((const f32x4*)(dhr + s * f))[2 * v] : z4;
+      const f32x4 wd1 = ok ? ((const f32x4*)(dhr + s * f))[2 * v + 1] : z4;
+      const u32x4 wa = ok ? ((const u32x4*)(saved_au + s * 2 * f))[v] : u32x4{0, 0, 0, 0};
+      const u32x4 wu = ok ? ((const u32x4*)(saved_au + s * 2 * f + f))[v] : u32x4{0, 0, 0, 0};
+      float da[8], du[8], hh[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float dh_raw = q < 4 ? wd0[q] : wd1[q - 4];
+        const float a = q & 1 ? hi_bf(wa[q / 2]) : lo_bf(wa[q / 2]);
+        const float u = q & 1 ? hi_bf(wu[q / 2]) : lo_bf(wu[q / 2]);
+        const float sg = sigm(a);
+        const float h = a * sg * u;
+        dgp = fmaf(dh_raw, h, dgp);
+        const float dh = g * dh_raw;
+        da[q] = dh * u * sg * (1.f + a * (1.f - sg));
+        du[q] = dh * a * sg;
+        hh[q] = g * h;
+      }
+      // MX codes of dA and dU along f: the 4 lanes of a 32-element block
+      float ama = 0.f, amu = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) { ama = fmaxf(ama, fabsf(da[q])); amu = fmaxf(amu, fabsf(du[q])); }
+      ama = group_max<4>(ama);
+      amu = group_max<4>(amu);
+      const int Xa = mx_block_exp(ama), Xu = mx_block_exp(amu);
+      if (ok) {
+        f32x4* pa = (f32x4*)(dau + s * 2 * f) + 2 * v;
+        f32x4* pu = (f32x4*)(dau + s * 2 * f + f) + 2 * v;
+        f32x4* ph = (f32x4*)(gh + s * f) + 2 * v;
+        pa[0] = f32x4{da[0], da[1], da[2], da[3]};
+        pa[1] = f32x4{da[4], da[5], da[6], da[7]};
+        pu[0] = f32x4{du[0], du[1], du[2], du[3]};
+        pu[1] = f32x4{du[4], du[5], du[6], du[7]};
+        ph[0] = f32x4{hh[0], hh[1], hh[2], hh[3]};
+        ph[1] = f32x4{hh[4], hh[5], hh[6], hh[7]};
+        uint32_t ca0 = 0, ca1 = 0, cu0 = 0, cu1 = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          ca0 |= e4m3_encode(da[q], Xa) << (8 * q);
+          ca1 |= e4m3_encode(da[4 + q], Xa) << (8 * q);
+          cu0 |= e4m3_encode(du[q], Xu) << (8 * q);
+          cu1 |= e4m3_encode(du[4 + q], Xu) << (8 * q);
+        }
+        *(u32x2*)(dau_q + s * 2 * f + (int64_t)v * 8) = u32x2{ca0, ca1};
+        *(u32x2*)(dau_q + s * 2 * f + f + (int64_t)v * 8) = u32x2{cu0, cu1};
+        if ((v & 3) == 0) {
+          const int ba = v / 4, bu = f / 32 + v / 4;   // block indices along the 2f row
+          dau_s[((int64_t)(ba / 4) * C + s) * 4 + (ba & 3)] = (uint8_t)(Xa + 127);
+          dau_s[((int64_t)(bu / 4) * C + s) * 4 + (bu & 3)] = (uint8_t)(Xu + 127);
+        }
+      }
+    }
+    const float dg = wave_sum(dgp);
+    if (lane == 0) dg_out[s] = dg;
+  }
+}
+
+// Value of an E4M3 code times 2^X (exact in fp32 for the scales MX produces here).
+__device__ __forceinline__ float e4m3_value_scaled(uint32_t code, int X) {
+  const int e = (code >> 3) & 15, m = code & 7;
+  const float v = e == 0 ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), e - 10);
+  return ldexpf((code & 0x80u) ? -v : v, X);
+}
+
+// Every expert's ring rows of src [C, cols] (fp32 or bf16) MX round-tripped along the token
+// axis into dst [C, cols] bf16 (may be src itself when src is bf16): blocks of 32 rows
+// aligned to the segment's end.  blocks: the tile list of 32-row tiles; tile (e, 32 q) is
+// taken as the q-th block from the end, rows [n_e - 32 (q + 1), n_e - 32 q) of the segment
+// (the first block is the partial one).  One thread per column.  The decoded values are
+// bf16 values (3 significant bits and a power-of-two scale).
+template <typename SRC>
+__global__ __launch_bounds__(256) void token_quant_kernel(
+    const int32_t* __restrict__ blocks, const int32_t* __restrict__ nblocks,
+    const int32_t* __restrict__ offset, int64_t head, int64_t C, int cols,
+    const SRC* src, bf16_t* dst) {
+  const int bi = blockIdx.x;
+  if (bi >= *nblocks) return;
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  if (c >= cols) return;
+  const int e = blocks[2 * bi], q = blocks[2 * bi + 1] / 32;
+  const int32_t seg = offset[e];
+  const int n = offset[e + 1] - seg;
+  const int hi = n - 32 * q, lo = max(0, hi - 32);
+  float v[32];
+  float am = 0.f;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    v[r] = 0.f;
+    if (lo + r < hi) {
+      const SRC w = src[ring_slot(head, seg, lo + r, C) * cols + c];
+      if constexpr (sizeof(SRC) == 4) v[r] = w;
+      else v[r] = bf2f(w);
+    }
+    am = fmaxf(am, fabsf(v[r]));
+  }
+  const int X = mx_block_exp(am);
+#pragma unroll
+  for (int r = 0; r < 32; ++r)
+    if (lo + r < hi)
+      dst[ring_slot(head, seg, lo + r, C) * cols + c] = f2bf(e4m3_value_scaled(e4m3_encode(v[r], X), X));
+}
+
+struct BwdMxLayout {
+  size_t tiles, blocks, rdy, rq, rqs, dhr, dau, dauq, daus, gh, dau16, gh16, dg, dxc, dl, xr,
+      rpart, rfirst, zero, total;
+};
+
+static BwdMxLayout bwd_mx_layout(int64_t T, int64_t C, int d, int E, int k, int f) {
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const int64_t n = T * k;
+  BwdMxLayout L;
+  size_t o = 0;
+  L.tiles = o;  o += al((size_t)(2 * bwd_max_tiles(n, E) + 64) * 4);
+  L.blocks = o; o += al((size_t)(2 * ((n + 31) / 32 + E) + 64) * 4);
+  L.rdy = o;    o += al((size_t)C * d * 2);
+  L.rq = o;     o += al((size_t)C * d);
+  L.rqs = o;    o += al((size_t)C * (d / 32));
+  L.dhr = o;    o += al((size_t)C * f * 4);
+  L.dau = o;    o += al((size_t)C * 2 * f * 4);
+  L.dauq = o;   o += al((size_t)C * 2 * f);
+  L.daus = o;   o += al((size_t)C * (2 * f / 32));
+  L.gh = o;     o += al((size_t)C * f * 4);
+  L.dau16 = o;  o += al((size_t)C * 2 * f * 2);
+  L.gh16 = o;   o += al((size_t)C * f * 2);
+  L.dg = o;     o += al((size_t)C * 4);
+  L.dxc = o;    o += al((size_t)C * d * 2);
+  L.dl = o;     o += al((size_t)C * 4);
+  L.xr = o;     o += al((size_t)C * d * 2);
+  L.rpart = o;  o += al((size_t)bwd_max_tiles(n, E) * d * 4);
+  L.rfirst = o; o += al((size_t)E * 4);
+  L.zero = o;   o += 1024;
+  L.total = o;
+  return L;
+}
+
+size_t backward_mx_workspace_bytes(int64_t T, int64_t C, int d, int E, int k, int f) {
+  return bwd_mx_layout(T, C, d, E, k, f).total;
+}
+
+hipError_t launch_backward_mx(const void* dy, const void* x, const float* w_r,
+                              const int32_t* topk_idx, const float* topk_gate,
+                              const int32_t* expert_offset, const int32_t* copy_slot,
+                              const int32_t* slot_copy, int64_t head, int64_t C,
+                              const void* saved_au, const uint8_t* w_gu_t,
+                              const uint8_t* w_gu_t_scale, const uint8_t* w_down_t,
+                              const uint8_t* w_down_t_scale, int64_t T, int d, int E, int k,
+                              int f, void* dx, void* dw_gate, void* dw_up, void* dw_down,
+                              float* dw_r, void* ws, hipStream_t st) {
+  if (d % BT || f % BT) return hipErrorInvalidValue;
+  const BwdMxLayout L = bwd_mx_layout(T, C, d, E, k, f);
+  uint8_t* w = (uint8_t*)ws;
+  int32_t* ntiles = (int32_t*)(w + L.tiles);
+  int32_t* tiles = ntiles + 64;
+  int32_t* nblocks = (int32_t*)(w + L.blocks);
+  int32_t* blocks = nblocks + 64;
+  bf16_t* rdy = (bf16_t*)(w + L.rdy);
+  float* dhr = (float*)(w + L.dhr);
+  float* dau = (float*)(w + L.dau);
+  float* gh = (float*)(w + L.gh);
+  bf16_t* dau16 = (bf16_t*)(w + L.dau16);
+  bf16_t* gh16 = (bf16_t*)(w + L.gh16);
+  float* dg = (float*)(w + L.dg);
+  bf16_t* dxc = (bf16_t*)(w + L.dxc);
+  float* dl = (float*)(w + L.dl);
+  bf16_t* xr = (bf16_t*)(w + L.xr);
+  const int64_t n = T * k;
+  const int max_tiles = bwd_max_tiles(n, E);
+  const int max_blocks = (int)((n + 31) / 32) + E;
+
+  hipError_t err = launch_build_tiles(expert_offset, E, BT, tiles, ntiles, st);
+  if (err == hipSuccess) err = launch_build_tiles(expert_offset, E, 32, blocks, nblocks, st);
+  if (err != hipSuccess) return err;
+  zero_fill_kernel<<<1, 256, 0, st>>>((uint32_t*)(w + L.zero), 256);
+  gather_to_ring_kernel<<<(unsigned)T, 256, 0, st>>>((const bf16_t*)dy, copy_slot, k, d, rdy);
+  gather_mx_kernel<<<(unsigned)T, 256, 0, st>>>((const bf16_t*)dy, copy_slot, k, d, C,
+                                                w + L.rq, w + L.rqs);
+  gather_to_ring_kernel<<<(unsigned)T, 256, 0, st>>>((const bf16_t*)x, copy_slot, k, d, xr);
+  // down dgrad: dH_raw = Q_d(dY) Q_d(W_down)
+  GemmArgs g{};
+  g.A = w + L.rq;
+  g.A_scale = w + L.rqs;
+  g.B0 = w_down_t;
+  g.B0_scale = w_down_t_scale;
+  g.K = d;
+  g.N = f;
+  g.offset = expert_offset;
+  g.tiles = tiles;
+  g.ntiles = ntiles;
+  g.head = head;
+  g.C = C;
+  g.out = (uint8_t*)dhr;
+  g.a_rows = C;
+  g.b_rows = (int64_t)E * f;
+  if ((err = launch_mx_plain_gemm128(g, n, E, true, st)) != hipSuccess) return err;
+  swiglu_bwd_mx_kernel<<<(unsigned)max_tiles, 256, 0, st>>>(
+      tiles, ntiles, expert_offset, head, C, f, dhr, (const bf16_t*)saved_au, slot_copy,
+      topk_gate, dau, w + L.dauq, w + L.daus, gh, dg);
+  // gate/up dgrad: dX_c = [Q_f(dA) | Q_f(dU)] [Q_f(W_gate); Q_f(W_up)]
+  GemmArgs g2 = g;
+  g2.A = w + L.dauq;
+  g2.A_scale = w + L.daus;
+  g2.B0 = w_gu_t;
+  g2.B0_scale = w_gu_t_scale;
+  g2.K = 2 * f;
+  g2.N = d;
+  g2.out = (uint8_t*)dxc;
+  g2.b_rows = (int64_t)E * d;
+  if ((err = launch_mx_plain_gemm128(g2, n, E, false, st)) != hipSuccess) return err;
+  token_kernel<<<(unsigned)T, 256, 0, st>>>(copy_slot, topk_idx, topk_gate, dg, 1, dxc, w_r, d,
+                                            k, dl, (bf16_t*)dx);
+  float* rpart = (float*)(w + L.rpart);
+  int32_t* rfirst = (int32_t*)(w + L.rfirst);
+  router_wgrad_part_kernel<<<dim3(max_tiles, (d / 8 + 127) / 128), 128, 0, st>>>(
+      tiles, ntiles, expert_offset, head, C, xr, dl, d, rpart, rfirst);
+  router_wgrad_sum_kernel<<<dim3(E, (d / 4 + 255) / 256), 256, 0, st>>>(expert_offset, rfirst,
+                                                                        rpart, d, dw_r);
+  // weight gradients on the operands quantised along the token axis
+  token_quant_kernel<bf16_t><<<dim3(max_blocks, (d + 255) / 256), 256, 0, st>>>(
+      blocks, nblocks, expert_offset, head, C, d, rdy, rdy);
+  token_quant_kernel<float><<<dim3(max_blocks, (f + 255) / 256), 256, 0, st>>>(
+      blocks, nblocks, expert_offset, head, C, f, gh, gh16);
+  token_quant_kernel<float><<<dim3(max_blocks, (2 * f + 255) / 256), 256, 0, st>>>(
+      blocks, nblocks, expert_offset, head, C, 2 * f, dau, dau16);
+  token_quant_kernel<bf16_t><<<dim3(max_blocks, (d + 255) / 256), 256, 0, st>>>(
+      blocks, nblocks, expert_offset, head, C, d, xr, xr);
+  WgradArgs wd{};
+  wd.A = rdy;
+  wd.B = gh16;
+  wd.M = d;
+  wd.N = f;
+  wd.msplit = d;
+  wd.lda = d;
+  wd.ldb = f;
+  wd.offset = expert_offset;
+  wd.E = E;
+  wd.head = head;
+  wd.C = C;
+  wd.zero = (const bf16_t*)(w + L.zero);
+  wd.out0 = (bf16_t*)dw_down;
+  wd.out1 = (bf16_t*)dw_down;
+  if ((err = run_wgrad(wd, st)) != hipSuccess) return err;
+  WgradArgs wu = wd;
+  wu.A = dau16;
+  wu.B = xr;
   wu.M = 2 * f;
   wu.N = d;
   wu.msplit = f;

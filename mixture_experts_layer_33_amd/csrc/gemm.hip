@@ -58,18 +58,20 @@ hipError_t launch_build_tiles(const int32_t* expert_offset, int E, int BM, int32
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S, int POL>
+template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S, int POL,
+          bool F32OUT = false>
 __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
-  gg_mfma_body<BM, BN, WM, WN, KB, SWIGLU, MX, S, POL>(p, (int)blockIdx.x, lds);
+  gg_mfma_body<BM, BN, WM, WN, KB, SWIGLU, MX, S, POL, F32OUT>(p, (int)blockIdx.x, lds);
 }
 
-template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S, int POL>
+template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S, int POL,
+          bool F32OUT = false>
 static hipError_t run_mfma(const GemmArgs& a, int max_tiles, hipStream_t st) {
   const int nt = SWIGLU ? (a.N + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
   const size_t lds = std::max<size_t>((size_t)S * StageLayout<BM, BN, KB, MX, WM * WN>::SIZE,
                                       EpiLayout<BM, BN, SWIGLU, MX>::SIZE);
-  auto kern = gg_mfma_kernel<BM, BN, WM, WN, KB, SWIGLU, MX, S, POL>;
+  auto kern = gg_mfma_kernel<BM, BN, WM, WN, KB, SWIGLU, MX, S, POL, F32OUT>;
   // opt in to more than 64 KB of LDS: a host-side attribute, set on every launch so that
   // nothing is kept between calls
   hipError_t err = hipFuncSetAttribute((const void*)kern,
@@ -79,6 +81,17 @@ static hipError_t run_mfma(const GemmArgs& a, int max_tiles, hipStream_t st) {
   const int64_t grid = 8 * ((vmax + 7) / 8);
   kern<<<(unsigned)grid, WM * WN * 64, lds, st>>>(a);
   return hipGetLastError();
+}
+
+hipError_t launch_mx_plain_gemm128(GemmArgs& g, int64_t n, int E, bool f32_out, hipStream_t st) {
+  g.rotate = kstart_rotates(false, 2, n, E, MFMA_BM);
+  const int max_tiles = max_tiles_for(n, E, MFMA_BM);
+  const bool nt = gemm_policy(false, 2, n, E, MFMA_BM) == 3;
+  if (f32_out)
+    return nt ? run_mfma<MFMA_BM, 256, 2, 4, 128, false, true, 3, 3, true>(g, max_tiles, st)
+              : run_mfma<MFMA_BM, 256, 2, 4, 128, false, true, 3, 2, true>(g, max_tiles, st);
+  return nt ? run_mfma<MFMA_BM, 256, 2, 4, 128, false, true, 3, 3>(g, max_tiles, st)
+            : run_mfma<MFMA_BM, 256, 2, 4, 128, false, true, 3, 2>(g, max_tiles, st);
 }
 
 // ============================================================ fp32 VALU path

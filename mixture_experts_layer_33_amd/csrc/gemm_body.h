@@ -125,7 +125,9 @@ struct EpiLayout {
 // The body of one workgroup's tile: vb is the workgroup's place in the 1-D grid (its
 // XCD is vb % 8), lds the dynamic LDS of the stage ring.  The kernel below runs it once
 // per workgroup; the single-launch forward runs it for a sequence of vb per workgroup.
-template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S, int POL>
+// F32OUT (not SWIGLU): the output rows are fp32 [C, N], stored from the accumulators.
+template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S, int POL,
+          bool F32OUT = false>
 __device__ __forceinline__ void gg_mfma_body(const GemmArgs p, int vb, uint8_t* lds) {
   constexpr int EB = MX ? 1 : 2;                 // element bytes
   constexpr int WTM = BM / WM, WTN = BN / WN;    // wave tile
@@ -463,25 +465,34 @@ __device__ __forceinline__ void gg_mfma_body(const GemmArgs p, int vb, uint8_t* 
   __syncthreads();
   // Copy the staged plane to dst (row pitch `pitch` bytes, tile columns from byte
   // col0b); rows beyond the segment and columns beyond N are not written.
-  auto flush = [&](uint8_t* dst, int64_t pitch, int col0b, int rowb) __attribute__((always_inline)) {
+  // RS, CPR: the staged row stride and 16-byte pieces per row (the layout of EL, or of
+  // bf16 planes beside an MX epilogue)
+  auto flush_as = [&](uint8_t* dst, int64_t pitch, int col0b, int rowb, int RS, int CPR)
+      __attribute__((always_inline)) {
     __syncthreads();
 #pragma unroll 4
-    for (int q = tid; q < BM * EL::CPR; q += NT) {
-      const int m = q / EL::CPR, cb = (q % EL::CPR) * 16;
+    for (int q = tid; q < BM * CPR; q += NT) {
+      const int m = q / CPR, cb = (q % CPR) * 16;
       if (m < rows && col0b + cb < rowb) {
         const int64_t sl = ring_slot(p.head, seg, row0 + m, p.C);
-        const u32x4 v = *(const u32x4*)(stg + m * EL::RS + cb);
+        const u32x4 v = *(const u32x4*)(stg + m * RS + cb);
         if (POL & 2) __builtin_nontemporal_store(v, (u32x4*)(dst + sl * pitch + col0b + cb));
         else *(u32x4*)(dst + sl * pitch + col0b + cb) = v;
       }
     }
     __syncthreads();
   };
+  auto flush = [&](uint8_t* dst, int64_t pitch, int col0b, int rowb) __attribute__((always_inline)) {
+    flush_as(dst, pitch, col0b, rowb, EL::RS, EL::CPR);
+  };
   if constexpr (SWIGLU) {
     constexpr int HALF = FN / 2;
     // plane 0: h = silu(a) * u (bf16, or E4M3 codes with per-32 scales); with saved
-    // A|U, planes 1 and 2 hold a and u in bf16
-    const int nplanes = (!MX && p.saved_au) ? 3 : 1;
+    // A|U, planes 1 and 2 hold a and u in bf16 (also beside MX codes: the MXFP8 backward
+    // reads them like the bf16 one), staged with a bf16 row stride
+    const int nplanes = p.saved_au ? 3 : 1;
+    constexpr int RS16 = (BN / 2) * 2 + 16, CPR16 = (BN / 2) * 2 / 16;
+    static_assert(!SWIGLU || BM * RS16 <= S * SL::SIZE, "bf16 planes fit the stage ring");
     for (int plane = 0; plane < nplanes; ++plane) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -492,7 +503,7 @@ __device__ __forceinline__ void gg_mfma_body(const GemmArgs p, int vb, uint8_t* 
           for (int r = 0; r < 16; ++r) {
             const int m = wm * WTM + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
             const float a = acc[i][j][r], u = acc[i][j + HALF][r];
-            if constexpr (MX) {
+            if (MX && plane == 0) {
               const float h = silu(a) * u;
               // the 32 columns of one row's block sit in the 32 lanes of a half-wave
               const float am = group_max<32>(fabsf(h));
@@ -504,14 +515,30 @@ __device__ __forceinline__ void gg_mfma_body(const GemmArgs p, int vb, uint8_t* 
                             (col / 32) % 4] = (uint8_t)(X + 127);
             } else {
               const float v = plane == 0 ? silu(a) * u : plane == 1 ? a : u;
-              *(uint16_t*)(stg + m * EL::RS + cl * 2) = f2bf(v);
+              *(uint16_t*)(stg + m * (MX ? RS16 : EL::RS) + cl * 2) = f2bf(v);
             }
           }
         }
       if (plane == 0) flush(p.out, (int64_t)p.N * EL::OEB, n0 * EL::OEB, p.N * EL::OEB);
-      else flush((uint8_t*)p.saved_au + (plane == 2 ? (int64_t)p.N * 2 : 0), (int64_t)p.N * 4,
-                 n0 * 2, p.N * 2);
+      else flush_as((uint8_t*)p.saved_au + (plane == 2 ? (int64_t)p.N * 2 : 0), (int64_t)p.N * 4,
+                    n0 * 2, p.N * 2, MX ? RS16 : EL::RS, MX ? CPR16 : EL::CPR);
     }
+  } else if constexpr (F32OUT) {
+    // 32 lanes store 32 consecutive columns of one row: 128-byte pieces
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm * WTM + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+        if (m < rows) {
+          float* orow = (float*)p.out + ring_slot(p.head, seg, row0 + m, p.C) * p.N;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn * WTN + j * 32 + lr;
+            if (col < p.N) orow[col] = acc[i][j][r];
+          }
+        }
+      }
   } else {
 #pragma unroll
     for (int i = 0; i < FM; ++i)

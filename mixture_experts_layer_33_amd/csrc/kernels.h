@@ -72,5 +72,26 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
 // MX quantisation of a bf16 matrix along its rows
 hipError_t launch_quantize_mx(const void* src, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t st);
+// ... and of the columns of each of `batch` matrices [R, Cc], written transposed
+hipError_t launch_quantize_mx_t(const void* src, int64_t batch, int64_t R, int64_t Cc,
+                                uint8_t* codes, int64_t ld, int64_t col0, uint8_t* scales,
+                                hipStream_t st);
+
+// a plain MX grouped GEMM with 128-row tiles over a prebuilt tile list (the MXFP8 backward's
+// dgrad GEMMs): out[slot] = A[slot] B[e]^T in bf16, or in fp32
+struct GemmArgs;
+hipError_t launch_mx_plain_gemm128(GemmArgs& g, int64_t n, int E, bool f32_out, hipStream_t st);
+
+// MXFP8 backward
+size_t backward_mx_workspace_bytes(int64_t T, int64_t C, int d, int E, int k, int f);
+hipError_t launch_backward_mx(const void* dy, const void* x, const float* w_r,
+                              const int32_t* topk_idx, const float* topk_gate,
+                              const int32_t* expert_offset, const int32_t* copy_slot,
+                              const int32_t* slot_copy, int64_t head, int64_t C,
+                              const void* saved_au, const uint8_t* w_gu_t,
+                              const uint8_t* w_gu_t_scale, const uint8_t* w_down_t,
+                              const uint8_t* w_down_t_scale, int64_t T, int d, int E, int k,
+                              int f, void* dx, void* dw_gate, void* dw_up, void* dw_down,
+                              float* dw_r, void* ws, hipStream_t st);
 
 }  // namespace moe

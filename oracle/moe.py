@@ -53,6 +53,14 @@ def from_f32(a: np.ndarray) -> np.ndarray:
     return np.asarray(a, dtype=np.float32).astype(np.float64)
 
 
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """fp64 -> fp32 (round to nearest even) -> bf16 (round to nearest even on the top 16
+    bits), as fp64: how the forward keeps its saved pre-activations."""
+    u = np.asarray(a, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return from_bf16_bits(r)
+
+
 # Expert weights are handed over lazily, one expert at a time: a callable
 # e -> (W_gate[e] [f,d], W_up[e] [f,d], W_down[e] [d,f]) in fp64.
 Weights = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]
@@ -427,8 +435,10 @@ def max_abs_rel(got: np.ndarray, ref: np.ndarray) -> float:
 # its recipe.  Reading: each backward GEMM takes its two operands MX-quantised (E4M3, one E8M0
 # scale per 32) along that GEMM's own reduction dimension, products accumulated exactly (fp64
 # here), everything elementwise unquantised; the forward's quantisation is the identity in
-# the backward (straight-through), and A, U are the MX forward's:
-#   A = Q_d(X) Q_d(W_gate)^T,  U = Q_d(X) Q_d(W_up)^T,  H = silu(A) U
+# the backward (straight-through), and A, U are the MX forward's as the forward saves them,
+# rounded to bf16 (each backward GEMM re-quantises values derived from them, so a rounding
+# there moves values across E4M3 rounding boundaries and is part of the definition):
+#   A = bf16(Q_d(X) Q_d(W_gate)^T),  U = bf16(Q_d(X) Q_d(W_up)^T),  H = silu(A) U
 #   dH_raw = Q_d(dY) Q_d(W_down)          W_down [d, f] quantised along d (its columns)
 #   dg = <dH_raw, H>;  dA, dU as in the bf16 backward
 #   dX_c = Q_f(dA) Q_f(W_gate) + Q_f(dU) Q_f(W_up)     W_gate, W_up [f, d] along f
@@ -461,8 +471,8 @@ def expert_backward_mx(e: int, x: np.ndarray, dy: np.ndarray, routing: Routing,
     X = x[ts]
     g = routing.gate[ts, js]
     Xq = mx.fake_quant(X, axis=1)
-    A = Xq @ mx.fake_quant(wg, axis=1).T
-    U = Xq @ mx.fake_quant(wu, axis=1).T
+    A = round_bf16(Xq @ mx.fake_quant(wg, axis=1).T)
+    U = round_bf16(Xq @ mx.fake_quant(wu, axis=1).T)
     s = sigmoid(A)
     H = A * s * U
     dY = dy[ts]

@@ -155,7 +155,10 @@ MOE_MUTATIONS = [
      "P = np.concatenate([M, np.zeros((pad,) + M.shape[1:])], axis=0)\n    return mx.fake_quant(P, axis=0)[:n]"),
     ("MX bwd: gH not token-quantised", "token_quant(g[:, None] * H)", "(g[:, None] * H)"),
     ("MX bwd: X not token-quantised", "Xt = token_quant(X)", "Xt = X"),
-    ("MX bwd: A from unquantised x", "A = Xq @ mx.fake_quant(wg, axis=1).T", "A = X @ mx.fake_quant(wg, axis=1).T"),
+    ("MX bwd: A from unquantised x", "A = round_bf16(Xq @ mx.fake_quant(wg, axis=1).T)",
+     "A = round_bf16(X @ mx.fake_quant(wg, axis=1).T)"),
+    ("MX bwd: U not rounded as saved", "U = round_bf16(Xq @ mx.fake_quant(wu, axis=1).T)",
+     "U = Xq @ mx.fake_quant(wu, axis=1).T"),
     ("MX bwd: copies in token order, not ring order", "copies = disp.slot_copy[segment_slots(disp, e)]",
      "copies = np.sort(disp.slot_copy[segment_slots(disp, e)])[::-1]"),
 ]

@@ -598,8 +598,9 @@ def torch_mx_backward(x, w_r, b, k, wg, wu, wd, dy):
             lS = l[t, S[t]]
             g = np.exp(lS[j] - lS.max()) / np.exp(lS - lS.max()).sum()
             xq = q(x[t][None, :], 1)[0]
-            a = q(wg[e], 1) @ xq
-            u = q(wu[e], 1) @ xq
+            bf = lambda v: torch.from_numpy(v).float().to(torch.bfloat16).double().numpy()
+            a = bf(q(wg[e], 1) @ xq)
+            u = bf(q(wu[e], 1) @ xq)
             sg = torch.sigmoid(torch.from_numpy(a)).numpy()
             h = a * sg * u
             dhr = q(dy[t][None, :], 1)[0] @ q(wd[e], 0)
@@ -663,3 +664,14 @@ def test_token_quant_end_alignment():
     Q = oracle.token_quant(M)
     assert Q[8, 0] == 5 * 2.0 ** -12 and Q[38, 0] == 5 * 2.0 ** -12
     assert Q[0, 0] == 352 * 2.0 ** -18 and Q[7, 0] == 352 * 2.0 ** -18
+
+
+def test_round_bf16_against_torch():
+    """The saved pre-activations' rounding: fp64 -> fp32 -> bf16, both round to nearest even,
+    against torch's own conversions, on values spread over 40 binades and on exact bf16 ties."""
+    rng = np.random.default_rng(19)
+    v = rng.standard_normal(50000) * np.exp(rng.uniform(-20, 20, 50000))
+    ties = (np.arange(1, 2001) * 2 + 1).astype(np.float64) * 2.0 ** -8   # odd multiples of half a bf16 step near 1..16
+    for a in (v, ties, -ties):
+        ref = torch.from_numpy(a).float().to(torch.bfloat16).double().numpy()
+        np.testing.assert_array_equal(oracle.moe.round_bf16(a), ref)
