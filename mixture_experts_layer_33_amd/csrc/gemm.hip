@@ -59,19 +59,19 @@ hipError_t launch_build_tiles(const int32_t* expert_offset, int E, int BM, int32
 }
 
 template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S, int POL,
-          bool F32OUT = false>
+          bool F32OUT = false, bool MXSAVE = false>
 __global__ __launch_bounds__(WM * WN * 64) void gg_mfma_kernel(GemmArgs p) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
-  gg_mfma_body<BM, BN, WM, WN, KB, SWIGLU, MX, S, POL, F32OUT>(p, (int)blockIdx.x, lds);
+  gg_mfma_body<BM, BN, WM, WN, KB, SWIGLU, MX, S, POL, F32OUT, MXSAVE>(p, (int)blockIdx.x, lds);
 }
 
 template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S, int POL,
-          bool F32OUT = false>
+          bool F32OUT = false, bool MXSAVE = false>
 static hipError_t run_mfma(const GemmArgs& a, int max_tiles, hipStream_t st) {
   const int nt = SWIGLU ? (a.N + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
   const size_t lds = std::max<size_t>((size_t)S * StageLayout<BM, BN, KB, MX, WM * WN>::SIZE,
                                       EpiLayout<BM, BN, SWIGLU, MX>::SIZE);
-  auto kern = gg_mfma_kernel<BM, BN, WM, WN, KB, SWIGLU, MX, S, POL, F32OUT>;
+  auto kern = gg_mfma_kernel<BM, BN, WM, WN, KB, SWIGLU, MX, S, POL, F32OUT, MXSAVE>;
   // opt in to more than 64 KB of LDS: a host-side attribute, set on every launch so that
   // nothing is kept between calls
   hipError_t err = hipFuncSetAttribute((const void*)kern,
@@ -244,10 +244,17 @@ hipError_t launch_ffn(int dtype, const void* ring_x, const uint8_t* ring_x_scale
 #define RUN_POL(P, G, ...)                                                 \
   err = (P) == 3 ? run_mfma<__VA_ARGS__, 3>(G, max_tiles, st)              \
                  : run_mfma<__VA_ARGS__, 2>(G, max_tiles, st);
-  if (big && dtype == 2) { RUN_POL(pol1, g1, MFMA_BM_BIG, 256, 4, 2, 128, true, true, 2) }
+#define RUN_POL_MXSAVE(P, G, ...)                                              \
+  err = (P) == 3 ? run_mfma<__VA_ARGS__, 3, false, true>(G, max_tiles, st)     \
+                 : run_mfma<__VA_ARGS__, 2, false, true>(G, max_tiles, st);
+  const bool mxsave = dtype == 2 && saved_au != nullptr;
+  if (big && mxsave) { RUN_POL_MXSAVE(pol1, g1, MFMA_BM_BIG, 256, 4, 2, 128, true, true, 2) }
+  else if (big && dtype == 2) { RUN_POL(pol1, g1, MFMA_BM_BIG, 256, 4, 2, 128, true, true, 2) }
   else if (big) { RUN_POL(pol1, g1, MFMA_BM_BIG, 256, 4, 4, 128, true, false, 2) }
   else if (dtype == 1) { RUN_POL(pol1, g1, MFMA_BM, 256, 2, 4, 128, true, false, 3) }
+  else if (mxsave) { RUN_POL_MXSAVE(pol1, g1, MFMA_BM, 256, 2, 4, 128, true, true, 3) }
   else { RUN_POL(pol1, g1, MFMA_BM, 256, 2, 4, 128, true, true, 3) }
+#undef RUN_POL_MXSAVE
   if (err != hipSuccess || (err = mark(1)) != hipSuccess) return err;
   if (big && dtype == 2) { RUN_POL(pol2, g2, MFMA_BM_BIG, 256, 4, 2, 128, false, true, 2) }
   else if (big) { RUN_POL(pol2, g2, MFMA_BM_BIG, 256, 4, 4, 128, false, false, 2) }

@@ -126,8 +126,11 @@ struct EpiLayout {
 // XCD is vb % 8), lds the dynamic LDS of the stage ring.  The kernel below runs it once
 // per workgroup; the single-launch forward runs it for a sequence of vb per workgroup.
 // F32OUT (not SWIGLU): the output rows are fp32 [C, N], stored from the accumulators.
+// MXSAVE (SWIGLU + MX): also write the saved A|U planes (bf16 takes them whenever
+// p.saved_au is set; the MX tiles have no registers to spare for that choice at run time:
+// the accumulators would stay live across the extra planes and spill).
 template <int BM, int BN, int WM, int WN, int KB, bool SWIGLU, bool MX, int S, int POL,
-          bool F32OUT = false>
+          bool F32OUT = false, bool MXSAVE = false>
 __device__ __forceinline__ void gg_mfma_body(const GemmArgs p, int vb, uint8_t* lds) {
   constexpr int EB = MX ? 1 : 2;                 // element bytes
   constexpr int WTM = BM / WM, WTN = BN / WN;    // wave tile
@@ -490,27 +493,31 @@ __device__ __forceinline__ void gg_mfma_body(const GemmArgs p, int vb, uint8_t* 
     // plane 0: h = silu(a) * u (bf16, or E4M3 codes with per-32 scales); with saved
     // A|U, planes 1 and 2 hold a and u in bf16 (also beside MX codes: the MXFP8 backward
     // reads them like the bf16 one), staged with a bf16 row stride
-    const int nplanes = p.saved_au ? 3 : 1;
     constexpr int RS16 = (BN / 2) * 2 + 16, CPR16 = (BN / 2) * 2 / 16;
     static_assert(!SWIGLU || BM * RS16 <= S * SL::SIZE, "bf16 planes fit the stage ring");
-    for (int plane = 0; plane < nplanes; ++plane) {
+    auto stage_plane = [&](auto plane_tag) __attribute__((always_inline)) {
+      constexpr int plane = decltype(plane_tag)::value;
+      // beside MX codes the lane's row and column are re-derived per plane, so that no
+      // plane's addresses stay live across the others
+      int plr = lr, plg = lg;
+      if constexpr (MX && MXSAVE) asm volatile("" : "+v"(plr), "+v"(plg));
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < HALF; ++j) {
-          const int cl = wn * (WTN / 2) + j * 32 + lr;   // column inside the tile
+          const int cl = wn * (WTN / 2) + j * 32 + plr;   // column inside the tile
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int m = wm * WTM + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+            const int m = wm * WTM + i * 32 + 8 * (r / 4) + 4 * plg + (r % 4);
             const float a = acc[i][j][r], u = acc[i][j + HALF][r];
-            if (MX && plane == 0) {
+            if constexpr (MX && plane == 0) {
               const float h = silu(a) * u;
               // the 32 columns of one row's block sit in the 32 lanes of a half-wave
               const float am = group_max<32>(fabsf(h));
               const int X = mx_block_exp(am);
               stg[m * EL::RS + cl] = (uint8_t)e4m3_encode(h, X);
               const int col = n0 + cl;
-              if (lr == 0 && m < rows && col < p.N)
+              if (plr == 0 && m < rows && col < p.N)
                 p.out_scale[((int64_t)(col / 128) * p.C + ring_slot(p.head, seg, row0 + m, p.C)) * 4 +
                             (col / 32) % 4] = (uint8_t)(X + 127);
             } else {
@@ -519,9 +526,24 @@ __device__ __forceinline__ void gg_mfma_body(const GemmArgs p, int vb, uint8_t* 
             }
           }
         }
-      if (plane == 0) flush(p.out, (int64_t)p.N * EL::OEB, n0 * EL::OEB, p.N * EL::OEB);
+      if constexpr (plane == 0) flush(p.out, (int64_t)p.N * EL::OEB, n0 * EL::OEB, p.N * EL::OEB);
       else flush_as((uint8_t*)p.saved_au + (plane == 2 ? (int64_t)p.N * 2 : 0), (int64_t)p.N * 4,
                     n0 * 2, p.N * 2, MX ? RS16 : EL::RS, MX ? CPR16 : EL::CPR);
+    };
+    if constexpr (MX) {
+      // the h plane last: it is the accumulators' final use, so its block reductions run
+      // as the accumulators die
+      if constexpr (MXSAVE) {
+        stage_plane(std::integral_constant<int, 1>{});
+        stage_plane(std::integral_constant<int, 2>{});
+      }
+      stage_plane(std::integral_constant<int, 0>{});
+    } else {
+      stage_plane(std::integral_constant<int, 0>{});
+      if (p.saved_au) {
+        stage_plane(std::integral_constant<int, 1>{});
+        stage_plane(std::integral_constant<int, 2>{});
+      }
     }
   } else if constexpr (F32OUT) {
     // 32 lanes store 32 consecutive columns of one row: 128-byte pieces
