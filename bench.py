@@ -54,8 +54,14 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle expert work in the CPU baseline sample")
-    ap.add_argument("--only", choices=["decode", "share", "skew", "skew-no-stack", "mxfp8"], default=None,
+    ap.add_argument("--only", choices=["decode", "share", "skew", "skew-no-stack", "skew-mx", "mxfp8"],
+                    default=None,
                     help="run one secondary workload alone (e.g. under a profiler) and print its JSON")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="leave out the single-launch forward (a cooperative launch, which "
+                         "rocprofv3 does not survive at exit)")
+    ap.add_argument("--decode-batch", type=int, choices=[1, 4, 8], default=None,
+                    help="with --only decode: this batch size alone")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (reference for counter scaling)")
     return ap.parse_args()
@@ -66,8 +72,12 @@ def progress(msg: str) -> None:
 
 
 def gemm_source_hash() -> str:
-    with open(os.path.join(ROOT, "mixture_experts_layer_33_amd", "csrc", "gemm.hip"), "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """Hash of the grouped GEMM's sources (the counters are void once they change)."""
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "gemm_body.h"):
+        with open(os.path.join(ROOT, "mixture_experts_layer_33_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, per_launch_alg_bytes: float):
@@ -276,6 +286,63 @@ def skew_fwd_bwd(torch, moe, steps, stack=True):
             **({"ring_stack": ring_stack(torch, moe, inp, layer, steps, fm, bm)} if stack else {})}
 
 
+def skew_fwd_bwd_mx(torch, moe, steps):
+    """The skewed workload in MXFP8: forward (saving A|U) and moe_backward_mx, timed apart;
+    the per-step weight quantisation (forward weights along K, backward weights transposed)
+    timed on its own.  Algorithmic bytes: forward = used experts' MX weights (codes + one
+    scale byte per 32) + W_r + x twice + ring (MX) written and read + H (MX) written and read
+    + saved A|U written + ring_y written and read + y; backward = used experts' transposed
+    MX weights + all three weight gradients written (bf16, every expert) + dW_r + dy and x
+    read + saved A|U read + dx."""
+    import numpy as np
+    from gen import SKEW_BWD, make_layer
+    cfg = SKEW_BWD.with_(name="skew_bwd_mx_t8192", dtype="mxfp8")
+    progress(f"skewed MXFP8 forward + backward {cfg.name}")
+    inp = make_layer(cfg, "cuda")
+    q = [moe.quantize_mx(w) for w in (inp.w_gate, inp.w_up, inp.w_down)]
+    wq, scales = tuple(c for c, _ in q), tuple(s for _, s in q)
+    bw = moe.quantize_mx_t_backward_weights(inp.w_gate, inp.w_up, inp.w_down)
+    layer = moe.Layer.create(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.C, dtype="mxfp8")
+    fargs = (inp.x, inp.w_router, inp.b_router, *wq)
+    for _ in range(2):
+        layer.forward(*fargs, scales=scales, save_au=True)
+        layer.backward_mx(inp.dy, inp.x, inp.w_router, *bw)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        layer.forward(*fargs, scales=scales, save_au=True)
+        ev[i][1].record()
+        layer.backward_mx(inp.dy, inp.x, inp.w_router, *bw)
+        ev[i][2].record()
+        for w, c, s in zip((inp.w_gate, inp.w_up, inp.w_down), wq, scales):
+            moe.moe_quantize_mx(w, c, s)
+        moe.quantize_mx_t_backward_weights(inp.w_gate, inp.w_up, inp.w_down)
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    fwd = [e[0].elapsed_time(e[1]) for e in ev]
+    bwd = [e[1].elapsed_time(e[2]) for e in ev]
+    wqt = [e[2].elapsed_time(e[3]) for e in ev]
+    counts = layer.bufs["expert_count"].cpu().numpy()
+    used = int((counts > 0).sum())
+    T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f
+    n = T * k
+    mxb = 1 + 1 / 32
+    w_used = used * 3 * f * d * mxb
+    fwd_bytes = (w_used + E * d * 4 + 2 * T * d * 2 + 2 * n * d * mxb + 2 * n * f * mxb
+                 + n * 2 * f * 2 + 2 * n * d * 2 + T * d * 2)
+    bwd_bytes = (w_used + E * 3 * f * d * 2 + E * d * 4 + 2 * T * d * 2 + n * 2 * f * 2 + T * d * 2)
+    fm, bm = float(np.median(fwd)), float(np.median(bwd))
+    return {"tokens": T, "fwd_ms_median": round(fm, 4), "fwd_ms_min": round(min(fwd), 4),
+            "bwd_ms_median": round(bm, 4), "bwd_ms_min": round(min(bwd), 4),
+            "weight_quant_ms_median": round(float(np.median(wqt)), 4),
+            "tokens_per_s_fwd_bwd": round(T / ((fm + bm) * 1e-3), 1),
+            "fwd_alg_bytes": fwd_bytes, "fwd_hbm_frac": round(fwd_bytes / (fm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bwd_alg_bytes": bwd_bytes, "bwd_hbm_frac": round(bwd_bytes / (bm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "experts_used": used, "max_load": int(counts.max()),
+            "max_over_mean": round(float(counts.max() / (n / E)), 2)}
+
+
 def ring_stack(torch, moe, inp, layer, steps, fwd_ms_1, bwd_ms_1, L=4):
     """L layers of the skewed shape sharing one ring (the same weights in every layer): the
     forwards advance the head, the backward consumes the layers last first with nothing
@@ -313,12 +380,12 @@ def ring_stack(torch, moe, inp, layer, steps, fwd_ms_1, bwd_ms_1, L=4):
     return out
 
 
-def part_decode(torch, moe, steps):
+def part_decode(torch, moe, steps, batches=(1, 4, 8)):
     """Small-batch decode, output-parallel, B = 1, 4, 8."""
     import numpy as np
     from gen import DECODE, make_layer
     dec, prev = {}, None
-    for B in (1, 4, 8):
+    for B in batches:
         cfg = DECODE(B)
         progress(f"decode B={B}")
         inp = make_layer(cfg, "cuda", reuse=prev)
@@ -436,6 +503,8 @@ def secondary(torch, moe, steps):
     out.update(part_share(torch, moe, steps))
     out["skew_fwd_bwd_t8192"] = skew_fwd_bwd(torch, moe, steps)
     torch.cuda.empty_cache()
+    out["skew_fwd_bwd_mx_t8192"] = skew_fwd_bwd_mx(torch, moe, steps)
+    torch.cuda.empty_cache()
     out["fwd_mxfp8_t2048"] = part_mxfp8(torch, moe, steps)
     return out
 
@@ -471,9 +540,12 @@ def main():
         calibrate_copy(torch, args)
         steps = max(2, args.steps)
         if args.only == "decode":
-            res = part_decode(torch, moe, steps)
+            res = part_decode(torch, moe, steps,
+                              (args.decode_batch,) if args.decode_batch else (1, 4, 8))
         elif args.only == "share":
             res = part_share(torch, moe, steps)
+        elif args.only == "skew-mx":
+            res = skew_fwd_bwd_mx(torch, moe, steps)
         elif args.only in ("skew", "skew-no-stack"):
             res = skew_fwd_bwd(torch, moe, steps, stack=args.only == "skew")
         else:
@@ -528,8 +600,9 @@ def main():
         "timed_wall_s": round(wall, 3),
     }
     result.update(spread)
-    progress("single-launch forward (moe_forward)")
-    result["fused_forward"] = measure_fused(torch, moe, inp, cfg, args.steps, args.warmup, layer)
+    if not args.no_fused:
+        progress("single-launch forward (moe_forward)")
+        result["fused_forward"] = measure_fused(torch, moe, inp, cfg, args.steps, args.warmup, layer)
     progress(f"forward {ms:.3f} ms/step, gate/up GEMM {g1:.3f} ms, down GEMM {g2:.3f} ms")
     calibrate_copy(torch, args)
     if not args.no_secondary:
