@@ -18,9 +18,10 @@
 // same results up to fp32 rounding order).  Nothing is accumulated across workgroups:
 // the result does not depend on the schedule.
 //
-// Measured (2,048 tokens, d 7168, 256 experts, one MI355X, per-phase timestamps of every
-// workgroup): 4.16 ms per call against 3.89 ms for the separate kernels.  The GEMM phases
-// take the time of the separate GEMMs (2.29 | 1.34 ms of work per workgroup); each grid
+// Measured (2,048 tokens, d 7168, 256 experts, one MI355X): 4.03 ms per call (HIP events
+// around back-to-back calls) against 3.89 ms for the separate kernels.  Per-phase
+// timestamps of every workgroup (an instrumented copy, 4.16 ms per call) show the GEMM
+// phases taking the time of the separate GEMMs (2.29 | 1.34 ms per workgroup); each grid
 // barrier costs about 15 us from the last arrival to the release (the arriving
 // workgroup's L2 write-back, which cross-XCD visibility needs, is on the critical path),
 // eight of them about 0.12 ms.  Earlier forms: an acquire load in the polling loop
