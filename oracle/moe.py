@@ -21,7 +21,7 @@ Dispatch follows the fixed token ring buffer of the dzen.guru page (paragraph
 on the ring buffer in "Три решения…"): no token is dropped, copies are laid
 out expert-contiguously from a ring head, slots wrap modulo the capacity.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * topk_idx is reported in ascending expert id; ties in l go to the lower id;
   * copies (t, j), c = t*k + j, are ordered stably by expert, i.e. by (e, t);
   * a segment occupies slots (head + offset[e] + i) mod C;
