@@ -20,10 +20,14 @@
 //                       per 128-row tile, then over the expert's tiles (last first)
 //   gather_to_ring      dy rows copied into ring order, one per copy (t, j)
 //   wgrad_kernel        dW_down[e] = dY_e^T (g H)_e;  [dW_gate;dW_up][e] = [dA|dU]_e^T X_e
-// The dgrad tiles are 128 x 128 with K in 32-element stages filled by global -> LDS
+// The dgrad tiles are 128 x 256 (eight waves; 128 x 128 with four when the output
+// width is not a multiple of 256) with K in 32-element stages filled by global -> LDS
 // copies; the weights, whose K index is their row index, are staged row-major and
 // read as MFMA fragments with transposing LDS reads, as are both operands of the
 // weight gradients.  No floating-point atomics: every sum has one fixed order.
+// The 256-column tiles copy each 128-row tile of copy rows once per 256 output columns
+// instead of once per 128 (skewed 8,192-token backward, same-GPU A/B: 9.85 ms with
+// 128 x 128 tiles, 9.37 with the gate/up dgrad widened, 9.04 with both).
 #include "common.h"
 #include "gemm_body.h"
 #include "kernels.h"
@@ -34,23 +38,29 @@ constexpr int BT = 128;            // dgrad tile rows and columns
 // Output tiles are staged row-major in LDS (BT rows of BT bf16, rows padded by 16
 // bytes) and written as whole 16-byte pieces of rows instead of 2-byte stores
 // scattered over rows.
-constexpr int SRS = BT * 2 + 16;            // staged row stride in bytes
-constexpr int STAGE_BYTES = BT * SRS;       // 34,816
+template <int W>   // staged tile width in columns
+struct Staging {
+  static constexpr int SRS = W * 2 + 16;    // staged row stride in bytes
+  static constexpr int BYTES = BT * SRS;    // 34,816 for 128 columns
+};
+constexpr int STAGE_BYTES = Staging<BT>::BYTES;
 
+template <int W = BT>
 __device__ __forceinline__ void stage_put(uint8_t* stg, int m, int n, float v) {
-  *(uint16_t*)(stg + m * SRS + n * 2) = f2bf(v);
+  *(uint16_t*)(stg + m * Staging<W>::SRS + n * 2) = f2bf(v);
 }
 
 // Write the staged tile: row m < rows goes to dst_row(m) (a pointer to the tile's first
-// column in that row), 16 bytes per thread and step.  Barriers before and after.
-template <typename RowF>
+// column in that row), 16 bytes per thread and step, NT threads.  Barriers before and after.
+template <int W = BT, int NT = 256, typename RowF>
 __device__ __forceinline__ void stage_flush(const uint8_t* stg, int rows, RowF dst_row) {
   __syncthreads();
-  constexpr int CPR = BT * 2 / 16;
+  constexpr int CPR = W * 2 / 16;
 #pragma unroll 4
-  for (int q = threadIdx.x; q < BT * CPR; q += 256) {
+  for (int q = threadIdx.x; q < BT * CPR; q += NT) {
     const int m = q / CPR, c = q % CPR;
-    if (m < rows) *(u32x4*)((uint8_t*)dst_row(m) + c * 16) = *(const u32x4*)(stg + m * SRS + c * 16);
+    if (m < rows)
+      *(u32x4*)((uint8_t*)dst_row(m) + c * 16) = *(const u32x4*)(stg + m * Staging<W>::SRS + c * 16);
   }
   __syncthreads();
 }
@@ -72,7 +82,7 @@ struct DgradArgs {
   const bf16_t* saved_au;   // DOWN: [C, 2f]
   bf16_t* dau;              // DOWN out: [C, 2f]
   bf16_t* gh;               // DOWN out: [C, f]
-  float* dgpart;            // DOWN out: [C, f / BT]
+  float* dgpart;            // DOWN out: [C, f / (tile columns)]
   bf16_t* dxc;              // UP out: [C, d]
 };
 
@@ -106,10 +116,19 @@ __device__ __forceinline__ v4i16_t ds_tr16(const uint8_t* lds_ptr) {
 // against four stages and two workgroups; five stages and two workgroups 10.9 ms, two
 // stages and four workgroups 9.76 ms.
 constexpr int DK = 32, DWS = 3;
-constexpr int DA_BYTES = BT * DK * 2, DB_BYTES = DK * BT * 2, DSTAGE = DA_BYTES + DB_BYTES;
-constexpr int DG_LDS = DWS * DSTAGE > STAGE_BYTES ? DWS * DSTAGE : STAGE_BYTES;   // the epilogue staging (34,816 bytes) reuses it
-static_assert(DG_LDS >= STAGE_BYTES && DG_LDS >= DWS * DSTAGE, "dgrad LDS holds the ring and the epilogue staging");
-constexpr int DL = (DA_BYTES + DB_BYTES) / 4096;   // 1 KB copies per wave per stage
+// Tile shape: 128 rows x 64 NWN columns, waves in 2 x NWN of 64 x 64.
+template <int NWN>
+struct DgShape {
+  static constexpr int NW = 2 * NWN, NT = 64 * NW;     // waves, threads
+  static constexpr int BN = 64 * NWN;                  // tile columns
+  static constexpr int A_BYTES = BT * DK * 2, B_BYTES = DK * BN * 2, STAGE = A_BYTES + B_BYTES;
+  // the stage ring; the epilogue staging reuses it
+  static constexpr int LDS = DWS * STAGE > Staging<BN>::BYTES ? DWS * STAGE : Staging<BN>::BYTES;
+  static constexpr int NA = A_BYTES / (1024 * NW), NB = B_BYTES / (1024 * NW);   // 1 KB copies per wave
+  static constexpr int L = NA + NB;
+  static constexpr int RPK = 1024 / (BN * 2), CPRB = BN * 2 / 16;   // B rows per KB, 16-byte chunks per B row
+  static constexpr int OCC = NWN == 2 ? 3 : 2;         // workgroups per CU (the LDS of each)
+};
 
 __device__ __forceinline__ int aswz(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
@@ -137,11 +156,16 @@ __device__ __forceinline__ void grouped_tile(int L, int nct, int G, const int32_
   mt = t0 + g * G + rem % rg;
 }
 
-template <bool DOWN>
-__global__ __launch_bounds__(256, 3) void dgrad_kernel(DgradArgs p) {
+// NWN = 2: 128 x 128 tiles, four waves (both dgrads); NWN = 4: 128 x 256, eight waves (the
+// gate/up dgrad: each 128-row tile of [dA|dU] is copied once per 256 output columns
+// instead of once per 128).
+template <bool DOWN, int NWN>
+__global__ __launch_bounds__(DgShape<NWN>::NT, DgShape<NWN>::OCC) void dgrad_kernel(DgradArgs p) {
+  using Sh = DgShape<NWN>;
+  constexpr int DA_BYTES = Sh::A_BYTES, NW = Sh::NW, BN = Sh::BN, DL = Sh::L;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-  __shared__ float red[2][BT];
+  __shared__ float red[NWN][BT];   // DOWN: per wave column, each row's partial of dg
   // Tile order: workgroup b runs on XCD b % 8, and XCD x takes the logical tiles
   // [x per, (x + 1) per), per = ceil(V / 8) of the V live tiles.  Logical tiles are
   // expert-major; an expert's row tiles form groups of G, and inside a group the column
@@ -153,7 +177,7 @@ __global__ __launch_bounds__(256, 3) void dgrad_kernel(DgradArgs p) {
   // 7.6 | 15.6 GB; this order 7.0 | 10.8 GB, against 5.3 | 8.9 GB algorithmic.  The
   // kernel times did not change (1.79 | 2.91 ms): these kernels are bound by their
   // copy-to-MFMA pipeline, not by HBM traffic.
-  const int nct = p.N / BT;
+  const int nct = p.N / BN;
   const int V = *p.ntiles * nct, per = (V + 7) / 8;
   const int li = (int)(blockIdx.x >> 3), L = (int)(blockIdx.x & 7) * per + li;
   if (li >= per || L >= V) return;
@@ -162,22 +186,26 @@ __global__ __launch_bounds__(256, 3) void dgrad_kernel(DgradArgs p) {
   const int e = p.tiles[2 * mt], row0 = p.tiles[2 * mt + 1];
   const int32_t seg = p.offset[e];
   const int rows = min(BT, p.offset[e + 1] - seg - row0);
-  const int n0 = ct * BT;
+  const int n0 = ct * BN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lg = lane >> 5;
+  const int wm = wave / NWN, wn = wave % NWN, lr = lane & 31, lg = lane >> 5;
 
-  // Copy i (0, 1) of this wave fills LDS kilobyte wave + 4 i of the A tile, rows
-  // 16 (wave + 4 i) .. + 15, and of the B tile, K rows 4 (wave + 4 i) .. + 3.
-  const uint8_t* a_addr[2];
-  int b_row[2], b_col[2];
+  // Copy i of this wave fills LDS kilobyte wave + NW i of the A tile, rows
+  // 16 (wave + NW i) .. + 15, or of the B tile, K rows RPK (wave + NW i) .. + RPK - 1.
+  const uint8_t* a_addr[Sh::NA];
+  int b_row[Sh::NB], b_col[Sh::NB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int j = wave + 4 * i;
+  for (int i = 0; i < Sh::NA; ++i) {
+    const int j = wave + NW * i;
     const int r = j * 16 + (lane >> 2), slot = lane & 3, c = slot ^ ((r >> 2) & 3);
     const int64_t sl = ring_slot(p.head, seg, row0 + min(r, rows - 1), p.C);
     a_addr[i] = (const uint8_t*)p.A + (sl * p.K) * 2 + c * 16;
-    const int rb = j * 4 + (lane >> 4), sb = lane & 15;
+  }
+#pragma unroll
+  for (int i = 0; i < Sh::NB; ++i) {
+    const int j = wave + NW * i;
+    const int rb = j * Sh::RPK + lane / Sh::CPRB, sb = lane % Sh::CPRB;
     b_row[i] = rb;
     b_col[i] = (n0 + wsw(rb, sb) * 8) * 2;
   }
@@ -187,14 +215,14 @@ __global__ __launch_bounds__(256, 3) void dgrad_kernel(DgradArgs p) {
                                      : p.B1 + ((int64_t)e * p.f + (kk - p.f)) * p.N);
   };
   auto issue = [&](int kt) __attribute__((always_inline)) {
-    const uint32_t st = lds0 + (uint32_t)(kt % DWS) * DSTAGE;
+    const uint32_t st = lds0 + (uint32_t)(kt % DWS) * Sh::STAGE;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      dma16_at(a_addr[i] + kt * (DK * 2), __builtin_amdgcn_readfirstlane(st + (wave + 4 * i) * 1024));
+    for (int i = 0; i < Sh::NA; ++i)
+      dma16_at(a_addr[i] + kt * (DK * 2), __builtin_amdgcn_readfirstlane(st + (wave + NW * i) * 1024));
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < Sh::NB; ++i)
       dma16_at(brow_ptr(kt * DK + b_row[i]) + b_col[i],
-               __builtin_amdgcn_readfirstlane(st + DA_BYTES + (wave + 4 * i) * 1024));
+               __builtin_amdgcn_readfirstlane(st + DA_BYTES + (wave + NW * i) * 1024));
   };
   auto wait_stage = [&](int later) __attribute__((always_inline)) {
     if (later <= 0) bwait_vm<0>();
@@ -209,7 +237,7 @@ __global__ __launch_bounds__(256, 3) void dgrad_kernel(DgradArgs p) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const int col = wn * 64 + jj * 32 + 16 * (g & 1) + 4 * ss;
-      boff[jj] = DA_BYTES + r0 * (BT * 2) + wsw(r0, col >> 3) * 16 + (col & 7) * 2;
+      boff[jj] = DA_BYTES + r0 * (BN * 2) + wsw(r0, col >> 3) * 16 + (col & 7) * 2;
     }
   }
 
@@ -227,7 +255,7 @@ __global__ __launch_bounds__(256, 3) void dgrad_kernel(DgradArgs p) {
     wait_stage(min(DWS - 2, KT - 1 - kt));
     __syncthreads();   // stage kt published; the buffer of stage kt - 1 is free
     if (kt + DWS - 1 < KT) issue(kt + DWS - 1);
-    const uint8_t* sb = smem + (kt % DWS) * DSTAGE;
+    const uint8_t* sb = smem + (kt % DWS) * Sh::STAGE;
 #pragma unroll
     for (int kk = 0; kk < DK / 16; ++kk) {
       bf16x8 af[2], bfr[2];
@@ -236,8 +264,8 @@ __global__ __launch_bounds__(256, 3) void dgrad_kernel(DgradArgs p) {
         af[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(sb + aswz(wm * 64 + i * 32 + lr, kk * 2 + lg)));
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint8_t* b = sb + boff[j] + kk * 16 * (BT * 2);
-        const v4i16_t lo = ds_tr16(b), hi = ds_tr16(b + 4 * (BT * 2));
+        const uint8_t* b = sb + boff[j] + kk * 16 * (BN * 2);
+        const v4i16_t lo = ds_tr16(b), hi = ds_tr16(b + 4 * (BN * 2));
         bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
@@ -287,7 +315,10 @@ __global__ __launch_bounds__(256, 3) void dgrad_kernel(DgradArgs p) {
     __syncthreads();
     if (tid < rows) {
       const int64_t s = ring_slot(p.head, seg, row0 + tid, p.C);
-      p.dgpart[s * (f / BT) + n0 / BT] = red[0][tid] + red[1][tid];
+      float dgt = red[0][tid];
+#pragma unroll
+      for (int w = 1; w < NWN; ++w) dgt += red[w][tid];   // wave columns in order
+      p.dgpart[s * (f / BN) + n0 / BN] = dgt;
     }
   } else {
 #pragma unroll
@@ -298,10 +329,10 @@ __global__ __launch_bounds__(256, 3) void dgrad_kernel(DgradArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = wm * 64 + i * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-          stage_put(stg, m, nl, acc[i][j][r]);
+          stage_put<BN>(stg, m, nl, acc[i][j][r]);
         }
       }
-    stage_flush(stg, rows, [&](int m) -> void* {
+    stage_flush<BN, Sh::NT>(stg, rows, [&](int m) -> void* {
       return p.dxc + ring_slot(p.head, seg, row0 + m, p.C) * p.N + n0;
     });
   }
@@ -729,10 +760,16 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
   gather_to_ring_kernel<<<(unsigned)T, 256, 0, st>>>((const bf16_t*)dy, copy_slot, k, d, rdy);
   // dynamic LDS of the dgrad kernels: the stage ring (or the epilogue staging), asked for
   // on every call (a host-side attribute, no state kept here)
-  if ((err = hipFuncSetAttribute((const void*)dgrad_kernel<true>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, DG_LDS)) != hipSuccess ||
-      (err = hipFuncSetAttribute((const void*)dgrad_kernel<false>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, DG_LDS)) != hipSuccess)
+  // 256-column tiles where the output width allows (the copy rows are then copied once
+  // per 256 output columns instead of once per 128)
+  const bool wide = d % DgShape<4>::BN == 0, wide_down = f % DgShape<4>::BN == 0;
+  const int dg_cols = wide_down ? DgShape<4>::BN : BT;   // column tile of the down dgrad (dg partials)
+  if ((err = hipFuncSetAttribute(wide_down ? (const void*)dgrad_kernel<true, 4> : (const void*)dgrad_kernel<true, 2>,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 wide_down ? DgShape<4>::LDS : DgShape<2>::LDS)) != hipSuccess ||
+      (err = hipFuncSetAttribute(wide ? (const void*)dgrad_kernel<false, 4> : (const void*)dgrad_kernel<false, 2>,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 wide ? DgShape<4>::LDS : DgShape<2>::LDS)) != hipSuccess)
     return err;
   DgradArgs a{};
   a.A = rdy;
@@ -753,7 +790,12 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
   a.gh = gh;
   a.dgpart = dgpart;
   // 1-D grids over the bound max_tiles x column tiles (XCD-contiguous tile order inside)
-  dgrad_kernel<true><<<(unsigned)(8 * (((int64_t)max_tiles * (f / BT) + 7) / 8)), 256, DG_LDS, st>>>(a);
+  if (wide_down)
+    dgrad_kernel<true, 4><<<(unsigned)(8 * (((int64_t)max_tiles * (f / DgShape<4>::BN) + 7) / 8)),
+                            DgShape<4>::NT, DgShape<4>::LDS, st>>>(a);
+  else
+    dgrad_kernel<true, 2><<<(unsigned)(8 * (((int64_t)max_tiles * (f / BT) + 7) / 8)), DgShape<2>::NT,
+                            DgShape<2>::LDS, st>>>(a);
   DgradArgs b = a;
   b.A = dau;
   b.B0 = (const bf16_t*)w_gate;
@@ -761,8 +803,13 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
   b.K = 2 * f;
   b.N = d;
   b.dxc = dxc;
-  dgrad_kernel<false><<<(unsigned)(8 * (((int64_t)max_tiles * (d / BT) + 7) / 8)), 256, DG_LDS, st>>>(b);
-  token_kernel<<<(unsigned)T, 256, 0, st>>>(copy_slot, topk_idx, topk_gate, dgpart, f / BT, dxc,
+  if (wide)
+    dgrad_kernel<false, 4><<<(unsigned)(8 * (((int64_t)max_tiles * (d / DgShape<4>::BN) + 7) / 8)),
+                             DgShape<4>::NT, DgShape<4>::LDS, st>>>(b);
+  else
+    dgrad_kernel<false, 2><<<(unsigned)(8 * (((int64_t)max_tiles * (d / BT) + 7) / 8)), DgShape<2>::NT,
+                             DgShape<2>::LDS, st>>>(b);
+  token_kernel<<<(unsigned)T, 256, 0, st>>>(copy_slot, topk_idx, topk_gate, dgpart, f / dg_cols, dxc,
                                             w_r, d, k, dl, (bf16_t*)dx);
   float* rpart = (float*)(w + L.rpart);
   int32_t* rfirst = (int32_t*)(w + L.rfirst);
