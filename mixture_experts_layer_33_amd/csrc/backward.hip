@@ -484,15 +484,18 @@ __global__ __launch_bounds__(256) void router_wgrad_sum_kernel(
 // columns.  Lanes l and l + 32 hold the two halves of 8 columns; one
 // v_permlane32_swap per packed word pair gives each lane 8 consecutive bf16 of one
 // row, which it writes straight from registers as one 16-byte piece.
-constexpr int WM_ = 128, WK_ = 32;
+constexpr int WK_ = 32;
 
-template <int NJ>   // 32-column blocks per wave: tile width WN = 64 NJ
+// WGM x WGN waves, each 64 rows x 32 NJ columns of the dW tile.
+template <int WGM, int WGN, int NJ>
 struct WgShape {
-  static constexpr int WN = 64 * NJ;
-  static constexpr int ARB = WM_ * 2, BRB = WN * 2;   // staged row bytes of A and B
+  static constexpr int NW = WGM * WGN, NT = 64 * NW;
+  static constexpr int WM = 64 * WGM, WN = 32 * NJ * WGN;   // tile rows (of dW) and columns
+  static constexpr int ARB = WM * 2, BRB = WN * 2;          // staged row bytes of A and B
   static constexpr int STAGE = WK_ * (ARB + BRB);
-  static constexpr int LA = WK_ * ARB / 4096, LB = WK_ * BRB / 4096;   // 1 KB copies per wave
+  static constexpr int LA = WK_ * ARB / (1024 * NW), LB = WK_ * BRB / (1024 * NW);   // 1 KB copies per wave
   static constexpr int L = LA + LB;
+  static_assert(WK_ * ARB % (1024 * NW) == 0 && WK_ * BRB % (1024 * NW) == 0, "copies split evenly");
 };
 
 template <typename T>
@@ -521,9 +524,10 @@ struct WgradArgs {
   bf16_t* out1;             // [E, M - msplit, N]
 };
 
-template <int NJ, int WS, int OCC>
-__global__ __launch_bounds__(256, OCC) void wgrad_kernel(WgradArgs p) {
-  using S = WgShape<NJ>;
+template <int WGM, int WGN, int NJ, int WS, int OCC>
+__global__ __launch_bounds__(64 * WGM * WGN, OCC) void wgrad_kernel(WgradArgs p) {
+  using S = WgShape<WGM, WGN, NJ>;
+  constexpr int WM_ = S::WM, NW = S::NW;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
   const int mtiles = (p.M + WM_ - 1) / WM_, ntiles = (p.N + S::WN - 1) / S::WN;
@@ -550,7 +554,7 @@ __global__ __launch_bounds__(256, OCC) void wgrad_kernel(WgradArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lg = lane >> 5;
+  const int wm = wave / WGN, wn = wave % WGN, lr = lane & 31, lg = lane >> 5;
 
   // Per copy c of this wave (fixed for the tile): the staged row this lane fills and
   // the byte offset of its 16-byte piece inside a source row.
@@ -558,7 +562,7 @@ __global__ __launch_bounds__(256, OCC) void wgrad_kernel(WgradArgs p) {
 #pragma unroll
   for (int c = 0; c < S::L; ++c) {
     const bool isa = c < S::LA;
-    const int j = 4 * (isa ? c : c - S::LA) + wave;
+    const int j = NW * (isa ? c : c - S::LA) + wave;
     const int rb = isa ? S::ARB : S::BRB;
     const int q = lane / (rb / 16), r = j * (1024 / rb) + q, lc = wsw(r, lane % (rb / 16));
     crow[c] = r;
@@ -570,7 +574,7 @@ __global__ __launch_bounds__(256, OCC) void wgrad_kernel(WgradArgs p) {
 #pragma unroll
     for (int c = 0; c < S::L; ++c) {
       const bool isa = c < S::LA;
-      const int j = 4 * (isa ? c : c - S::LA) + wave;
+      const int j = NW * (isa ? c : c - S::LA) + wave;
       const int i = rbase + crow[c];
       int64_t sl = hs + i;
       sl = sl >= p.C ? sl - p.C : sl;
@@ -715,20 +719,25 @@ __global__ void zero_fill_kernel(uint32_t* __restrict__ p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
 }
 
-// 128 x 256 tiles, 2 stages, 3 workgroups per CU (measured best of 128 x 128 / 128 x 256,
-// 2 / 3 stages, 2 to 4 workgroups per CU)
-constexpr int WG_NJ = 4, WG_WS = 2, WG_OCC = 3;
+// 128 x 256 tiles (2 x 2 waves of 64 x 128), 2 stages, 3 workgroups per CU (measured best of
+// 128 x 128 / 128 x 256, 2 / 3 stages, 2 to 4 workgroups per CU).  Skewed 8,192-token bf16
+// backward, same-GPU A/B: this shape 9.0 ms; 256 x 256 in 4 x 4 waves of 64 x 64, one
+// workgroup per CU, 2 / 3 / 4 stages 9.8-10.0 / 9.2-9.3 / 9.1-9.2 ms; 128 x 256 in 2 x 4
+// waves of 64 x 64, two per CU, 9.6 ms (a third fewer copied bytes per dW element does not
+// pay for fewer independent workgroups per CU).
+constexpr int WG_M = 2, WG_N = 2, WG_NJ = 4, WG_WS = 2, WG_OCC = 3;
 
 static hipError_t run_wgrad(const WgradArgs& a, hipStream_t st) {
-  auto kern = wgrad_kernel<WG_NJ, WG_WS, WG_OCC>;
-  constexpr int lds = WG_WS * WgShape<WG_NJ>::STAGE;
+  using S = WgShape<WG_M, WG_N, WG_NJ>;
+  auto kern = wgrad_kernel<WG_M, WG_N, WG_NJ, WG_WS, WG_OCC>;
+  constexpr int lds = WG_WS * S::STAGE;
   if (lds > 65536) {   // opt in to more than 64 KB of LDS (a host-side call, on every launch)
     hipError_t err = hipFuncSetAttribute((const void*)kern,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (err != hipSuccess) return err;
   }
-  const int64_t P = (int64_t)((a.M + WM_ - 1) / WM_) * ((a.N + WgShape<WG_NJ>::WN - 1) / WgShape<WG_NJ>::WN);
-  kern<<<(unsigned)(8 * P * ((a.E + 7) / 8)), 256, lds, st>>>(a);   // 8 XCDs x P x the longest expert list
+  const int64_t P = (int64_t)((a.M + S::WM - 1) / S::WM) * ((a.N + S::WN - 1) / S::WN);
+  kern<<<(unsigned)(8 * P * ((a.E + 7) / 8)), S::NT, lds, st>>>(a);   // 8 XCDs x P x the longest expert list
   return hipGetLastError();
 }
 
