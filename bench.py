@@ -289,7 +289,9 @@ def skew_fwd_bwd(torch, moe, steps, stack=True):
 def skew_fwd_bwd_mx(torch, moe, steps):
     """The skewed workload in MXFP8: forward (saving A|U) and moe_backward_mx, timed apart;
     the per-step weight quantisation (forward weights along K, backward weights transposed)
-    timed on its own.  Algorithmic bytes: forward = used experts' MX weights (codes + one
+    timed on its own, in one pass per weight (moe_quantize_mx_both; its bytes: every bf16
+    weight read once, both MX layouts written) and, for comparison, as the two separate
+    quantisers.  Algorithmic bytes: forward = used experts' MX weights (codes + one
     scale byte per 32) + W_r + x twice + ring (MX) written and read + H (MX) written and read
     + saved A|U written + ring_y written and read + y; backward = used experts' transposed
     MX weights + all three weight gradients written (bf16, every expert) + dW_r + dy and x
@@ -308,21 +310,24 @@ def skew_fwd_bwd_mx(torch, moe, steps):
         layer.forward(*fargs, scales=scales, save_au=True)
         layer.backward_mx(inp.dy, inp.x, inp.w_router, *bw)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     for i in range(steps):
         ev[i][0].record()
         layer.forward(*fargs, scales=scales, save_au=True)
         ev[i][1].record()
         layer.backward_mx(inp.dy, inp.x, inp.w_router, *bw)
         ev[i][2].record()
+        moe.quantize_mx_training_weights(inp.w_gate, inp.w_up, inp.w_down)
+        ev[i][3].record()
         for w, c, s in zip((inp.w_gate, inp.w_up, inp.w_down), wq, scales):
             moe.moe_quantize_mx(w, c, s)
         moe.quantize_mx_t_backward_weights(inp.w_gate, inp.w_up, inp.w_down)
-        ev[i][3].record()
+        ev[i][4].record()
     torch.cuda.synchronize()
     fwd = [e[0].elapsed_time(e[1]) for e in ev]
     bwd = [e[1].elapsed_time(e[2]) for e in ev]
     wqt = [e[2].elapsed_time(e[3]) for e in ev]
+    wqs = [e[3].elapsed_time(e[4]) for e in ev]
     counts = layer.bufs["expert_count"].cpu().numpy()
     used = int((counts > 0).sum())
     T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f
@@ -333,9 +338,14 @@ def skew_fwd_bwd_mx(torch, moe, steps):
                  + n * 2 * f * 2 + 2 * n * d * 2 + T * d * 2)
     bwd_bytes = (w_used + E * 3 * f * d * 2 + E * d * 4 + 2 * T * d * 2 + n * 2 * f * 2 + T * d * 2)
     fm, bm = float(np.median(fwd)), float(np.median(bwd))
+    qm = float(np.median(wqt))
+    q_bytes = 3 * E * f * d * (2 + 2 * mxb)
     return {"tokens": T, "fwd_ms_median": round(fm, 4), "fwd_ms_min": round(min(fwd), 4),
             "bwd_ms_median": round(bm, 4), "bwd_ms_min": round(min(bwd), 4),
-            "weight_quant_ms_median": round(float(np.median(wqt)), 4),
+            "weight_quant_ms_median": round(qm, 4),
+            "weight_quant_hbm_frac": round(q_bytes / (qm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "weight_quant_separate_ms_median": round(float(np.median(wqs)), 4),
+            "training_step_ms": round(fm + bm + qm, 4),
             "tokens_per_s_fwd_bwd": round(T / ((fm + bm) * 1e-3), 1),
             "fwd_alg_bytes": fwd_bytes, "fwd_hbm_frac": round(fwd_bytes / (fm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bwd_alg_bytes": bwd_bytes, "bwd_hbm_frac": round(bwd_bytes / (bm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

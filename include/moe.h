@@ -337,6 +337,19 @@ int moe_quantize_mx_t(const void* src_bf16, int64_t batch, int64_t rows, int64_t
                       uint8_t* codes, int64_t ld, int64_t col0, uint8_t* scales,
                       hipStream_t stream);
 
+/*
+ * moe_quantize_mx_both: both MX layouts of `batch` bf16 matrices in one pass, for an MXFP8
+ * training step that re-quantises its weights for the forward and for moe_backward_mx.
+ * Writes exactly what moe_quantize_mx(src, batch*rows, cols, codes, scales) and
+ * moe_quantize_mx_t(src, batch, rows, cols, codes_t, ld, col0, scales_t) write, bit for
+ * bit, reading each bf16 value once.  rows, cols, ld and col0 multiples of 128, col0 +
+ * rows <= ld (MOE_ERR_SHAPE otherwise); NULL pointers: MOE_ERR_NULL.  Both code matrices
+ * and scale arrays are the caller's, as for the two calls it replaces.
+ */
+int moe_quantize_mx_both(const void* src_bf16, int64_t batch, int64_t rows, int64_t cols,
+                         uint8_t* codes, uint8_t* scales, uint8_t* codes_t, int64_t ld,
+                         int64_t col0, uint8_t* scales_t, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -160,6 +160,31 @@ def quantize_mx_t_backward_weights(w_gate, w_up, w_down, stream=None):
     return gu, gus, dn, dns
 
 
+def quantize_mx_training_weights(w_gate, w_up, w_down, stream=None):
+    """Every MX weight an MXFP8 training step needs, from the bf16 ones, reading each once
+    (moe_quantize_mx_both): ((W_gate, W_up, W_down) codes, (their scales), and the
+    backward's w_gu_t, w_gu_t scales, w_down_t, w_down_t scales) -- the outputs of
+    quantize_mx on each weight and of quantize_mx_t_backward_weights, bit for bit."""
+    E, f, d = w_gate.shape
+    dev = w_gate.device
+    codes = tuple(torch.empty(w.shape, dtype=torch.uint8, device=dev) for w in (w_gate, w_up, w_down))
+    scales = (torch.empty((d // 128, E * f, 4), dtype=torch.uint8, device=dev),
+              torch.empty((d // 128, E * f, 4), dtype=torch.uint8, device=dev),
+              torch.empty((f // 128, E * d, 4), dtype=torch.uint8, device=dev))
+    gu = torch.empty((E, d, 2 * f), dtype=torch.uint8, device=dev)
+    gus = torch.empty((2 * f // 128, E * d, 4), dtype=torch.uint8, device=dev)
+    dn = torch.empty((E, f, d), dtype=torch.uint8, device=dev)
+    dns = torch.empty((d // 128, E * f, 4), dtype=torch.uint8, device=dev)
+    L = lib()
+    s = _s(stream)
+    for w, c, sc, ct, ld, col0, sct, R, Cc in ((w_gate, codes[0], scales[0], gu, 2 * f, 0, gus, f, d),
+                                               (w_up, codes[1], scales[1], gu, 2 * f, f, gus, f, d),
+                                               (w_down, codes[2], scales[2], dn, d, 0, dns, d, f)):
+        check("moe_quantize_mx_both", L.moe_quantize_mx_both(_p(w), E, R, Cc, _p(c), _p(sc), _p(ct),
+                                                             ld, col0, _p(sct), s))
+    return codes, scales, (gu, gus, dn, dns)
+
+
 def moe_quantize_mx(src, codes, scales, stream=None):
     rows = src.numel() // src.shape[-1]
     check("moe_quantize_mx", lib().moe_quantize_mx(_p(src), rows, src.shape[-1], _p(codes),

@@ -43,6 +43,7 @@ SIGNATURES = {
     "moe_status_string": [C.c_int],
     "moe_quantize_mx": [P, I64, I64, P, P, P],
     "moe_quantize_mx_t": [P, I64, I64, I64, P, I64, I64, P, P],
+    "moe_quantize_mx_both": [P, I64, I64, I64, P, P, P, I64, I64, P, P],
     "moe_backward_mx": [SHP, P, P, P, P, P, P, P, P, I64, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
 }
 _RESTYPE = {"moe_workspace_bytes": SZ, "moe_status_string": C.c_char_p}

@@ -388,6 +388,21 @@ int moe_quantize_mx_t(const void* src_bf16, int64_t batch, int64_t rows, int64_t
   }
 }
 
+int moe_quantize_mx_both(const void* src_bf16, int64_t batch, int64_t rows, int64_t cols,
+                         uint8_t* codes, uint8_t* scales, uint8_t* codes_t, int64_t ld,
+                         int64_t col0, uint8_t* scales_t, hipStream_t stream) {
+  try {
+    if (!src_bf16 || !codes || !scales || !codes_t || !scales_t) return MOE_ERR_NULL;
+    if (batch < 0 || rows <= 0 || cols <= 0 || rows % 128 || cols % 128 || ld % 128 || col0 < 0 ||
+        col0 % 128 || col0 + rows > ld)
+      return MOE_ERR_SHAPE;
+    return hip_status(moe::launch_quantize_mx_both(src_bf16, batch, rows, cols, codes, scales,
+                                                   codes_t, ld, col0, scales_t, stream));
+  } catch (...) {
+    return MOE_ERR_HIP;
+  }
+}
+
 int moe_quantize_mx(const void* src_bf16, int64_t rows, int64_t cols, uint8_t* codes,
                     uint8_t* scales, hipStream_t stream) {
   try {

@@ -73,6 +73,9 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
 hipError_t launch_quantize_mx(const void* src, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, hipStream_t st);
 // ... and of the columns of each of `batch` matrices [R, Cc], written transposed
+hipError_t launch_quantize_mx_both(const void* src, int64_t batch, int64_t R, int64_t Cc,
+                                   uint8_t* codes, uint8_t* scales, uint8_t* codes_t, int64_t ld,
+                                   int64_t col0, uint8_t* scales_t, hipStream_t st);
 hipError_t launch_quantize_mx_t(const void* src, int64_t batch, int64_t R, int64_t Cc,
                                 uint8_t* codes, int64_t ld, int64_t col0, uint8_t* scales,
                                 hipStream_t st);

@@ -253,6 +253,14 @@ void quantizers() {
   expect("quantize_mx_t NULL scales", moe_quantize_mx_t(P, 1, 64, 128, PB, 128, 0, nullptr,
                                                         nullptr),
          MOE_ERR_NULL);
+  expect("quantize_mx_both NULL transposed scales",
+         moe_quantize_mx_both(P, 1, 128, 128, PB, PB, PB, 128, 0, nullptr, nullptr), MOE_ERR_NULL);
+  expect("quantize_mx_both rows % 128",
+         moe_quantize_mx_both(P, 1, 96, 128, PB, PB, PB, 128, 0, PB, nullptr), MOE_ERR_SHAPE);
+  expect("quantize_mx_both col0 % 128",
+         moe_quantize_mx_both(P, 1, 128, 128, PB, PB, PB, 256, 64, PB, nullptr), MOE_ERR_SHAPE);
+  expect("quantize_mx_both col0 + rows > ld",
+         moe_quantize_mx_both(P, 1, 256, 128, PB, PB, PB, 128, 0, PB, nullptr), MOE_ERR_SHAPE);
 }
 
 }  // namespace

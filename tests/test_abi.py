@@ -175,3 +175,18 @@ def test_decode_noalloc_validates_on_the_host():
     assert L.moe_decode_noalloc(moe.make_shape(9, 1024, 16, 4, 512), *([FAKE] * 12), None) == _lib.MOE_ERR_SHAPE
     assert L.moe_decode_noalloc(ok, *([FAKE] * 9), None, FAKE, FAKE, None) == _lib.MOE_ERR_NULL
     assert b"scratch" in L.moe_status_string(_lib.MOE_ERR_SCRATCH)
+
+
+def test_quantize_mx_both_validates_on_the_host():
+    """The two-layout quantiser rejects, before any HIP call, NULL pointers and sizes that
+    are not multiples of 128 or whose transposed columns overrun ld."""
+    L = _lib.lib()
+    q = L.moe_quantize_mx_both
+    assert q(None, 1, 128, 128, FAKE, FAKE, FAKE, 128, 0, FAKE, None) == _lib.MOE_ERR_NULL
+    assert q(FAKE, 1, 128, 128, FAKE, FAKE, FAKE, 128, 0, None, None) == _lib.MOE_ERR_NULL
+    assert q(FAKE, 1, 96, 128, FAKE, FAKE, FAKE, 128, 0, FAKE, None) == _lib.MOE_ERR_SHAPE
+    assert q(FAKE, 1, 128, 160, FAKE, FAKE, FAKE, 128, 0, FAKE, None) == _lib.MOE_ERR_SHAPE
+    assert q(FAKE, 1, 128, 128, FAKE, FAKE, FAKE, 128, 64, FAKE, None) == _lib.MOE_ERR_SHAPE
+    assert q(FAKE, 1, 256, 128, FAKE, FAKE, FAKE, 128, 0, FAKE, None) == _lib.MOE_ERR_SHAPE
+    assert q(FAKE, -1, 128, 128, FAKE, FAKE, FAKE, 128, 0, FAKE, None) == _lib.MOE_ERR_SHAPE
+
