@@ -1011,8 +1011,12 @@ __device__ __forceinline__ float e4m3_value_scaled(uint32_t code, int X) {
 // axis into dst [C, cols] bf16 (may be src itself when src is bf16): blocks of 32 rows
 // aligned to the segment's end.  blocks: the tile list of 32-row tiles; tile (e, 32 q) is
 // taken as the q-th block from the end, rows [n_e - 32 (q + 1), n_e - 32 q) of the segment
-// (the first block is the partial one).  One thread per column.  The decoded values are
-// bf16 values (3 significant bits and a power-of-two scale).
+// (the first block is the partial one).  One thread per 8 consecutive columns: the block's
+// rows are read twice (the column maxima, then the codes), in 16-byte pieces (two per row
+// for fp32), and written in 16-byte pieces; a thread owns its columns in every row of the
+// block, so the round trip may be in place.  (One thread per column with 2-byte accesses:
+// 735 us per bf16 launch at 8,192 skewed tokens.)  The decoded values are bf16 values
+// (3 significant bits and a power-of-two scale).
 template <typename SRC>
 __global__ __launch_bounds__(256) void token_quant_kernel(
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nblocks,
@@ -1020,29 +1024,49 @@ __global__ __launch_bounds__(256) void token_quant_kernel(
     const SRC* src, bf16_t* dst) {
   const int bi = blockIdx.x;
   if (bi >= *nblocks) return;
-  const int c = blockIdx.y * 256 + threadIdx.x;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
   if (c >= cols) return;
   const int e = blocks[2 * bi], q = blocks[2 * bi + 1] / 32;
   const int32_t seg = offset[e];
   const int n = offset[e + 1] - seg;
   const int hi = n - 32 * q, lo = max(0, hi - 32);
-  float v[32];
-  float am = 0.f;
+  auto load8 = [&](int64_t slot, float (&v)[8]) __attribute__((always_inline)) {
+    const SRC* p = src + slot * cols + c;
+    if constexpr (sizeof(SRC) == 4) {
+      const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    v[r] = 0.f;
-    if (lo + r < hi) {
-      const SRC w = src[ring_slot(head, seg, lo + r, C) * cols + c];
-      if constexpr (sizeof(SRC) == 4) v[r] = w;
-      else v[r] = bf2f(w);
+      for (int k = 0; k < 4; ++k) { v[k] = a[k]; v[4 + k] = b[k]; }
+    } else {
+      const u32x4 w = *(const u32x4*)p;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { v[2 * k] = lo_bf(w[k]); v[2 * k + 1] = hi_bf(w[k]); }
     }
-    am = fmaxf(am, fabsf(v[r]));
-  }
-  const int X = mx_block_exp(am);
+  };
+  float am[8];
 #pragma unroll
-  for (int r = 0; r < 32; ++r)
-    if (lo + r < hi)
-      dst[ring_slot(head, seg, lo + r, C) * cols + c] = f2bf(e4m3_value_scaled(e4m3_encode(v[r], X), X));
+  for (int j = 0; j < 8; ++j) am[j] = 0.f;
+#pragma unroll 8
+  for (int r = lo; r < hi; ++r) {
+    float v[8];
+    load8(ring_slot(head, seg, r, C), v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) am[j] = fmaxf(am[j], fabsf(v[j]));
+  }
+  int X[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) X[j] = mx_block_exp(am[j]);
+#pragma unroll 8
+  for (int r = lo; r < hi; ++r) {
+    const int64_t slot = ring_slot(head, seg, r, C);
+    float v[8];
+    load8(slot, v);
+    u32x4 out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      out[k] = pack_bf2(e4m3_value_scaled(e4m3_encode(v[2 * k], X[2 * k]), X[2 * k]),
+                        e4m3_value_scaled(e4m3_encode(v[2 * k + 1], X[2 * k + 1]), X[2 * k + 1]));
+    *(u32x4*)(dst + slot * cols + c) = out;
+  }
 }
 
 struct BwdMxLayout {
@@ -1160,13 +1184,13 @@ hipError_t launch_backward_mx(const void* dy, const void* x, const float* w_r,
   router_wgrad_sum_kernel<<<dim3(E, (d / 4 + 255) / 256), 256, 0, st>>>(expert_offset, rfirst,
                                                                         rpart, d, dw_r);
   // weight gradients on the operands quantised along the token axis
-  token_quant_kernel<bf16_t><<<dim3(max_blocks, (d + 255) / 256), 256, 0, st>>>(
+  token_quant_kernel<bf16_t><<<dim3(max_blocks, (d + 2047) / 2048), 256, 0, st>>>(
       blocks, nblocks, expert_offset, head, C, d, rdy, rdy);
-  token_quant_kernel<float><<<dim3(max_blocks, (f + 255) / 256), 256, 0, st>>>(
+  token_quant_kernel<float><<<dim3(max_blocks, (f + 2047) / 2048), 256, 0, st>>>(
       blocks, nblocks, expert_offset, head, C, f, gh, gh16);
-  token_quant_kernel<float><<<dim3(max_blocks, (2 * f + 255) / 256), 256, 0, st>>>(
+  token_quant_kernel<float><<<dim3(max_blocks, (2 * f + 2047) / 2048), 256, 0, st>>>(
       blocks, nblocks, expert_offset, head, C, 2 * f, dau, dau16);
-  token_quant_kernel<bf16_t><<<dim3(max_blocks, (d + 255) / 256), 256, 0, st>>>(
+  token_quant_kernel<bf16_t><<<dim3(max_blocks, (d + 2047) / 2048), 256, 0, st>>>(
       blocks, nblocks, expert_offset, head, C, d, xr, xr);
   WgradArgs wd{};
   wd.A = rdy;
