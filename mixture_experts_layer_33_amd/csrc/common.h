@@ -56,11 +56,28 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
-// Reduction over aligned groups of `G` lanes (G a power of two <= 64).
+// Maximum over aligned groups of `G` lanes (G a power of two <= 64), in VALU cross-lane
+// moves instead of LDS permutes: DPP quad permutations (lanes 1 and 2 apart), the half-row
+// and row mirrors (4 and 8 apart), and gfx950's permlane swaps of 16- and 32-lane halves
+// (given the same value twice, a swap hands each lane its partner's value in one of its
+// two results).  Checked on the GPU against the ds_bpermute butterfly for G = 4 .. 64
+// (bitwise equal).  The butterfly left a wave waiting ~100 cycles per step: the MX
+// gate/up epilogue's 32 block maxima per wave took ~10 us of its tile's time.
 template <int G>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = G / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  static_assert(G >= 2 && G <= 64 && (G & (G - 1)) == 0, "groups of 2 .. 64 lanes");
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false)));  // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false)));  // [2,3,0,1]
+  if constexpr (G >= 8) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false)));  // row_half_mirror
+  if constexpr (G >= 16) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false)));  // row_mirror
+  if constexpr (G >= 32) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+    v = fmaxf(__int_as_float(s[0]), __int_as_float(s[1]));
+  }
+  if constexpr (G >= 64) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    v = fmaxf(__int_as_float(s[0]), __int_as_float(s[1]));
+  }
   return v;
 }
 
