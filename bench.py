@@ -74,7 +74,7 @@ def progress(msg: str) -> None:
 def gemm_source_hash() -> str:
     """Hash of the grouped GEMM's sources (the counters are void once they change)."""
     h = hashlib.sha256()
-    for name in ("gemm.hip", "gemm_body.h"):
+    for name in ("gemm.hip", "gemm_body.h", "common.h"):
         with open(os.path.join(ROOT, "mixture_experts_layer_33_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -650,12 +650,16 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void wgrad_kernel(WgradArgs p)
   }
 
   // acc[jn][i][r]: output row m0 + wm*64 + 32i + lr, column
-  // n0 + wn*32*NJ + 32jn + 8(r/4) + 4lg + r%4.
+  // n0 + wn*32*NJ + 32jn + 8(r/4) + 4lg + r%4.  Each half i (32 rows x 32 NJ columns) is
+  // staged in a wave-private LDS area and written back as whole row pieces: 64 lanes store
+  // four rows' 256 contiguous bytes, 8 full cache lines per instruction, where storing
+  // from the accumulator layout would put 32 bytes into each of 32 rows.
+  static_assert(NJ == 4, "the staging swizzle assumes 256-byte rows (16 chunks)");
+  static_assert(NW * 32 * 64 * NJ <= WS * S::STAGE, "the staging areas fit in the stage ring");
+  __syncthreads();   // every wave is done with the stages
+  uint8_t* wl = lds + wave * (32 * 64 * NJ);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int m = m0 + wm * 64 + 32 * i + lr;
-    bf16_t* row = m < p.msplit ? p.out0 + ((int64_t)e * p.msplit + m) * p.N
-                               : p.out1 + ((int64_t)e * (p.M - p.msplit) + (m - p.msplit)) * p.N;
 #pragma unroll
     for (int jn = 0; jn < NJ; ++jn)
 #pragma unroll
@@ -668,9 +672,21 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void wgrad_kernel(WgradArgs p)
         const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
         const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
         const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
-        const int n = n0 + wn * 32 * NJ + 32 * jn + 16 * h + 8 * lg;
-        if (m < p.M && n < p.N) *(u32x4*)(row + n) = v;
+        // chunk 4jn + 2h + lg of row lr; chunks XOR-swizzled by the row so the 16 rows
+        // of a 16-lane group land on distinct 16-byte groups of the bank line
+        *(u32x4*)(wl + lr * 256 + (((4 * jn + 2 * h + lg) ^ (lr & 15)) << 4)) = v;
       }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      const int r = 4 * s2 + (lane >> 4), c = lane & 15;
+      const u32x4 v = *(const u32x4*)(wl + r * 256 + ((c ^ (r & 15)) << 4));
+      const int m = m0 + wm * 64 + 32 * i + r, n = n0 + wn * 32 * NJ + 8 * c;
+      bf16_t* row = m < p.msplit ? p.out0 + ((int64_t)e * p.msplit + m) * p.N
+                                 : p.out1 + ((int64_t)e * (p.M - p.msplit) + (m - p.msplit)) * p.N;
+      if (m < p.M && n < p.N) *(u32x4*)(row + n) = v;
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 

@@ -42,8 +42,13 @@ __device__ __forceinline__ int64_t ring_slot(int64_t head, int64_t off, int64_t 
   return s >= C ? s - C : s;
 }
 
-__device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
-__device__ __forceinline__ float sigm(float a) { return 1.0f / (1.0f + expf(-a)); }
+// SiLU and the logistic function on the hardware exp and reciprocal (about 2 ulp each) instead of
+// the full-precision expf and an IEEE division: in the GEMM epilogue that is 32 evaluations per
+// lane per tile.  Same-GPU A/B in alternating processes, forward per call: 2,048 tokens bf16
+// 3.720 -> 3.710 ms, MXFP8 2.258 -> 2.236 ms, skewed 8,192 tokens 4.04 -> 3.995 ms bf16,
+// 2.71 -> 2.65 ms MXFP8.  For a -> -inf, exp(-a) overflows to inf and the result is -0 (or 0).
+__device__ __forceinline__ float sigm(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
+__device__ __forceinline__ float silu(float a) { return a * sigm(a); }
 
 // Butterfly reductions over the 64 lanes of a wavefront (fixed order: deterministic).
 __device__ __forceinline__ float wave_sum(float v) {
