@@ -50,15 +50,10 @@ __device__ __forceinline__ int64_t ring_slot(int64_t head, int64_t off, int64_t 
 __device__ __forceinline__ float sigm(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 __device__ __forceinline__ float silu(float a) { return a * sigm(a); }
 
-// Butterfly reductions over the 64 lanes of a wavefront (fixed order: deterministic).
+// Butterfly sum over the 64 lanes of a wavefront (fixed order: deterministic).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
 // Maximum over aligned groups of `G` lanes (G a power of two <= 64), in VALU cross-lane
@@ -86,12 +81,35 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Minimum over aligned groups of `G` lanes, by the same cross-lane moves as group_max.
+template <int G>
+__device__ __forceinline__ int group_min_i(int v) {
+  static_assert(G >= 2 && G <= 64 && (G & (G - 1)) == 0, "groups of 2 .. 64 lanes");
+  v = min(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false));
+  if constexpr (G >= 4) v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false));
+  if constexpr (G >= 8) v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false));
+  if constexpr (G >= 16) v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false));
+  if constexpr (G >= 32) {
+    const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = min((int)s[0], (int)s[1]);
+  }
+  if constexpr (G >= 64) {
+    const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = min((int)s[0], (int)s[1]);
+  }
+  return v;
+}
+
 // ---------------------------------------------------------------- router row
 // Softmax statistics and top-k of one row of E <= 64*VPL logits held by a
 // wavefront (lane owns entries lane + 64 i).  k rounds of a wave-wide argmax,
 // ties to the lower expert id.  On return lane r < k holds the r-th selected
 // expert (`choice`), its rank in ascending expert order (`rank`) and its
 // renormalised gate p / sum_S p with p = exp(l - max) / sum_e exp(l - max).
+// Each round's wave-wide argmax is a maximum (group_max) and then the lowest expert id
+// among the lanes holding it (group_min_i), both exact, so the selection is that of a
+// pairwise butterfly; with ds_bpermute shuffles (two per step, six steps, eight rounds)
+// the decode's routing wavefront took ~13 us beside the weight stream.
 template <int VPL, typename LogitF>
 __device__ __forceinline__ void wave_route_row_f(LogitF logit, int E, int k, int& choice, int& rank,
                                                  float& gate) {
@@ -104,7 +122,7 @@ __device__ __forceinline__ void wave_route_row_f(LogitF logit, int E, int k, int
     v[i] = e < E ? logit(e) : -INFINITY;
     m = fmaxf(m, v[i]);
   }
-  m = wave_max(m);
+  m = group_max<64>(m);
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < VPL; ++i) s += (lane + 64 * i < E) ? expf(v[i] - m) : 0.f;
@@ -117,25 +135,23 @@ __device__ __forceinline__ void wave_route_row_f(LogitF logit, int E, int k, int
     int bi = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
+      if (64 * i >= E) break;   // uniform: no lane holds entries from here on
       const int e = lane + 64 * i;
       if (e < E && !((taken >> i) & 1u) && (v[i] > bv || (v[i] == bv && e < bi))) {
         bv = v[i];
         bi = e;
       }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
+    const float mv = group_max<64>(bv);
+    bi = group_min_i<64>(bv == mv ? bi : 0x7fffffff);
+    bv = mv;
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == r) { choice = bi; my_logit = bv; }
   }
   const float p = lane < k ? expf(my_logit - m) / s : 0.f;
   const float ps = wave_sum(p);
   rank = 0;
-  for (int i = 0; i < k; ++i) rank += (__shfl(choice, i, 64) < choice) ? 1 : 0;
+  for (int i = 0; i < k; ++i) rank += (__builtin_amdgcn_readlane(choice, i) < choice) ? 1 : 0;
   gate = p / ps;
 }
 

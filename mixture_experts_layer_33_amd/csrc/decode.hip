@@ -10,7 +10,7 @@
 //   next launch consumes them).
 // Kernel 1: every workgroup rebuilds top-k and gates from the logits
 //   (((p0 + p1) + p2) + p3 + bias) and the list of experts the batch selected; then
-//   one wavefront per row streams the shared expert's gate/up rows,
+//   its wavefronts claim rows one at a time: the shared expert's gate/up rows,
 //   hs[b][i] = silu(a) u, and the selected experts' rows (expert, row i): the
 //   W_gate and W_up rows are read once and h[b][j][i] = silu(a) u (fp32,
 //   token-major) is written for every token b that chose that expert as its j-th.
@@ -159,9 +159,29 @@ __global__ __launch_bounds__(256) void decode_router(DecodeArgs p) {
   }
 }
 
+// Kernel 1's rows: the shared expert's fs rows, then the (distinct expert, row) items
+// of the U selected experts, numbered g = 0 .. fs + U f - 1.  Workgroup b owns the rows g
+// with (g / 8) mod G = b (groups of 8 consecutive rows dealt round-robin, so the rows in
+// flight across the chip are neighbours), and its wavefronts claim them in order from a
+// counter in LDS: the c-th claim is row 8b + c mod 8 + (c / 8) 8G.  Every row is computed
+// whole by one wavefront with the same code, so the results do not depend on who takes it.
+//
+// Timestamps of a B = 1 call (wall clock, per wavefront) showed where the time went when
+// the routing sat between barriers: the weight stream ran at ~6.9 TB/s once every
+// workgroup had its expert list, but that took ~20 us from the kernel's start, because
+// the routing wave's logit loads queued behind the shared expert's rows already in
+// flight.  Now the routing waves issue their logit loads before any weight row is
+// requested, and after one barrier (x in LDS, logits arrived) nothing waits for the
+// routing: the other wavefronts stream the shared expert's rows at once, and a wavefront
+// that claims a routed row before the expert list is ready waits on an LDS flag that the
+// last routing wavefront raises (a bounded wait: were it ever exceeded, the wavefront would
+// stop claiming rather than hang).
+constexpr int DEC_SPIN_MAX = 1 << 20;   // ~64 cycles each: ~30 ms, far beyond any routing
+
 template <int NQ>   // d = NQ * 512
 __global__ __launch_bounds__(DEC_THREADS) void decode_k1(DecodeArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  __shared__ int claims, routed, ready;
   bf16_t* xs = (bf16_t*)lds;                                   // [B][d]
   int32_t* sel = (int32_t*)(lds + (size_t)p.B * p.d * 2);      // [B][DEC_KMAX]
   int32_t* uniq = sel + DEC_BMAX * DEC_KMAX;                   // [<= B*k]
@@ -170,84 +190,120 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_k1(DecodeArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), nwave = DEC_THREADS / 64;
-  const int gw = blockIdx.x * nwave + wave, W = gridDim.x * nwave;
+  const int W = gridDim.x * nwave;
   const int B = p.B, E = p.E, k = p.k, f = p.f, fs = p.fs;
   constexpr int d = NQ * 512;
+  const bool routes = wave < B;   // wavefronts 0..B-1 route one token each
 
-  for (int v = tid; v < B * d / 8; v += DEC_THREADS) ((u32x4*)xs)[v] = ((const u32x4*)p.x)[v];
-  for (int w = tid; w < (E + 31) / 32; w += DEC_THREADS) bits[w] = 0u;
-  __syncthreads();
-  // The shared expert's rows need no routing: while wavefronts 0..B-1 route one
-  // token each, the other wavefronts stream them (when B fills the workgroup, every
-  // wavefront streams them after the routing).
-  auto shared_rows = [&](int first, int stride) __attribute__((always_inline)) {
-    for (int i = first; i < fs; i += stride) {
-      u32x4 wg[NQ], wu[NQ];
-      load_row<NQ>(p.ws_gate + (int64_t)i * d, wg);
-      load_row<NQ>(p.ws_up + (int64_t)i * d, wu);
-      for (int b = 0; b < B; ++b) {
-        float sa, su;
-        part_dot2<NQ>(wg, wu, xs + b * d, sa, su);
-        const float a = wave_sum(sa), u = wave_sum(su);
-        if (lane == 0) p.hs[b * fs + i] = silu(a) * u;
-      }
-    }
-  };
-  const int nr = nwave - min(B, nwave);   // wavefronts of a workgroup that do not route
-  if (nr > 0 && wave >= B) shared_rows(blockIdx.x * nr + (wave - B), gridDim.x * nr);
-  // routing, one wavefront per token.  The logits (four partial planes + bias) of
-  // all of the lane's experts are loaded unconditionally (indices clamped, values
-  // past E masked afterwards), so the loads go out together instead of one guarded
-  // group after another.
-  for (int b = wave; b < B; b += nwave) {
-    int choice, rank;
-    float gate;
-    const float* l0 = p.logits + (int64_t)b * E;
+  // The logits (four partial planes + bias) of all of the lane's experts, loaded
+  // unconditionally (indices clamped, values past E masked afterwards) so the loads go
+  // out together, and before any weight row is requested.
+  float lv[16];
+  if (routes) {
+    const float* l0 = p.logits + (int64_t)wave * E;
     const int64_t ps = (int64_t)B * E;   // stride between the partial-logit planes
-    float lv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int e = min(lane + 64 * i, E - 1);
       lv[i] = (((l0[e] + l0[ps + e]) + l0[2 * ps + e]) + l0[3 * ps + e]) + (p.b_r ? p.b_r[e] : 0.f);
     }
+  }
+  for (int v = tid; v < B * d / 8; v += DEC_THREADS) ((u32x4*)xs)[v] = ((const u32x4*)p.x)[v];
+  for (int w = tid; w < (E + 31) / 32; w += DEC_THREADS) bits[w] = 0u;
+  if (tid == 0) {
+    claims = 0;
+    routed = 0;
+    ready = 0;
+  }
+  __syncthreads();
+
+  if (routes) {
+    int choice, rank;
+    float gate;
     wave_route_row_f<16>([&](int e) { return lv[(e - lane) >> 6]; }, E, k, choice, rank, gate);
     if (lane < k) {
-      sel[b * DEC_KMAX + rank] = choice;             // ascending expert id
+      sel[wave * DEC_KMAX + rank] = choice;          // ascending expert id
       if (blockIdx.x == 0) {
-        p.topk_idx[b * k + rank] = choice;
-        p.topk_gate[b * k + rank] = gate;
+        p.topk_idx[wave * k + rank] = choice;
+        p.topk_gate[wave * k + rank] = gate;
+      }
+    }
+    int done = 0;
+    if (lane == 0) done = __hip_atomic_fetch_add(&routed, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (__builtin_amdgcn_readfirstlane(done) == B - 1) {
+      // the last routing wavefront: the distinct experts, ascending
+      for (int q = lane; q < B * k; q += 64) {
+        const int e = sel[(q / k) * DEC_KMAX + q % k];
+        atomicOr(&bits[e >> 5], 1u << (e & 31));
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");   // every lane's bits before lane 0 reads them
+      if (lane == 0) {
+        int u = 0;
+        for (int w = 0; w < (E + 31) / 32; ++w)
+          for (uint32_t m = bits[w]; m; m &= m - 1) uniq[u++] = w * 32 + __builtin_ctz(m);
+        *nuniq = u;
+        if (blockIdx.x == 0) {     // the list kernel 2 reads
+          for (int q = 0; q < u; ++q) p.uniq[q] = uniq[q];
+          p.uniq[DEC_BMAX * DEC_KMAX] = u;
+        }
+        __hip_atomic_store(&ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
   }
-  __syncthreads();
-  for (int q = tid; q < B * k; q += DEC_THREADS) {
-    const int e = sel[(q / k) * DEC_KMAX + q % k];
-    atomicOr(&bits[e >> 5], 1u << (e & 31));
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int u = 0;
-    for (int w = 0; w < (E + 31) / 32; ++w)
-      for (uint32_t m = bits[w]; m; m &= m - 1) uniq[u++] = w * 32 + __builtin_ctz(m);
-    *nuniq = u;
-    if (blockIdx.x == 0) {       // the list kernel 2 reads
-      for (int q = 0; q < u; ++q) p.uniq[q] = uniq[q];
-      p.uniq[DEC_BMAX * DEC_KMAX] = u;
+
+  // The next row of this wavefront, or -1 once the workgroup's rows are all claimed (or
+  // the expert list never came).  Once the list is ready, lane l keeps the experts of the
+  // (token, slot) pairs l and l + 64 (16 bits each, 0xffff for none: E <= 1024), so a
+  // row's pairs are two ballots.
+  bool listed = false;
+  uint32_t pe = 0xffffffffu;
+  auto next = [&]() __attribute__((always_inline)) -> int {
+    int c = 0;
+    if (lane == 0) c = __hip_atomic_fetch_add(&claims, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    c = __builtin_amdgcn_readfirstlane(c);
+    const int g = blockIdx.x * nwave + c % nwave + (c / nwave) * W;
+    if (g < fs) return g;
+    if (!listed) {
+      for (int n = 0; n < DEC_SPIN_MAX && !listed; ++n) {
+        listed = __hip_atomic_load(&ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0;
+        if (!listed) __builtin_amdgcn_s_sleep(1);
+      }
+      if (!listed) return -1;
+      const int q0 = lane, q1 = lane + 64;
+      const uint32_t e0 = q0 < B * k ? (uint32_t)sel[(q0 / k) * DEC_KMAX + q0 % k] : 0xffffu;
+      const uint32_t e1 = q1 < B * k ? (uint32_t)sel[(q1 / k) * DEC_KMAX + q1 % k] : 0xffffu;
+      pe = e0 | e1 << 16;
     }
-  }
-  __syncthreads();
-  // the shared expert's rows (if the routing did not overlap them), then the selected
-  // experts' rows, as one sequence of rows dealt round-robin to the wavefronts
-  const int first = nr > 0 ? gw : gw - fs % W + (gw < fs % W ? W : 0);
-  if (nr == 0) shared_rows(gw, W);
-  const int U = *nuniq;
-  for (int item = first; item < U * f; item += W) {
-    const int e = uniq[item / f], i = item % f;
-    u32x4 wg[NQ], wu[NQ];
-    load_row<NQ>(p.w_gate + ((int64_t)e * f + i) * d, wg);
-    load_row<NQ>(p.w_up + ((int64_t)e * f + i) * d, wu);
-    unsigned long long m0, m1;
-    pairs_of(sel, B, k, e, m0, m1);
+    return g < fs + *nuniq * f ? g : -1;
+  };
+  // the W_gate and W_up rows of row g (routed rows only once the expert list is ready)
+  auto load = [&](int g, u32x4(&wg)[NQ], u32x4(&wu)[NQ]) __attribute__((always_inline)) {
+    const bf16_t *rg, *ru;
+    if (g < fs) {
+      rg = p.ws_gate + (int64_t)g * d;
+      ru = p.ws_up + (int64_t)g * d;
+    } else {
+      const int it = g - fs, e = uniq[it / f], i = it % f;
+      rg = p.w_gate + ((int64_t)e * f + i) * d;
+      ru = p.w_up + ((int64_t)e * f + i) * d;
+    }
+    load_row<NQ>(rg, wg);
+    load_row<NQ>(ru, wu);
+  };
+  // hs[b][g] = silu(a) u for every token (shared row), or h[b][j][i] for every token b
+  // that chose the row's expert as its j-th
+  auto consume = [&](int g, const u32x4(&wg)[NQ], const u32x4(&wu)[NQ]) __attribute__((always_inline)) {
+    if (g < fs) {
+      for (int b = 0; b < B; ++b) {
+        float sa, su;
+        part_dot2<NQ>(wg, wu, xs + b * d, sa, su);
+        const float a = wave_sum(sa), u = wave_sum(su);
+        if (lane == 0) p.hs[b * fs + g] = silu(a) * u;
+      }
+      return;
+    }
+    const int it = g - fs, e = uniq[it / f], i = it % f;
+    const unsigned long long m0 = __ballot((pe & 0xffffu) == (uint32_t)e), m1 = __ballot(pe >> 16 == (uint32_t)e);
     for (int half = 0; half < 2; ++half)
       for (unsigned long long m = half ? m1 : m0; m; m &= m - 1) {
         const int q = half * 64 + __builtin_ctzll(m), b = q / k, j = q % k;
@@ -256,6 +312,15 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_k1(DecodeArgs p) {
         const float a = wave_sum(sa), u = wave_sum(su);
         if (lane == 0) p.h[((int64_t)b * k + j) * f + i] = silu(a) * u;
       }
+  };
+
+  // One row in flight per wavefront: a second register set (the next row's loads issued
+  // before this row is consumed) measured slower at B = 1 / 4 / 8 (132.6 / 451 / 838 us
+  // against 130.7 / 449 / 831): 2,048 wavefronts already keep ~57 MB in flight.
+  u32x4 wg[NQ], wu[NQ];
+  for (int row = next(); row >= 0; row = next()) {
+    load(row, wg, wu);
+    consume(row, wg, wu);
   }
 }
 
