@@ -503,12 +503,6 @@ __device__ __forceinline__ T bld_meta(const T* q) {   // scalar load of data wri
   return *(const __attribute__((address_space(4))) T*)q;
 }
 
-// Two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
-}
 
 struct WgradArgs {
   const bf16_t* A;          // ring-ordered rows: DOWN dy gathered into ring order [C, d]; UP dAU [C, 2f]
@@ -667,8 +661,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void wgrad_kernel(WgradArgs p)
         const f32x16& a = acc[jn][i];
         // x: columns 16h + 4lg + 0..3, y: columns 16h + 8 + 4lg + 0..3.  The swap hands
         // x of lanes 32..63 to lanes 0..31 and y of lanes 0..31 to lanes 32..63.
-        const uint32_t x0 = cvt_pk_bf16(a[8 * h + 0], a[8 * h + 1]), x1 = cvt_pk_bf16(a[8 * h + 2], a[8 * h + 3]);
-        const uint32_t y0 = cvt_pk_bf16(a[8 * h + 4], a[8 * h + 5]), y1 = cvt_pk_bf16(a[8 * h + 6], a[8 * h + 7]);
+        const uint32_t x0 = pack_bf2(a[8 * h + 0], a[8 * h + 1]), x1 = pack_bf2(a[8 * h + 2], a[8 * h + 3]);
+        const uint32_t y0 = pack_bf2(a[8 * h + 4], a[8 * h + 5]), y1 = pack_bf2(a[8 * h + 6], a[8 * h + 7]);
         const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
         const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
         const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
