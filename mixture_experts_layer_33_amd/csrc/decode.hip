@@ -416,6 +416,85 @@ __global__ __launch_bounds__(256) void decode_k2(DecodeArgs p) {
     }
 }
 
+// Kernel 2 for one token (B = 1).  Its k experts are distinct and topk_idx lists them
+// ascending, so expert u of the sequence (u < k, then the shared expert) has exactly one
+// h row, h[u] (hs for the shared one), and the gate topk_gate[u].  A wavefront keeps two
+// experts in flight: the W_down rows and the h row of expert u + 1 are requested before
+// expert u is consumed, so waiting for expert u never waits for anything issued after it
+// (vector memory operations complete in issue order; decode_k2, whose h rows are read as
+// each expert is consumed, cannot prefetch that way).  The products and sums are those of
+// decode_k2 in the same order: bitwise the same y.
+template <int NF>   // f = fs (when present) = NF * 512
+__global__ __launch_bounds__(256) void decode_k2_one(DecodeArgs p) {
+  __shared__ int32_t ex[DEC_KMAX];
+  __shared__ float gt[DEC_KMAX];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int d = p.d, k = p.k, fs = p.fs;
+  constexpr int ff = NF * 512;
+  if (tid < k) {
+    ex[tid] = p.topk_idx[tid];
+    gt[tid] = p.topk_gate[tid];
+  }
+  __syncthreads();
+  const int o0 = (blockIdx.x * 4 + (tid >> 6)) * DEC_R;
+  if (o0 >= d) return;
+  const int U = k + (fs > 0 ? 1 : 0);
+  auto fetch = [&](int u, u32x4(&w)[DEC_R][NF], f32x4(&h)[NF][2]) __attribute__((always_inline)) {
+    const bool shared = u == k;
+    const bf16_t* wbase = shared ? p.ws_down : p.w_down + (int64_t)ex[u] * d * ff;
+#pragma unroll
+    for (int r = 0; r < DEC_R; ++r) {
+      const int o = min(o0 + r, d - 1);
+#pragma unroll
+      for (int c = 0; c < NF; ++c)
+        w[r][c] = __builtin_nontemporal_load((const u32x4*)(wbase + (int64_t)o * ff + c * 512 + lane * 8));
+    }
+    const float* hv = shared ? p.hs : p.h + (int64_t)u * ff;
+#pragma unroll
+    for (int c = 0; c < NF; ++c) {
+      h[c][0] = *(const f32x4*)(hv + c * 512 + lane * 8);
+      h[c][1] = *(const f32x4*)(hv + c * 512 + lane * 8 + 4);
+    }
+  };
+  float acc[DEC_R] = {};
+  auto consume = [&](int u, const u32x4(&w)[DEC_R][NF], const f32x4(&h)[NF][2]) __attribute__((always_inline)) {
+    const float g = u == k ? 1.f : gt[u];
+    float s[DEC_R] = {};
+#pragma unroll
+    for (int c = 0; c < NF; ++c) {
+      const f32x4 h0 = h[c][0], h1 = h[c][1];
+#pragma unroll
+      for (int r = 0; r < DEC_R; ++r) {
+        s[r] = fmaf(lo_bf(w[r][c][0]), h0[0], s[r]);
+        s[r] = fmaf(hi_bf(w[r][c][0]), h0[1], s[r]);
+        s[r] = fmaf(lo_bf(w[r][c][1]), h0[2], s[r]);
+        s[r] = fmaf(hi_bf(w[r][c][1]), h0[3], s[r]);
+        s[r] = fmaf(lo_bf(w[r][c][2]), h1[0], s[r]);
+        s[r] = fmaf(hi_bf(w[r][c][2]), h1[1], s[r]);
+        s[r] = fmaf(lo_bf(w[r][c][3]), h1[2], s[r]);
+        s[r] = fmaf(hi_bf(w[r][c][3]), h1[3], s[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < DEC_R; ++r) acc[r] = fmaf(g, s[r], acc[r]);
+  };
+  u32x4 wa[DEC_R][NF], wb[DEC_R][NF];
+  f32x4 ha[NF][2], hb[NF][2];
+  fetch(0, wa, ha);
+  for (int u = 0; u < U; u += 2) {
+    if (u + 1 < U) fetch(u + 1, wb, hb);
+    consume(u, wa, ha);
+    if (u + 1 >= U) break;
+    if (u + 2 < U) fetch(u + 2, wa, ha);
+    consume(u + 1, wb, hb);
+  }
+#pragma unroll
+  for (int r = 0; r < DEC_R; ++r) {
+    const float v = wave_sum(acc[r]);
+    if (lane == 0 && o0 + r < d) p.y[o0 + r] = f2bf(v);
+  }
+}
+
 // Workspace: partial logits [DEC_RP,B,E] f32 | shared h [B,max(fs,1)] f32 |
 // h [B,k,f] f32 | unique-expert list [DEC_BMAX*DEC_KMAX + 1] i32.
 size_t decode_workspace_bytes(int B, int E, int k, int f, int fs) {
@@ -517,6 +596,15 @@ hipError_t launch_decode(const void* x, const float* w_r, const float* b_r, cons
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const unsigned g2 = (unsigned)(((d + DEC_R - 1) / DEC_R + 3) / 4);
+  if (B == 1 && f / 512 <= 4) {   // two experts in flight per wavefront (registers allow up to f = 2048)
+    switch (f / 512) {
+      case 1: decode_k2_one<1><<<g2, 256, 0, st>>>(a); break;
+      case 2: decode_k2_one<2><<<g2, 256, 0, st>>>(a); break;
+      case 3: decode_k2_one<3><<<g2, 256, 0, st>>>(a); break;
+      default: decode_k2_one<4><<<g2, 256, 0, st>>>(a); break;
+    }
+    return hipGetLastError();
+  }
   switch (f / 512) {
     case 1: decode_k2<1><<<g2, 256, 0, st>>>(a); break;
     case 2: decode_k2<2><<<g2, 256, 0, st>>>(a); break;

@@ -44,6 +44,12 @@ def check_decode(cfg, reps=5):
     LayerConfig("dec_small_b8_noshared", T=8, d=512, E=64, k=8, f=1024, fs=0, cid=41),
     LayerConfig("dec_small_b5_bias", T=5, d=1536, E=48, k=6, f=512, fs=512, zipf_s=1.1,
                 hot_ratio=4.0, cid=42),
+    # one token: the kernel that keeps two experts in flight (f up to 2048), with and
+    # without the shared expert, and an odd and an even number of experts
+    LayerConfig("dec_small_b1_noshared", T=1, d=1024, E=32, k=4, f=512, fs=0, cid=84),
+    LayerConfig("dec_small_b1_f1536", T=1, d=2560, E=40, k=6, f=1536, fs=1536, cid=85),
+    LayerConfig("dec_small_b1_k1", T=1, d=512, E=16, k=1, f=1024, fs=1024, cid=86),
+    LayerConfig("dec_small_b1_f2560", T=1, d=1024, E=24, k=3, f=2560, fs=2560, cid=87),
 ], ids=lambda c: c.name)
 def test_decode_small(cfg):
     print(f"\n[case] decode {cfg.name}", flush=True)
