@@ -521,6 +521,11 @@ __device__ __forceinline__ void gg_mfma_body(const GemmArgs p, int vb, uint8_t* 
     // reads them like the bf16 one), staged with a bf16 row stride
     constexpr int RS16 = (BN / 2) * 2 + 16, CPR16 = (BN / 2) * 2 / 16;
     static_assert(!SWIGLU || BM * RS16 <= S * SL::SIZE, "bf16 planes fit the stage ring");
+    // MX h plane: the 16 block exponents of each (fragment pair, half-wave), handed from
+    // the lanes that computed them to every lane of the half-wave through LDS past the
+    // staged planes
+    constexpr int XOFF = ((EL::SIZE > BM * RS16 ? EL::SIZE : BM * RS16) + 255) / 256 * 256;
+    static_assert(!MX || XOFF + NW * FM * HALF * 2 * 16 <= S * SL::SIZE, "exponent bytes fit the ring");
     auto stage_plane = [&](auto plane_tag) __attribute__((always_inline)) {
       constexpr int plane = decltype(plane_tag)::value;
       // beside MX codes the lane's row and column are re-derived per plane, so that no
@@ -532,21 +537,62 @@ __device__ __forceinline__ void gg_mfma_body(const GemmArgs p, int vb, uint8_t* 
 #pragma unroll
         for (int j = 0; j < HALF; ++j) {
           const int cl = wn * (WTN / 2) + j * 32 + plr;   // column inside the tile
+          if constexpr (MX && plane == 0) {
+            // The 32 columns of a row's block sit in the 32 lanes of a half-wave, and a
+            // lane holds 16 rows (r).  Halving exchanges give each lane the block maximum
+            // of one row: with partners lane ^ 16 (permlane16 swap), ^ 15 (row mirror),
+            // ^ 7 (half-row mirror), ^ 2 and ^ 1 (quad permutations), each step keeps
+            // half of the rows still held and takes the partner's values of the same rows;
+            // lane l ends with row rr = 8 b4 + 4 b3 + 2 b2 + b1 (bits of l mod 32).  That
+            // is 8 + 4 + 2 + 1 + 1 cross-lane moves for the 16 rows instead of 5 per row,
+            // one block exponent per row instead of one per value, and one store
+            // instruction for 16 rows' scale bytes.  Maxima are exact in any order: the
+            // same codes and scales as a per-row reduction.
+            float hv[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = wm * WTM + i * 32 + 8 * (r / 4) + 4 * plg + (r % 4);
-            const float a = acc[i][j][r], u = acc[i][j + HALF][r];
-            if constexpr (MX && plane == 0) {
-              const float h = silu(a) * u;
-              // the 32 columns of one row's block sit in the 32 lanes of a half-wave
-              const float am = group_max<32>(fabsf(h));
-              const int X = mx_block_exp(am);
-              stg[m * EL::RS + cl] = (uint8_t)e4m3_encode(h, X);
-              const int col = n0 + cl;
-              if (plr == 0 && m < rows && col < p.N)
+            for (int r = 0; r < 16; ++r) hv[r] = silu(acc[i][j][r]) * acc[i][j + HALF][r];
+            auto dpp = [](float v, auto ctrl) __attribute__((always_inline)) {
+              return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, false));
+            };
+            float t8[8], t4[4], t2[2];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_int(fabsf(hv[q])),
+                                                               __float_as_int(fabsf(hv[q + 8])), false, false);
+              t8[q] = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
+            }
+            const bool b3 = plr & 8, b2 = plr & 4, b1 = plr & 2;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              t4[q] = fmaxf(b3 ? t8[q + 4] : t8[q], dpp(b3 ? t8[q] : t8[q + 4], std::integral_constant<int, 0x140>{}));
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+              t2[q] = fmaxf(b2 ? t4[q + 2] : t4[q], dpp(b2 ? t4[q] : t4[q + 2], std::integral_constant<int, 0x141>{}));
+            float t1 = fmaxf(b1 ? t2[1] : t2[0], dpp(b1 ? t2[0] : t2[1], std::integral_constant<int, 0x4E>{}));
+            t1 = fmaxf(t1, dpp(t1, std::integral_constant<int, 0xB1>{}));
+            const int X = mx_block_exp(t1);
+            const int rr = ((plr >> 4) & 1) * 8 + ((plr >> 3) & 1) * 4 + ((plr >> 2) & 1) * 2 + ((plr >> 1) & 1);
+            uint8_t* xb = lds + XOFF + (((wave * FM + i) * HALF + j) * 2 + plg) * 16;
+            if ((plr & 1) == 0) {
+              xb[rr] = (uint8_t)(X + 127);
+              const int m = wm * WTM + i * 32 + 8 * (rr / 4) + 4 * plg + (rr % 4);
+              const int col = n0 + wn * (WTN / 2) + j * 32;   // the block's first column
+              if (m < rows && col < p.N)
                 p.out_scale[((int64_t)(col / 128) * p.C + ring_slot(p.head, seg, row0 + m, p.C)) * 4 +
                             (col / 32) % 4] = (uint8_t)(X + 127);
-            } else {
+            }
+            const u32x4 xw = *(const u32x4*)xb;   // the half-wave's 16 exponents (one wave: in order)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int m = wm * WTM + i * 32 + 8 * (r / 4) + 4 * plg + (r % 4);
+              const int Xr = (int)((xw[r / 4] >> (8 * (r % 4))) & 0xffu) - 127;
+              stg[m * EL::RS + cl] = (uint8_t)e4m3_encode(hv[r], Xr);
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int m = wm * WTM + i * 32 + 8 * (r / 4) + 4 * plg + (r % 4);
+              const float a = acc[i][j][r], u = acc[i][j + HALF][r];
               const float v = plane == 0 ? silu(a) * u : plane == 1 ? a : u;
               *(uint16_t*)(stg + m * (MX ? RS16 : EL::RS) + cl * 2) = f2bf(v);
             }
