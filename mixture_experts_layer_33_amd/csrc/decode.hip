@@ -25,6 +25,7 @@
 // used once per call, and on gfx950 such streaming loads reach a higher HBM rate
 // (a bare 16-byte-per-lane read: about 6.9 against 6.2 TB/s; at B = 1 the call went
 // from 154.6 to 138-141 us) while W_r, x and h keep the default policy.
+#include <algorithm>
 #include <mutex>
 
 #include "common.h"
@@ -39,6 +40,13 @@ constexpr int DEC_RP = 4;        // router row parts (kernel 0)
 constexpr int DQ = 16;           // largest row, in groups of 512 elements (d <= 8192)
 constexpr int DEC_R = 4;         // output rows per wavefront in kernel 2
 constexpr int DEC_NF = 8;        // largest f (and fs) in groups of 512 in kernel 2
+// Kernel 2's workgroups hold ceil(ceil(d / DEC_R) / CUs) wavefronts (at most this many), so
+// every CU gets one workgroup and an equal share of the output rows: with four-wavefront
+// workgroups (448 at d = 7168) three quarters of the CUs ran two of them and finished last.
+// Rows of more than 5 x 512 elements keep four-wavefront workgroups: at two wavefronts per
+// SIMD their two register sets would spill.
+constexpr int DEC_K2_MAXW = 8;
+__host__ __device__ constexpr int dec_k2_maxw(int nf) { return nf <= 5 ? DEC_K2_MAXW : 4; }
 
 struct DecodeArgs {
   const bf16_t* x;
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_k1(DecodeArgs p) {
 // g * <row, h> for each token that chose the expert into per-lane partials;
 // one fixed-order wave reduction per (row, token) at the end.
 template <int NF>   // f = fs (when present) = NF * 512
-__global__ __launch_bounds__(256) void decode_k2(DecodeArgs p) {
+__global__ __launch_bounds__(64 * dec_k2_maxw(NF)) void decode_k2(DecodeArgs p) {
   __shared__ int32_t sel[DEC_BMAX * DEC_KMAX];
   __shared__ float gate[DEC_BMAX * DEC_KMAX];
   __shared__ int32_t uniq[DEC_BMAX * DEC_KMAX];
@@ -337,19 +345,19 @@ __global__ __launch_bounds__(256) void decode_k2(DecodeArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int B = p.B, d = p.d, k = p.k, f = p.f, fs = p.fs;
   (void)f;
-  for (int q = tid; q < DEC_BMAX * DEC_KMAX; q += 256) {
+  for (int q = tid; q < DEC_BMAX * DEC_KMAX; q += blockDim.x) {
     sel[q] = -1;
     gate[q] = 0.f;
     uniq[q] = p.uniq[q];
   }
   if (tid == 0) nuniq = p.uniq[DEC_BMAX * DEC_KMAX];
   __syncthreads();
-  for (int q = tid; q < B * k; q += 256) {   // b < B <= 8, j < k <= 16: index < 128
+  for (int q = tid; q < B * k; q += blockDim.x) {   // b < B <= 8, j < k <= 16: index < 128
     sel[(q / k) * DEC_KMAX + q % k] = p.topk_idx[q];
     gate[(q / k) * DEC_KMAX + q % k] = p.topk_gate[q];
   }
   __syncthreads();
-  const int o0 = (blockIdx.x * 4 + (tid >> 6)) * DEC_R;
+  const int o0 = (int)(blockIdx.x * (blockDim.x >> 6) + (tid >> 6)) * DEC_R;
   if (o0 >= d) return;
   float acc[DEC_R][DEC_BMAX];
 #pragma unroll
@@ -425,7 +433,7 @@ __global__ __launch_bounds__(256) void decode_k2(DecodeArgs p) {
 // each expert is consumed, cannot prefetch that way).  The products and sums are those of
 // decode_k2 in the same order: bitwise the same y.
 template <int NF>   // f = fs (when present) = NF * 512
-__global__ __launch_bounds__(256) void decode_k2_one(DecodeArgs p) {
+__global__ __launch_bounds__(64 * DEC_K2_MAXW) void decode_k2_one(DecodeArgs p) {
   __shared__ int32_t ex[DEC_KMAX];
   __shared__ float gt[DEC_KMAX];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -436,7 +444,7 @@ __global__ __launch_bounds__(256) void decode_k2_one(DecodeArgs p) {
     gt[tid] = p.topk_gate[tid];
   }
   __syncthreads();
-  const int o0 = (blockIdx.x * 4 + (tid >> 6)) * DEC_R;
+  const int o0 = (int)(blockIdx.x * (blockDim.x >> 6) + (tid >> 6)) * DEC_R;
   if (o0 >= d) return;
   const int U = k + (fs > 0 ? 1 : 0);
   auto fetch = [&](int u, u32x4(&w)[DEC_R][NF], f32x4(&h)[NF][2]) __attribute__((always_inline)) {
@@ -595,25 +603,27 @@ hipError_t launch_decode(const void* x, const float* w_r, const float* b_r, cons
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const unsigned g2 = (unsigned)(((d + DEC_R - 1) / DEC_R + 3) / 4);
+  const int waves2 = (d + DEC_R - 1) / DEC_R;
+  const int nw2 = std::min(dec_k2_maxw(f / 512), std::max(1, (waves2 + ncu - 1) / ncu));
+  const unsigned g2 = (unsigned)((waves2 + nw2 - 1) / nw2), t2 = (unsigned)(64 * nw2);
   if (B == 1 && f / 512 <= 4) {   // two experts in flight per wavefront (registers allow up to f = 2048)
     switch (f / 512) {
-      case 1: decode_k2_one<1><<<g2, 256, 0, st>>>(a); break;
-      case 2: decode_k2_one<2><<<g2, 256, 0, st>>>(a); break;
-      case 3: decode_k2_one<3><<<g2, 256, 0, st>>>(a); break;
-      default: decode_k2_one<4><<<g2, 256, 0, st>>>(a); break;
+      case 1: decode_k2_one<1><<<g2, t2, 0, st>>>(a); break;
+      case 2: decode_k2_one<2><<<g2, t2, 0, st>>>(a); break;
+      case 3: decode_k2_one<3><<<g2, t2, 0, st>>>(a); break;
+      default: decode_k2_one<4><<<g2, t2, 0, st>>>(a); break;
     }
     return hipGetLastError();
   }
   switch (f / 512) {
-    case 1: decode_k2<1><<<g2, 256, 0, st>>>(a); break;
-    case 2: decode_k2<2><<<g2, 256, 0, st>>>(a); break;
-    case 3: decode_k2<3><<<g2, 256, 0, st>>>(a); break;
-    case 4: decode_k2<4><<<g2, 256, 0, st>>>(a); break;
-    case 5: decode_k2<5><<<g2, 256, 0, st>>>(a); break;
-    case 6: decode_k2<6><<<g2, 256, 0, st>>>(a); break;
-    case 7: decode_k2<7><<<g2, 256, 0, st>>>(a); break;
-    case 8: decode_k2<8><<<g2, 256, 0, st>>>(a); break;
+    case 1: decode_k2<1><<<g2, t2, 0, st>>>(a); break;
+    case 2: decode_k2<2><<<g2, t2, 0, st>>>(a); break;
+    case 3: decode_k2<3><<<g2, t2, 0, st>>>(a); break;
+    case 4: decode_k2<4><<<g2, t2, 0, st>>>(a); break;
+    case 5: decode_k2<5><<<g2, t2, 0, st>>>(a); break;
+    case 6: decode_k2<6><<<g2, t2, 0, st>>>(a); break;
+    case 7: decode_k2<7><<<g2, t2, 0, st>>>(a); break;
+    case 8: decode_k2<8><<<g2, t2, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
