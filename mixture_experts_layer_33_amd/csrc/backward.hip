@@ -912,11 +912,8 @@ __global__ __launch_bounds__(256) void gather_mx_kernel(const bf16_t* __restrict
     for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(fv[q]));
     am = group_max<4>(am);
     const int X = mx_block_exp(am);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lo |= e4m3_encode(fv[q], X) << (8 * q);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) hi |= e4m3_encode(fv[4 + q], X) << (8 * q);
+    const uint32_t lo = e4m3_encode4(fv[0], fv[1], fv[2], fv[3], X);
+    const uint32_t hi = e4m3_encode4(fv[4], fv[5], fv[6], fv[7], X);
     if (ok)
       for (int j = 0; j < k; ++j) {
         *(u32x2*)(codes + slots[j] * d + (int64_t)v * 8) = u32x2{lo, hi};
@@ -990,14 +987,10 @@ __global__ __launch_bounds__(256) void swiglu_bwd_mx_kernel(
         pu[1] = f32x4{du[4], du[5], du[6], du[7]};
         ph[0] = f32x4{hh[0], hh[1], hh[2], hh[3]};
         ph[1] = f32x4{hh[4], hh[5], hh[6], hh[7]};
-        uint32_t ca0 = 0, ca1 = 0, cu0 = 0, cu1 = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          ca0 |= e4m3_encode(da[q], Xa) << (8 * q);
-          ca1 |= e4m3_encode(da[4 + q], Xa) << (8 * q);
-          cu0 |= e4m3_encode(du[q], Xu) << (8 * q);
-          cu1 |= e4m3_encode(du[4 + q], Xu) << (8 * q);
-        }
+        const uint32_t ca0 = e4m3_encode4(da[0], da[1], da[2], da[3], Xa);
+        const uint32_t ca1 = e4m3_encode4(da[4], da[5], da[6], da[7], Xa);
+        const uint32_t cu0 = e4m3_encode4(du[0], du[1], du[2], du[3], Xu);
+        const uint32_t cu1 = e4m3_encode4(du[4], du[5], du[6], du[7], Xu);
         *(u32x2*)(dau_q + s * 2 * f + (int64_t)v * 8) = u32x2{ca0, ca1};
         *(u32x2*)(dau_q + s * 2 * f + f + (int64_t)v * 8) = u32x2{cu0, cu1};
         if ((v & 3) == 0) {

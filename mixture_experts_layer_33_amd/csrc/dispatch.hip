@@ -109,11 +109,8 @@ __global__ __launch_bounds__(256) void dispatch_mx_kernel(
     for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(f[q]));
     am = group_max<4>(am);
     const int X = mx_block_exp(am);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lo |= e4m3_encode(f[q], X) << (8 * q);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) hi |= e4m3_encode(f[4 + q], X) << (8 * q);
+    const uint32_t lo = e4m3_encode4(f[0], f[1], f[2], f[3], X);
+    const uint32_t hi = e4m3_encode4(f[4], f[5], f[6], f[7], X);
     if (ok)
       for (int j = 0; j < k; ++j) {
         *(u32x2*)(ring + slots[j] * d + (int64_t)v * 8) = u32x2{lo, hi};

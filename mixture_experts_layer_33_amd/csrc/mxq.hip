@@ -34,11 +34,8 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const bf16_t* __restri
     for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(f[q]));
     am = group_max<4>(am);
     const int X = mx_block_exp(am);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lo |= e4m3_encode(f[q], X) << (8 * q);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) hi |= e4m3_encode(f[4 + q], X) << (8 * q);
+    const uint32_t lo = e4m3_encode4(f[0], f[1], f[2], f[3], X);
+    const uint32_t hi = e4m3_encode4(f[4], f[5], f[6], f[7], X);
     if (ok) {
       ((u32x2*)codes)[v] = u32x2{lo, hi};
       if ((v & 3) == 0) {   // block cb of row r: vpr = cols / 8 vectors per row
@@ -77,9 +74,7 @@ __global__ __launch_bounds__(256) void quantize_mx_t_kernel(const bf16_t* __rest
     uint32_t w[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      w[u] = 0;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) w[u] |= e4m3_encode(v[4 * u + q4], X) << (8 * q4);
+      w[u] = e4m3_encode4(v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3], X);
     }
     const int64_t row = b * Cc + c, col = col0 + q * 32;
     u32x4* dst = (u32x4*)(codes + row * ld + col);
@@ -148,9 +143,7 @@ __global__ __launch_bounds__(256) void quantize_mx_both_kernel(
         uint32_t w32[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          w32[u] = 0;
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) w32[u] |= e4m3_encode(v[4 * u + q4], X) << (8 * q4);
+          w32[u] = e4m3_encode4(v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3], X);
         }
         out[2 * blk] = u32x4{w32[0], w32[1], w32[2], w32[3]};
         out[2 * blk + 1] = u32x4{w32[4], w32[5], w32[6], w32[7]};
@@ -181,12 +174,8 @@ __global__ __launch_bounds__(256) void quantize_mx_both_kernel(
       const int X0 = mx_block_exp(a0), X1 = mx_block_exp(a1);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          w0 |= e4m3_encode(v0[4 * u + q4], X0) << (8 * q4);
-          w1 |= e4m3_encode(v1[4 * u + q4], X1) << (8 * q4);
-        }
+        const uint32_t w0 = e4m3_encode4(v0[4 * u], v0[4 * u + 1], v0[4 * u + 2], v0[4 * u + 3], X0);
+        const uint32_t w1 = e4m3_encode4(v1[4 * u], v1[4 * u + 1], v1[4 * u + 2], v1[4 * u + 3], X1);
         *(uint32_t*)(tile + (2 * p) * QB_TS + 32 * q + 4 * u) = w0;
         *(uint32_t*)(tile + (2 * p + 1) * QB_TS + 32 * q + 4 * u) = w1;
       }
@@ -194,15 +183,17 @@ __global__ __launch_bounds__(256) void quantize_mx_both_kernel(
       tscb[(2 * p + 1) * 4 + q] = (uint8_t)(X1 + 127);
     }
     __syncthreads();
-    // destination row c0 + c of item b (c = t / 2), bytes col0 + r0 + 64 (t % 2) .. + 63
+    // destination rows c0 + c of item b, bytes col0 + r0 .. + 127: per store instruction a
+    // wave writes 8 whole rows (consecutive lanes take consecutive 16-byte pieces); two
+    // lanes per row, a quarter row per instruction, took 5.400 ms against 5.354 for the
+    // skewed training weights
     {
-      const int c = t >> 1, h = t & 1;
-      const int64_t drow = b * Cc + c0 + c;
-      const u32x4* sl = (const u32x4*)(tile + c * QB_TS + h * 64);
-      u32x4* dst = (u32x4*)(codes_t + drow * ld + col0 + r0 + h * 64);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) dst[k] = sl[k];
-      if (h == 0) ((uint32_t*)scales_t)[((col0 + r0) / 128) * (batch * Cc) + drow] = ((const uint32_t*)tscb)[c];
+      for (int k = 0; k < 4; ++k) {
+        const int id = k * 256 + t, c = id >> 3, ch = id & 7;
+        *(u32x4*)(codes_t + (b * Cc + c0 + c) * ld + col0 + r0 + ch * 16) = *(const u32x4*)(tile + c * QB_TS + ch * 16);
+      }
+      if (t < QB_T) ((uint32_t*)scales_t)[((col0 + r0) / 128) * (batch * Cc) + b * Cc + c0 + t] = ((const uint32_t*)tscb)[t];
     }
     __syncthreads();   // before the next tile overwrites the LDS
   }
