@@ -6,8 +6,8 @@
 //
 // One workgroup of 512 threads (eight waves, the GEMM tile's) per CU; every workgroup
 // runs the phases in order and waits at a grid barrier between them:
-//   P0 W_r split into three exact bf16 planes     P5 every token row copied to its k slots
-//   P1 router logit tiles (MFMA)                   P6 gate/up GEMM tiles, SwiGLU epilogue
+//   P1 router logit tiles (MFMA, W_r split into     P5 every token row copied to its k slots
+//      its bf16 planes as it is staged)            P6 gate/up GEMM tiles, SwiGLU epilogue
 //   P2 top-k and gates, one wavefront per token    P7 down GEMM tiles
 //   P3 per-chunk expert masks                      P8 gate-weighted combine per token
 //   P4 (workgroup 0) offsets, counts, tile list
@@ -24,7 +24,8 @@
 // phases taking the time of the separate GEMMs (2.29 | 1.34 ms per workgroup); each grid
 // barrier costs about 15 us from the last arrival to the release (the arriving
 // workgroup's L2 write-back, which cross-XCD visibility needs, is on the critical path),
-// eight of them about 0.12 ms.  Earlier forms: an acquire load in the polling loop
+// eight of them about 0.12 ms.  (W_r's bf16 planes were then a phase of their own; made
+// while the logit tiles stage W_r, they save that phase and its barrier: 3.935 -> 3.910 ms.)  Earlier forms: an acquire load in the polling loop
 // invalidated the caches at every poll (about 30 us per barrier); a fixed assignment of
 // GEMM tiles to workgroups ended each GEMM phase 0.2 ms after its median workgroup; one
 // token per workgroup in the copy and combine phases was latency-bound (2x slower).
@@ -60,7 +61,6 @@ struct FusedArgs {
   int d, E, k, f;
   int64_t head, C;
   // router
-  bf16_t* w3;            // [3, E, d]
   float* logits;         // [ks, T, E]
   int ks;
   // dispatch
@@ -306,17 +306,13 @@ __global__ __launch_bounds__(FU_NT) void fused_forward_kernel(FusedArgs a) {
   // a barrier of an earlier call gave up: its state may be out of step, do nothing
   if (__hip_atomic_load(a.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 1u) return;
 
-  // P0: W_r into three bf16 planes
-  router_split_range(a.w_r, (int64_t)a.E * a.d, a.w3, (int64_t)b * FU_NT + tid, (int64_t)G * FU_NT);
-  if (!grid_sync(a, ok)) return;
-
   // P1: router logits, 128 tokens x 64 experts x K split z per tile
   {
     const int nbx = (a.E + 63) / 64, nby = (int)((a.T + 127) / 128);
     const int ntile = nbx * nby * a.ks;
     for (int v = b; v < ntile; v += G) {
       const int bx = v % nbx, by = (v / nbx) % nby, z = v / (nbx * nby);
-      router_mfma_body<128>(a.x, a.w3, a.logits, a.T, a.d, a.E, bx, by, z, a.ks, lds,
+      router_mfma_body<128>(a.x, a.w_r, a.logits, a.T, a.d, a.E, bx, by, z, a.ks, lds,
                             lds + 2 * 128 * RM_K);
       __syncthreads();
     }
@@ -375,10 +371,9 @@ __global__ __launch_bounds__(FU_NT) void fused_forward_kernel(FusedArgs a) {
 }
 
 // Workspace: [0, 256) ticket counter (8 bytes), status word (at byte 8), the GEMM phases'
-// tile counters (16 words at byte 64, reset inside every call) | W_r planes |
-// logit planes | chunk masks | chunk counts/bases | tile list | H.
+// tile counters (16 words at byte 64, reset inside every call) | logit planes | chunk masks | chunk counts/bases | tile list | H.
 struct FusedLayout {
-  size_t w3, logits, masks, base, tiles, H, total;
+  size_t logits, masks, base, tiles, H, total;
 };
 
 static FusedLayout fused_layout(int64_t T, int64_t C, int d, int E, int f) {
@@ -388,7 +383,6 @@ static FusedLayout fused_layout(int64_t T, int64_t C, int d, int E, int f) {
   const int64_t n_max_tiles = max_tiles_for(C, E, FU_BM);   // C >= n copies
   FusedLayout L;
   size_t o = 256;
-  L.w3 = o;     o += al((size_t)3 * E * d * 2);
   L.logits = o; o += al((size_t)ks * T * E * 4);
   L.masks = o;  o += al((size_t)nch * E * 8);
   L.base = o;   o += al((size_t)nch * E * 4);
@@ -418,7 +412,6 @@ hipError_t launch_forward_fused(const void* x, const float* w_r, const float* b_
   a.b_r = b_r;
   a.T = T; a.d = d; a.E = E; a.k = k; a.f = f;
   a.head = head; a.C = C;
-  a.w3 = (bf16_t*)(w + L.w3);
   a.logits = (float*)(w + L.logits);
   a.ks = router_ksplit(T, E, d);
   a.masks = (unsigned long long*)(w + L.masks);

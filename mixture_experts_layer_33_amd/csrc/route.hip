@@ -84,18 +84,15 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 // bf16 planes, w = hi + mid + lo (hi = bf16(w), mid = bf16(w - hi),
 // lo = w - hi - mid; 3 x 8 significand bits cover fp32's 24), so every product
 // x * w_plane of a bf16 x is exact in fp32 and the MFMA accumulates in fp32.
-__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ w,
-                                                           int64_t n, bf16_t* __restrict__ w3) {
-  router_split_range(w, n, w3, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256);
-}
+// The split is done in registers as each K slice of W_r is staged (router_split8).
 
 template <int BM>
 __global__ __launch_bounds__(BM * 4) void router_mfma_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w3, float* __restrict__ logits,
+    const bf16_t* __restrict__ x, const float* __restrict__ w_r, float* __restrict__ logits,
     int64_t T, int d, int E) {
   __shared__ __attribute__((aligned(16))) uint8_t As[2 * BM * RM_K];
   __shared__ __attribute__((aligned(16))) uint8_t Bs[2 * 192 * RM_K];
-  router_mfma_body<BM>(x, w3, logits, T, d, E, (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z,
+  router_mfma_body<BM>(x, w_r, logits, T, d, E, (int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z,
                        (int)gridDim.z, As, Bs);
 }
 
@@ -106,11 +103,15 @@ __global__ __launch_bounds__(BM * 4) void router_mfma_kernel(
 // flight in registers while the other is multiplied: a second register set would spill.
 constexpr int R2_BM = 128, R2_BN = 128, R2_NT = 1024;
 constexpr int R2_LDS = 2 * (R2_BM + 3 * R2_BN) * RM_K;
+//
+// W_r is read in fp32 and split into its three planes in registers (router_split8): thread q
+// takes 8 consecutive weights of expert row q / 8 per 64-wide K slice.
 __global__ __launch_bounds__(R2_NT) void router_mfma2_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w3, float* __restrict__ logits,
+    const bf16_t* __restrict__ x, const float* __restrict__ w_r, float* __restrict__ logits,
     int64_t T, int d, int E) {
   constexpr int BM = R2_BM, BNE = R2_BN, BNR = 3 * BNE, NT = R2_NT;
-  constexpr int A_LD = BM * 8 / NT, B_LD = BNR * 8 / NT;
+  constexpr int A_LD = BM * 8 / NT;
+  static_assert(BNE * 8 == NT, "one 8-weight group of one expert row per thread and slice");
   extern __shared__ __attribute__((aligned(16))) uint8_t r2lds[];
 #define AS2(buf) (r2lds + (buf) * (BM * RM_K))
 #define BS2(buf) (r2lds + 2 * BM * RM_K + (buf) * (BNR * RM_K))
@@ -118,29 +119,25 @@ __global__ __launch_bounds__(R2_NT) void router_mfma2_kernel(
   const int e0 = blockIdx.x * BNE;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3, lr = lane & 31, lg = lane >> 5;
-  const int64_t n = (int64_t)E * d;
   const int KS = gridDim.z, z = blockIdx.z, KA = d / 64;
   const int kb = (int)((int64_t)KA * z / KS);
   const int KT = (int)((int64_t)KA * (z + 1) / KS) - kb;
   const bf16_t* a_src[A_LD];
-  const bf16_t* b_src[B_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     const int q = tid + NT * i;
     const int64_t t = min(t0 + q / 8, T - 1);
     a_src[i] = x + t * d + (int64_t)kb * 64 + (q % 8) * 8;
   }
-#pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int q = tid + NT * i, r = q / 8;
-    const int e = min(e0 + r % BNE, E - 1);
-    b_src[i] = w3 + (r / BNE) * n + (int64_t)e * d + (int64_t)kb * 64 + (q % 8) * 8;
-  }
-  u32x4 ra0[A_LD], rb0[B_LD];
+  const int br = tid / 8, bc = tid % 8;   // this thread's expert row and 8-weight group
+  const float* b_src = w_r + (int64_t)min(e0 + br, E - 1) * d + (int64_t)kb * 64 + bc * 8;
+  u32x4 ra0[A_LD];
+  f32x4 rb0[2];
 #define R_LOAD(kt, RA, RB)                                                                   \
   {                                                                                          \
     _Pragma("unroll") for (int i = 0; i < A_LD; ++i) RA[i] = *(const u32x4*)(a_src[i] + (kt) * 64); \
-    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) RB[i] = *(const u32x4*)(b_src[i] + (kt) * 64); \
+    RB[0] = *(const f32x4*)(b_src + (kt) * 64);                                              \
+    RB[1] = *(const f32x4*)(b_src + (kt) * 64 + 4);                                          \
   }
 #define R_STORE(buf, RA, RB)                                                                 \
   {                                                                                          \
@@ -148,10 +145,11 @@ __global__ __launch_bounds__(R2_NT) void router_mfma2_kernel(
       const int q = tid + NT * i;                                                            \
       *(u32x4*)(AS2(buf) + rswz(q / 8, q % 8)) = RA[i];                                      \
     }                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) {                                      \
-      const int q = tid + NT * i;                                                            \
-      *(u32x4*)(BS2(buf) + rswz(q / 8, q % 8)) = RB[i];                                      \
-    }                                                                                        \
+    u32x4 ph, pm, pl;                                                                        \
+    router_split8(RB, ph, pm, pl);                                                           \
+    *(u32x4*)(BS2(buf) + rswz(br, bc)) = ph;                                                 \
+    *(u32x4*)(BS2(buf) + rswz(BNE + br, bc)) = pm;                                           \
+    *(u32x4*)(BS2(buf) + rswz(2 * BNE + br, bc)) = pl;                                       \
   }
   f32x16 acc[3];
 #pragma unroll
@@ -231,7 +229,7 @@ __global__ __launch_bounds__(1024) void expert_count_kernel(const int32_t* __res
 }
 
 size_t route_workspace_bytes(int64_t T, int E, int d) {
-  return logits_bytes(T, E, d) + (size_t)3 * E * d * 2;
+  return logits_bytes(T, E, d);
 }
 
 hipError_t launch_route(const void* x, bool x_f32, const float* w_r, const float* b_r, int64_t T,
@@ -243,19 +241,16 @@ hipError_t launch_route(const void* x, bool x_f32, const float* w_r, const float
     router_logits_kernel<true><<<g1, 256, 0, st>>>(x, w_r, logits, T, d, E);
   } else {
     // d % 64 == 0 for bf16 layers
-    bf16_t* w3 = (bf16_t*)((uint8_t*)logits + logits_bytes(T, E, d));
-    const int64_t n = (int64_t)E * d;
-    router_split_kernel<<<(unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096), 256, 0, st>>>(w_r, n, w3);
     ks = router_ksplit(T, E, d);
     if (router_big(E)) {
       hipError_t e = hipFuncSetAttribute((const void*)router_mfma2_kernel,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, R2_LDS);
       if (e != hipSuccess) return e;
       router_mfma2_kernel<<<dim3((unsigned)((E + 127) / 128), (unsigned)((T + 127) / 128), (unsigned)ks),
-                            R2_NT, R2_LDS, st>>>((const bf16_t*)x, w3, logits, T, d, E);
+                            R2_NT, R2_LDS, st>>>((const bf16_t*)x, w_r, logits, T, d, E);
     } else {
       router_mfma_kernel<64><<<dim3((unsigned)((E + 63) / 64), (unsigned)((T + 63) / 64), (unsigned)ks),
-                               256, 0, st>>>((const bf16_t*)x, w3, logits, T, d, E);
+                               256, 0, st>>>((const bf16_t*)x, w_r, logits, T, d, E);
     }
   }
   const unsigned g2 = (unsigned)((T + 3) / 4);

@@ -9,20 +9,17 @@
 
 namespace moe {
 
-// Elements i0, i0 + stride, ... of W_r ([E, d] flattened, n elements) into the three
-// bf16 planes w3[0 .. n), w3[n .. 2n), w3[2n .. 3n).
-__device__ __forceinline__ void router_split_range(const float* __restrict__ w, int64_t n,
-                                                   bf16_t* __restrict__ w3, int64_t i0,
-                                                   int64_t stride) {
-  for (int64_t i = i0; i < n; i += stride) {
-    const float v = w[i];
-    const bf16_t hi = f2bf(v);
-    const float r1 = v - bf2f(hi);
-    const bf16_t mid = f2bf(r1);
-    const bf16_t lo = f2bf(r1 - bf2f(mid));
-    w3[i] = hi;
-    w3[n + i] = mid;
-    w3[2 * n + i] = lo;
+// Eight consecutive fp32 weights into the three bf16 planes w = hi + mid + lo (hi = bf16(w),
+// mid = bf16(w - hi), lo = bf16(w - hi - mid), round to nearest even; the differences are
+// exact in fp32, and 3 x 8 significand bits cover fp32's 24), as packed 16-byte pieces.
+__device__ __forceinline__ void router_split8(const f32x4 (&w)[2], u32x4& hi, u32x4& mid, u32x4& lo) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float v0 = w[j / 2][2 * (j % 2)], v1 = w[j / 2][2 * (j % 2) + 1];
+    hi[j] = pack_bf2(v0, v1);
+    const float r0 = v0 - lo_bf(hi[j]), r1 = v1 - hi_bf(hi[j]);
+    mid[j] = pack_bf2(r0, r1);
+    lo[j] = pack_bf2(r0 - lo_bf(mid[j]), r1 - hi_bf(mid[j]));
   }
 }
 
@@ -39,24 +36,26 @@ __device__ __forceinline__ int rswz(int r, int c) { return r * RM_K + ((c ^ (r &
 
 // One workgroup's tile: expert tile bx (64 experts), token tile by (BM tokens), K split z
 // of KS; As / Bs: two LDS buffers of BM x RM_K and 192 x RM_K bytes each.
+// W_r is read in fp32 and split into its planes in registers (router_split8): 4 bytes per
+// weight instead of the planes' 6, and no separate split pass.
 template <int BM>
 __device__ __forceinline__ void router_mfma_body(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w3, float* __restrict__ logits,
+    const bf16_t* __restrict__ x, const float* __restrict__ w_r, float* __restrict__ logits,
     int64_t T, int d, int E, int bx, int by, int z, int KS, uint8_t* As0, uint8_t* Bs0) {
-  constexpr int NT = BM * 4, BNR = 192;          // threads; B rows = 3 planes x 64 experts
-  constexpr int A_LD = BM * 8 / NT, B_LD = BNR * 8 / NT;
+  constexpr int NT = BM * 4;                     // threads; B rows = 3 planes x 64 experts
+  constexpr int A_LD = BM * 8 / NT, BG = 64 * 8 / NT;   // 8-weight groups per thread and slice
+  static_assert(64 * 8 % NT == 0, "whole 8-weight groups per thread");
   auto As = [&](int buf) { return As0 + buf * (BM * RM_K); };
-  auto Bs = [&](int buf) { return Bs0 + buf * (BNR * RM_K); };
+  auto Bs = [&](int buf) { return Bs0 + buf * (192 * RM_K); };
   const int64_t t0 = (int64_t)by * BM;
   const int e0 = bx * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lg = lane >> 5;
-  const int64_t n = (int64_t)E * d;
   const int KA = d / 64;
   const int kb = (int)((int64_t)KA * z / KS);
   const int KT = (int)((int64_t)KA * (z + 1) / KS) - kb;
   const bf16_t* a_src[A_LD];
-  const bf16_t* b_src[B_LD];
+  const float* b_src[BG];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
     const int q = tid + NT * i;
@@ -64,16 +63,19 @@ __device__ __forceinline__ void router_mfma_body(
     a_src[i] = x + t * d + (int64_t)kb * 64 + (q % 8) * 8;
   }
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int q = tid + NT * i, r = q / 8;
-    const int e = min(e0 + r % 64, E - 1);
-    b_src[i] = w3 + (r / 64) * n + (int64_t)e * d + (int64_t)kb * 64 + (q % 8) * 8;
+  for (int g = 0; g < BG; ++g) {   // group q: expert row q / 8, weights 8 (q % 8) .. + 7
+    const int q = tid + NT * g;
+    b_src[g] = w_r + (int64_t)min(e0 + q / 8, E - 1) * d + (int64_t)kb * 64 + (q % 8) * 8;
   }
-  u32x4 ra0[A_LD], rb0[B_LD], ra1[A_LD], rb1[B_LD];
+  u32x4 ra0[A_LD], ra1[A_LD];
+  f32x4 rb0[BG][2], rb1[BG][2];
 #define R_LOAD(kt, RA, RB)                                                                   \
   {                                                                                          \
     _Pragma("unroll") for (int i = 0; i < A_LD; ++i) RA[i] = *(const u32x4*)(a_src[i] + (kt) * 64); \
-    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) RB[i] = *(const u32x4*)(b_src[i] + (kt) * 64); \
+    _Pragma("unroll") for (int g = 0; g < BG; ++g) {                                        \
+      RB[g][0] = *(const f32x4*)(b_src[g] + (kt) * 64);                                      \
+      RB[g][1] = *(const f32x4*)(b_src[g] + (kt) * 64 + 4);                                  \
+    }                                                                                        \
   }
 #define R_STORE(buf, RA, RB)                                                                 \
   {                                                                                          \
@@ -81,9 +83,13 @@ __device__ __forceinline__ void router_mfma_body(
       const int q = tid + NT * i;                                                            \
       *(u32x4*)(As(buf) + rswz(q / 8, q % 8)) = RA[i];                                       \
     }                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) {                                      \
-      const int q = tid + NT * i;                                                            \
-      *(u32x4*)(Bs(buf) + rswz(q / 8, q % 8)) = RB[i];                                       \
+    _Pragma("unroll") for (int g = 0; g < BG; ++g) {                                        \
+      const int q = tid + NT * g;                                                            \
+      u32x4 ph, pm, pl;                                                                      \
+      router_split8(RB[g], ph, pm, pl);                                                      \
+      *(u32x4*)(Bs(buf) + rswz(q / 8, q % 8)) = ph;                                          \
+      *(u32x4*)(Bs(buf) + rswz(64 + q / 8, q % 8)) = pm;                                     \
+      *(u32x4*)(Bs(buf) + rswz(128 + q / 8, q % 8)) = pl;                                    \
     }                                                                                        \
   }
   f32x16 acc[3];
