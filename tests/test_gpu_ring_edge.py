@@ -4,7 +4,8 @@ The grouped GEMMs address ring rows with 32-bit byte offsets and the boundary re
 any ring array of 4 GiB or more.  These cases take the largest accepted capacity and a
 head that wraps the copies' segment around the ring's end, so that the rows the kernels
 read and write sit at the top of a ring just under 4 GiB, and compare the forward (bf16
-and MXFP8) and the bf16 backward with the fp64 oracle as the medium-size tests do."""
+and MXFP8, chained and single-launch) and the bf16 backward with the fp64 oracle as the
+medium-size tests do."""
 import numpy as np
 import pytest
 import torch
@@ -89,4 +90,36 @@ def test_mxfp8_forward_at_the_largest_ring():
     print(f"  forward: y max-abs-rel {err:.3e}", flush=True)
     assert err <= TOL["mxfp8"]
     del layer, inp
+    torch.cuda.empty_cache()
+
+
+def test_fused_forward_at_the_largest_ring():
+    """The single-launch forward at the largest bf16 ring: bitwise the chained calls' y and
+    ring rows, and the oracle's y."""
+    cfg = LayerConfig("ring_edge_fused", T=48, d=D, E=8, k=2, f=256, cid=88)
+    C = largest_ring(D * 2)
+    head = C - cfg.n // 2
+    print(f"\n[case] fused ring edge T={cfg.T} d={D} E={cfg.E} k={cfg.k} f={cfg.f} C={C} head={head}",
+          flush=True)
+    inp = make_layer(cfg, DEV)
+    x, w_r = to_oracle(inp.x), to_oracle(inp.w_router)
+    b = None if inp.b_router is None else to_oracle(inp.b_router)
+    args = (inp.x, inp.w_router, inp.b_router, inp.w_gate, inp.w_up, inp.w_down)
+    chained = moe.Layer.create(cfg.T, D, cfg.E, cfg.k, cfg.f, C)
+    y_c = chained.forward(*args, head=head).clone()
+    fused = moe.Layer.create(cfg.T, D, cfg.E, cfg.k, cfg.f, C)
+    y_f = fused.forward_fused(*args, head=head)
+    torch.cuda.synchronize()
+    assert fused.forward_status() == 0
+    assert torch.equal(y_c, y_f)
+    r = oracle.route(x, w_r, b, cfg.k)
+    disp = oracle.dispatch(r.idx, cfg.E, C, head)
+    used = torch.from_numpy(np.nonzero(disp.slot_copy >= 0)[0]).to(DEV)
+    assert int(used.max()) == C - 1
+    for name in ("ring_x", "ring_y"):
+        assert torch.equal(chained.bufs[name][used], fused.bufs[name][used]), name
+    err = rel(to_oracle(y_f), oracle.forward_tokens(range(cfg.T), x, r, LazyWeights(inp.w_gate, inp.w_up, inp.w_down)))
+    print(f"  bitwise equal to the chained calls; y max-abs-rel {err:.3e}", flush=True)
+    assert err <= TOL["bf16"]
+    del chained, fused, inp
     torch.cuda.empty_cache()
