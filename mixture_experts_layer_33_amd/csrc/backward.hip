@@ -67,6 +67,11 @@ __device__ __forceinline__ void stage_flush(const uint8_t* stg, int rows, RowF d
   __syncthreads();
 }
 
+template <typename T>
+__device__ __forceinline__ T bld_meta(const T* q) {   // scalar load of data written by earlier kernels
+  return *(const __attribute__((address_space(4))) T*)q;
+}
+
 // ----------------------------------------------------------------------------- dgrad
 struct DgradArgs {
   const bf16_t* A;          // ring-ordered rows: DOWN dy [C, d] (gathered into ring order); UP dAU [C, 2f]
@@ -405,7 +410,9 @@ __global__ __launch_bounds__(128) void router_wgrad_part_kernel(
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles,
     const int32_t* __restrict__ offset, int64_t head, int64_t C,
     const bf16_t* __restrict__ ring_x, const float* __restrict__ dl_slot, int d,
-    float* __restrict__ part, int32_t* __restrict__ first_tile) {
+    float* __restrict__ part, int32_t* __restrict__ first_tile, const int32_t* __restrict__ x_map,
+    int kdiv) {
+  // x_map set: ring_x is token-major x [T, d] and ring slot s takes row x_map[s] / kdiv
   const int mt = blockIdx.x;
   if (mt >= *ntiles) return;
   const int e = tiles[2 * mt], row0 = tiles[2 * mt + 1];
@@ -431,15 +438,17 @@ __global__ __launch_bounds__(128) void router_wgrad_part_kernel(
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
       const int64_t s = ring_slot(head, seg, row0 + i - u, C);
+      const int64_t xr = x_map ? (int64_t)(bld_meta(x_map + s) / kdiv) : s;
       l[u] = dl_slot[s];
-      w[u] = ((const u32x4*)(ring_x + s * d))[v];
+      w[u] = ((const u32x4*)(ring_x + xr * d))[v];
     }
 #pragma unroll
     for (int u = 0; u < RB; ++u) add(l[u], w[u]);
   }
   for (; i >= 0; --i) {
     const int64_t s = ring_slot(head, seg, row0 + i, C);
-    add(dl_slot[s], ((const u32x4*)(ring_x + s * d))[v]);
+    const int64_t xr = x_map ? (int64_t)(bld_meta(x_map + s) / kdiv) : s;
+    add(dl_slot[s], ((const u32x4*)(ring_x + xr * d))[v]);
   }
   f32x4* dst = (f32x4*)(part + (int64_t)mt * d + v * 8);
   dst[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
@@ -500,10 +509,6 @@ struct WgShape {
   static_assert(WK_ * ARB % (1024 * NW) == 0 && WK_ * BRB % (1024 * NW) == 0, "copies split evenly");
 };
 
-template <typename T>
-__device__ __forceinline__ T bld_meta(const T* q) {   // scalar load of data written by earlier kernels
-  return *(const __attribute__((address_space(4))) T*)q;
-}
 
 
 struct WgradArgs {
@@ -835,7 +840,7 @@ hipError_t launch_backward(const void* dy, const void* x, const float* w_r,
   float* rpart = (float*)(w + L.rpart);
   int32_t* rfirst = (int32_t*)(w + L.rfirst);
   router_wgrad_part_kernel<<<dim3(max_tiles, (d / 8 + 127) / 128), 128, 0, st>>>(
-      tiles, ntiles, expert_offset, head, C, (const bf16_t*)ring_x, dl, d, rpart, rfirst);
+      tiles, ntiles, expert_offset, head, C, (const bf16_t*)ring_x, dl, d, rpart, rfirst, nullptr, 1);
   router_wgrad_sum_kernel<<<dim3(E, (d / 4 + 255) / 256), 256, 0, st>>>(expert_offset, rfirst,
                                                                         rpart, d, dw_r);
   WgradArgs wd{};
@@ -1005,7 +1010,6 @@ __global__ __launch_bounds__(256) void swiglu_bwd_mx_kernel(
   }
 }
 
-// Value of an E4M3 code times 2^X (exact in fp32 for the scales MX produces here).
 // Two values through their E4M3 codes and back, packed as bf16 (a in the low half): each
 // value times 2^-X, clamped to +-448, converted to E4M3 with round to nearest even (the
 // codes of e4m3_encode), the pair decoded by the hardware fp8 -> fp32 conversion (exact:
@@ -1021,7 +1025,8 @@ __device__ __forceinline__ uint32_t e4m3_round_trip2(float a, float b, int Xa, i
   return pack_bf2(ldexpf(v[0], Xa), ldexpf(v[1], Xb));
 }
 // Every expert's ring rows of src [C, cols] (fp32 or bf16) MX round-tripped along the token
-// axis into dst [C, cols] bf16 (may be src itself when src is bf16): blocks of 32 rows
+// axis into dst [C, cols] bf16 (may be src itself when src is bf16; with src_map, bf16 only,
+// src is token-major [T, cols] and ring slot s takes row src_map[s] / kdiv): blocks of 32 rows
 // aligned to the segment's end.  blocks: the tile list of 32-row tiles; tile (e, 32 q) is
 // taken as the q-th block from the end, rows [n_e - 32 (q + 1), n_e - 32 q) of the segment
 // (the first block is the partial one).  One thread per 8 consecutive columns: bf16 rows are
@@ -1035,7 +1040,7 @@ template <typename SRC>
 __global__ __launch_bounds__(256) void token_quant_kernel(
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nblocks,
     const int32_t* __restrict__ offset, int64_t head, int64_t C, int cols,
-    const SRC* src, bf16_t* dst) {
+    const SRC* src, bf16_t* dst, const int32_t* __restrict__ src_map, int kdiv) {
   const int bi = blockIdx.x;
   if (bi >= *nblocks) return;
   const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
@@ -1063,7 +1068,11 @@ __global__ __launch_bounds__(256) void token_quant_kernel(
     u32x4 w[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i)
-      if (lo + i < hi) w[i] = *(const u32x4*)(src + ring_slot(head, seg, lo + i, C) * cols + c);
+      if (lo + i < hi) {
+        const int64_t sl = ring_slot(head, seg, lo + i, C);
+        const int64_t sr = src_map ? (int64_t)(bld_meta(src_map + sl) / kdiv) : sl;
+        w[i] = *(const u32x4*)(src + sr * cols + c);
+      }
     float am[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) am[j] = 0.f;
@@ -1186,10 +1195,8 @@ hipError_t launch_backward_mx(const void* dy, const void* x, const float* w_r,
   if (err == hipSuccess) err = launch_build_tiles(expert_offset, E, 32, blocks, nblocks, st);
   if (err != hipSuccess) return err;
   zero_fill_kernel<<<1, 256, 0, st>>>((uint32_t*)(w + L.zero), 256);
-  gather_to_ring_kernel<<<(unsigned)T, 256, 0, st>>>((const bf16_t*)dy, copy_slot, k, d, rdy);
   gather_mx_kernel<<<(unsigned)T, 256, 0, st>>>((const bf16_t*)dy, copy_slot, k, d, C,
                                                 w + L.rq, w + L.rqs);
-  gather_to_ring_kernel<<<(unsigned)T, 256, 0, st>>>((const bf16_t*)x, copy_slot, k, d, xr);
   // down dgrad: dH_raw = Q_d(dY) Q_d(W_down)
   GemmArgs g{};
   g.A = w + L.rq;
@@ -1226,18 +1233,19 @@ hipError_t launch_backward_mx(const void* dy, const void* x, const float* w_r,
   float* rpart = (float*)(w + L.rpart);
   int32_t* rfirst = (int32_t*)(w + L.rfirst);
   router_wgrad_part_kernel<<<dim3(max_tiles, (d / 8 + 127) / 128), 128, 0, st>>>(
-      tiles, ntiles, expert_offset, head, C, xr, dl, d, rpart, rfirst);
+      tiles, ntiles, expert_offset, head, C, (const bf16_t*)x, dl, d, rpart, rfirst, slot_copy, k);
   router_wgrad_sum_kernel<<<dim3(E, (d / 4 + 255) / 256), 256, 0, st>>>(expert_offset, rfirst,
                                                                         rpart, d, dw_r);
-  // weight gradients on the operands quantised along the token axis
+  // weight gradients on the operands quantised along the token axis; dy and x are read in
+  // place, each ring slot's token row through slot_copy (no copy into ring order first)
   token_quant_kernel<bf16_t><<<dim3(max_blocks, (d + 2047) / 2048), 256, 0, st>>>(
-      blocks, nblocks, expert_offset, head, C, d, rdy, rdy);
+      blocks, nblocks, expert_offset, head, C, d, (const bf16_t*)dy, rdy, slot_copy, k);
   token_quant_kernel<float><<<dim3(max_blocks, (f + 2047) / 2048), 256, 0, st>>>(
-      blocks, nblocks, expert_offset, head, C, f, gh, gh16);
+      blocks, nblocks, expert_offset, head, C, f, gh, gh16, nullptr, 1);
   token_quant_kernel<float><<<dim3(max_blocks, (2 * f + 2047) / 2048), 256, 0, st>>>(
-      blocks, nblocks, expert_offset, head, C, 2 * f, dau, dau16);
+      blocks, nblocks, expert_offset, head, C, 2 * f, dau, dau16, nullptr, 1);
   token_quant_kernel<bf16_t><<<dim3(max_blocks, (d + 2047) / 2048), 256, 0, st>>>(
-      blocks, nblocks, expert_offset, head, C, d, xr, xr);
+      blocks, nblocks, expert_offset, head, C, d, (const bf16_t*)x, xr, slot_copy, k);
   WgradArgs wd{};
   wd.A = rdy;
   wd.B = gh16;
