@@ -298,7 +298,8 @@ int moe_check_shape(const moe_shape* shape);
  *      scales w_down_t_scale [d/128][E*f][4] (both as moe_quantize_mx_t writes them).
  * Out: dx [T,d] bf16; dw_gate, dw_up [E,f,d] and dw_down [E,d,f] bf16; dw_router [E,d] f32.
  * workspace: moe_workspace_bytes(shape with dtype MOE_MXFP8, MOE_OP_BACKWARD) bytes.
- * MOE_MXFP8 only; d and f multiples of 128.
+ * MOE_MXFP8 only; d and f multiples of 128, f at most 13568 (the SwiGLU backward keeps
+ * three f-wide rows of column maxima in LDS); MOE_ERR_SHAPE otherwise.
  */
 int moe_backward_mx(const moe_shape* shape, const void* dy, const void* x,
                     const float* w_router, const int32_t* topk_idx, const float* topk_gate,

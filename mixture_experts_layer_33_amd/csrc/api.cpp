@@ -347,7 +347,8 @@ int moe_backward_mx(const moe_shape* s, const void* dy, const void* x, const flo
     int st = check_shape(s);
     if (st) return st;
     if (s->dtype != MOE_MXFP8) return MOE_ERR_DTYPE;
-    if (s->hidden % 128 || s->ffn % 128) return MOE_ERR_SHAPE;
+    // f: the SwiGLU backward keeps 3 f words of column maxima in a workgroup's 160 KB of LDS
+    if (s->hidden % 128 || s->ffn % 128 || s->ffn > 13568) return MOE_ERR_SHAPE;
     const int64_t T = s->tokens;
     if (missing_tok(dy, T) || missing_tok(x, T) || !w_router || missing_tok(topk_idx, T) ||
         missing_tok(topk_gate, T) || !expert_offset || missing_tok(copy_slot, T) || !slot_copy ||

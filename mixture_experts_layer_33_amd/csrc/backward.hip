@@ -928,70 +928,147 @@ __global__ __launch_bounds__(256) void gather_mx_kernel(const bf16_t* __restrict
   }
 }
 
-// The SwiGLU backward per copy from dH_raw (fp32 [C, f]) and the saved A|U, one row per
-// wavefront: dg = sum_i dH_raw_i h_i (lane partials in column order, then the wavefront's
-// fixed butterfly), dA|dU (fp32 [C, 2f], and MX along f: codes [C, 2f], scales
-// [2f/128][C][4]) and g h (fp32 [C, f]).  Every value that a later step MX-quantises stays
-// in fp32 up to its quantisation: a bf16 rounding in between moves values across E4M3
-// rounding boundaries (skewed workload, hottest expert's dW_up: 6.1e-2 from the oracle
-// with bf16 dH_raw, g h and dA|dU).  Workgroup = one 128-row tile of the tile list.
-__global__ __launch_bounds__(256) void swiglu_bwd_mx_kernel(
-    const int32_t* __restrict__ tiles, const int32_t* __restrict__ ntiles,
+// Two values through their E4M3 codes and back, packed as bf16 (a in the low half): each
+// value times 2^-X, clamped to +-448, converted to E4M3 with round to nearest even (the
+// codes of e4m3_encode), the pair decoded by the hardware fp8 -> fp32 conversion (exact:
+// every E4M3 value is an fp32 value) and scaled back by 2^X, where decoding the codes bit by
+// bit took a few dozen instructions per value.
+typedef float f32x2_rt __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t e4m3_round_trip2(float a, float b, int Xa, int Xb) {
+  const float ca = __builtin_amdgcn_fmed3f(ldexpf(a, -Xa), -448.0f, 448.0f);
+  const float cb = __builtin_amdgcn_fmed3f(ldexpf(b, -Xb), -448.0f, 448.0f);
+  const int codes = __builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
+  const f32x2_rt v = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);
+  return pack_bf2(ldexpf(v[0], Xa), ldexpf(v[1], Xb));
+}
+// Every expert's ring rows of a bf16 src MX round-tripped along the token axis into dst
+// [C, cols] bf16: blocks of 32 rows aligned to the segment's end.  src is ring-ordered
+// [C, cols] (dst may be src itself), or with src_map token-major [T, cols], ring slot s taking
+// row src_map[s] / kdiv.  blocks: the tile list of 32-row tiles; tile (e, 32 q) is taken as
+// the q-th block from the end, rows [n_e - 32 (q + 1), n_e - 32 q) of the segment (the first
+// block is the partial one).  One thread per 8 consecutive columns: the block's rows are
+// read once into registers (16-byte pieces, all in flight together) and written in 16-byte
+// pieces; a thread owns its columns in every row of the block, so the round trip may be in
+// place.  (One thread per column with 2-byte accesses: 735 us per launch at 8,192 skewed
+// tokens; two passes over the rows with a bit-level decode: 352 us; now ~300 us.)  The
+// decoded values are bf16 values (3 significant bits and a power-of-two scale).
+__global__ __launch_bounds__(256) void token_quant_kernel(
+    const int32_t* __restrict__ blocks, const int32_t* __restrict__ nblocks,
+    const int32_t* __restrict__ offset, int64_t head, int64_t C, int cols,
+    const bf16_t* src, bf16_t* dst, const int32_t* __restrict__ src_map, int kdiv) {
+  const int bi = blockIdx.x;
+  if (bi >= *nblocks) return;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (c >= cols) return;
+  // the block's coordinates are uniform over the workgroup: kept in scalar registers
+  const int e = __builtin_amdgcn_readfirstlane(blocks[2 * bi]);
+  const int q = __builtin_amdgcn_readfirstlane(blocks[2 * bi + 1]) / 32;
+  const int32_t seg = __builtin_amdgcn_readfirstlane(offset[e]);
+  const int n = __builtin_amdgcn_readfirstlane(offset[e + 1]) - seg;
+  const int hi = n - 32 * q, lo = max(0, hi - 32);
+  // the block's (at most 32) row pieces are held in registers, read once
+  u32x4 w[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (lo + i < hi) {
+      const int64_t sl = ring_slot(head, seg, lo + i, C);
+      const int64_t sr = src_map ? (int64_t)(bld_meta(src_map + sl) / kdiv) : sl;
+      w[i] = *(const u32x4*)(src + sr * cols + c);
+    }
+  float am[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) am[j] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (lo + i < hi)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        am[2 * k] = fmaxf(am[2 * k], fabsf(lo_bf(w[i][k])));
+        am[2 * k + 1] = fmaxf(am[2 * k + 1], fabsf(hi_bf(w[i][k])));
+      }
+  int X[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) X[j] = mx_block_exp(am[j]);
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (lo + i < hi) {
+      u32x4 out;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        out[k] = e4m3_round_trip2(lo_bf(w[i][k]), hi_bf(w[i][k]), X[2 * k], X[2 * k + 1]);
+      *(u32x4*)(dst + ring_slot(head, seg, lo + i, C) * cols + c) = out;
+    }
+}
+
+// The SwiGLU backward of the MXFP8 backward with both of its quantisations, per 32-row token
+// block (the blocks of token_quant_kernel).  Per copy, from dH_raw (fp32 [C, f]) and the
+// saved A|U: dg = sum_i dH_raw_i h_i (lane partials in column order, then the wavefront's
+// fixed butterfly), dA|dU quantised along f (codes [C, 2f], scales [2f/128][C][4], as the
+// gate/up dgrad reads them), and dA|dU and g·h round-tripped along the token axis into dau16
+// and gh16 (bf16 [C, 2f] and [C, f], the weight gradients' operands).  The block's column
+// maxima are gathered in LDS and the values recomputed from the same inputs (read again,
+// from L2) for the round trip, instead of being stored in fp32 and read back by a separate
+// round-trip pass: skewed MXFP8 backward 8.35 -> 7.74 ms (same GPU, gradients bitwise
+// equal).  Four wavefronts, each the block
+// rows lo + wave + 4 j, one row at a time.
+__global__ __launch_bounds__(256) void swiglu_bwd_mx_tq_kernel(
+    const int32_t* __restrict__ blocks, const int32_t* __restrict__ nblocks,
     const int32_t* __restrict__ offset, int64_t head, int64_t C, int f,
     const float* __restrict__ dhr, const bf16_t* __restrict__ saved_au,
     const int32_t* __restrict__ slot_copy, const float* __restrict__ gate,
-    float* __restrict__ dau, uint8_t* __restrict__ dau_q, uint8_t* __restrict__ dau_s,
-    float* __restrict__ gh, float* __restrict__ dg_out) {
-  const int mt = blockIdx.x;
-  if (mt >= *ntiles) return;
-  const int e = tiles[2 * mt], row0 = tiles[2 * mt + 1];
-  const int32_t seg = offset[e];
-  const int rows = min(BT, offset[e + 1] - seg - row0);
+    uint8_t* __restrict__ dau_q, uint8_t* __restrict__ dau_s, bf16_t* __restrict__ dau16,
+    bf16_t* __restrict__ gh16, float* __restrict__ dg_out) {
+  extern __shared__ uint32_t colmax[];   // [3][f]: |dA|, |dU|, |g h| maxima over the block's rows
+  const int bi = blockIdx.x;
+  if (bi >= *nblocks) return;
+  const int e = __builtin_amdgcn_readfirstlane(blocks[2 * bi]);
+  const int q = __builtin_amdgcn_readfirstlane(blocks[2 * bi + 1]) / 32;
+  const int32_t seg = __builtin_amdgcn_readfirstlane(offset[e]);
+  const int n = __builtin_amdgcn_readfirstlane(offset[e + 1]) - seg;
+  const int hi = n - 32 * q, lo = max(0, hi - 32);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nv = f / 8, iters = (nv + 63) / 64;
-  for (int r = wave; r < rows; r += 4) {
-    const int64_t s = ring_slot(head, seg, row0 + r, C);
+  for (int i = threadIdx.x; i < 3 * f; i += 256) colmax[i] = 0u;
+  __syncthreads();
+  // one row's values at the 8 columns 8 v .. 8 v + 7 (ok: v inside the row)
+  auto row_values = [&](int64_t s, float g, int v, bool ok, float (&da)[8], float (&du)[8],
+                        float (&hh)[8], float& dgp) __attribute__((always_inline)) {
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 wd0 = ok ? ((const f32x4*)(dhr + s * f))[2 * v] : z4;
+    const f32x4 wd1 = ok ? ((const f32x4*)(dhr + s * f))[2 * v + 1] : z4;
+    const u32x4 wa = ok ? ((const u32x4*)(saved_au + s * 2 * f))[v] : u32x4{0, 0, 0, 0};
+    const u32x4 wu = ok ? ((const u32x4*)(saved_au + s * 2 * f + f))[v] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float dh_raw = k < 4 ? wd0[k] : wd1[k - 4];
+      const float a = k & 1 ? hi_bf(wa[k / 2]) : lo_bf(wa[k / 2]);
+      const float u = k & 1 ? hi_bf(wu[k / 2]) : lo_bf(wu[k / 2]);
+      const float sg = sigm(a);
+      const float h = a * sg * u;
+      dgp = fmaf(dh_raw, h, dgp);
+      const float dh = g * dh_raw;
+      da[k] = dh * u * sg * (1.f + a * (1.f - sg));
+      du[k] = dh * a * sg;
+      hh[k] = g * h;
+    }
+  };
+  // pass 1: f-axis codes, dg, the block's column maxima
+  for (int r = lo + wave; r < hi; r += 4) {
+    const int64_t s = ring_slot(head, seg, r, C);
     const float g = gate[slot_copy[s]];
     float dgp = 0.f;
     for (int it = 0; it < iters; ++it) {
       const int v = it * 64 + lane;
       const bool ok = v < nv;
-      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 wd0 = ok ? ((const f32x4*)(dhr + s * f))[2 * v] : z4;
-      const f32x4 wd1 = ok ? ((const f32x4*)(dhr + s * f))[2 * v + 1] : z4;
-      const u32x4 wa = ok ? ((const u32x4*)(saved_au + s * 2 * f))[v] : u32x4{0, 0, 0, 0};
-      const u32x4 wu = ok ? ((const u32x4*)(saved_au + s * 2 * f + f))[v] : u32x4{0, 0, 0, 0};
       float da[8], du[8], hh[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float dh_raw = q < 4 ? wd0[q] : wd1[q - 4];
-        const float a = q & 1 ? hi_bf(wa[q / 2]) : lo_bf(wa[q / 2]);
-        const float u = q & 1 ? hi_bf(wu[q / 2]) : lo_bf(wu[q / 2]);
-        const float sg = sigm(a);
-        const float h = a * sg * u;
-        dgp = fmaf(dh_raw, h, dgp);
-        const float dh = g * dh_raw;
-        da[q] = dh * u * sg * (1.f + a * (1.f - sg));
-        du[q] = dh * a * sg;
-        hh[q] = g * h;
-      }
-      // MX codes of dA and dU along f: the 4 lanes of a 32-element block
+      row_values(s, g, v, ok, da, du, hh, dgp);
       float ama = 0.f, amu = 0.f;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) { ama = fmaxf(ama, fabsf(da[q])); amu = fmaxf(amu, fabsf(du[q])); }
+      for (int k = 0; k < 8; ++k) { ama = fmaxf(ama, fabsf(da[k])); amu = fmaxf(amu, fabsf(du[k])); }
       ama = group_max<4>(ama);
       amu = group_max<4>(amu);
       const int Xa = mx_block_exp(ama), Xu = mx_block_exp(amu);
       if (ok) {
-        f32x4* pa = (f32x4*)(dau + s * 2 * f) + 2 * v;
-        f32x4* pu = (f32x4*)(dau + s * 2 * f + f) + 2 * v;
-        f32x4* ph = (f32x4*)(gh + s * f) + 2 * v;
-        pa[0] = f32x4{da[0], da[1], da[2], da[3]};
-        pa[1] = f32x4{da[4], da[5], da[6], da[7]};
-        pu[0] = f32x4{du[0], du[1], du[2], du[3]};
-        pu[1] = f32x4{du[4], du[5], du[6], du[7]};
-        ph[0] = f32x4{hh[0], hh[1], hh[2], hh[3]};
-        ph[1] = f32x4{hh[4], hh[5], hh[6], hh[7]};
         const uint32_t ca0 = e4m3_encode4(da[0], da[1], da[2], da[3], Xa);
         const uint32_t ca1 = e4m3_encode4(da[4], da[5], da[6], da[7], Xa);
         const uint32_t cu0 = e4m3_encode4(du[0], du[1], du[2], du[3], Xu);
@@ -1003,129 +1080,51 @@ __global__ __launch_bounds__(256) void swiglu_bwd_mx_kernel(
           dau_s[((int64_t)(ba / 4) * C + s) * 4 + (ba & 3)] = (uint8_t)(Xa + 127);
           dau_s[((int64_t)(bu / 4) * C + s) * 4 + (bu & 3)] = (uint8_t)(Xu + 127);
         }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {   // non-negative floats order as their bits
+          atomicMax(&colmax[8 * v + k], __float_as_uint(fabsf(da[k])));
+          atomicMax(&colmax[f + 8 * v + k], __float_as_uint(fabsf(du[k])));
+          atomicMax(&colmax[2 * f + 8 * v + k], __float_as_uint(fabsf(hh[k])));
+        }
       }
     }
     const float dg = wave_sum(dgp);
     if (lane == 0) dg_out[s] = dg;
   }
-}
-
-// Two values through their E4M3 codes and back, packed as bf16 (a in the low half): each
-// value times 2^-X, clamped to +-448, converted to E4M3 with round to nearest even (the
-// codes of e4m3_encode), the pair decoded by the hardware fp8 -> fp32 conversion (exact:
-// every E4M3 value is an fp32 value) and scaled back by 2^X.  Decoding the codes bit by
-// bit took a few dozen instructions per value (token-axis round trip 352 -> 328 us per bf16
-// launch, 268 -> 253 us per fp32 launch at 8,192 skewed tokens; outputs bitwise equal).
-typedef float f32x2_rt __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t e4m3_round_trip2(float a, float b, int Xa, int Xb) {
-  const float ca = __builtin_amdgcn_fmed3f(ldexpf(a, -Xa), -448.0f, 448.0f);
-  const float cb = __builtin_amdgcn_fmed3f(ldexpf(b, -Xb), -448.0f, 448.0f);
-  const int codes = __builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false);
-  const f32x2_rt v = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);
-  return pack_bf2(ldexpf(v[0], Xa), ldexpf(v[1], Xb));
-}
-// Every expert's ring rows of src [C, cols] (fp32 or bf16) MX round-tripped along the token
-// axis into dst [C, cols] bf16 (may be src itself when src is bf16; with src_map, bf16 only,
-// src is token-major [T, cols] and ring slot s takes row src_map[s] / kdiv): blocks of 32 rows
-// aligned to the segment's end.  blocks: the tile list of 32-row tiles; tile (e, 32 q) is
-// taken as the q-th block from the end, rows [n_e - 32 (q + 1), n_e - 32 q) of the segment
-// (the first block is the partial one).  One thread per 8 consecutive columns: bf16 rows are
-// read once into registers (16-byte pieces, all of the block's rows in flight), fp32 rows
-// twice (the column maxima, then the codes; two 16-byte pieces per row), and the results
-// written in 16-byte pieces; a thread owns its columns in every row of the block, so the
-// round trip may be in place.  (One thread per column with 2-byte accesses:
-// 735 us per bf16 launch at 8,192 skewed tokens.)  The decoded values are bf16 values
-// (3 significant bits and a power-of-two scale).
-template <typename SRC>
-__global__ __launch_bounds__(256) void token_quant_kernel(
-    const int32_t* __restrict__ blocks, const int32_t* __restrict__ nblocks,
-    const int32_t* __restrict__ offset, int64_t head, int64_t C, int cols,
-    const SRC* src, bf16_t* dst, const int32_t* __restrict__ src_map, int kdiv) {
-  const int bi = blockIdx.x;
-  if (bi >= *nblocks) return;
-  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
-  if (c >= cols) return;
-  // the block's coordinates are uniform over the workgroup: kept in scalar registers
-  const int e = __builtin_amdgcn_readfirstlane(blocks[2 * bi]);
-  const int q = __builtin_amdgcn_readfirstlane(blocks[2 * bi + 1]) / 32;
-  const int32_t seg = __builtin_amdgcn_readfirstlane(offset[e]);
-  const int n = __builtin_amdgcn_readfirstlane(offset[e + 1]) - seg;
-  const int hi = n - 32 * q, lo = max(0, hi - 32);
-  auto load8 = [&](int64_t slot, float (&v)[8]) __attribute__((always_inline)) {
-    const SRC* p = src + slot * cols + c;
-    if constexpr (sizeof(SRC) == 4) {
-      const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+  __syncthreads();
+  // pass 2: the token-axis round trip of the recomputed values
+  for (int it = 0; it < iters; ++it) {
+    const int v = it * 64 + lane;
+    const bool ok = v < nv;
+    if (!ok) continue;
+    int Xa[8], Xu[8], Xh[8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) { v[k] = a[k]; v[4 + k] = b[k]; }
-    } else {
-      const u32x4 w = *(const u32x4*)p;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) { v[2 * k] = lo_bf(w[k]); v[2 * k + 1] = hi_bf(w[k]); }
+    for (int k = 0; k < 8; ++k) {
+      Xa[k] = mx_block_exp(__uint_as_float(colmax[8 * v + k]));
+      Xu[k] = mx_block_exp(__uint_as_float(colmax[f + 8 * v + k]));
+      Xh[k] = mx_block_exp(__uint_as_float(colmax[2 * f + 8 * v + k]));
     }
-  };
-  if constexpr (sizeof(SRC) == 2) {
-    // bf16: the block's (at most 32) row pieces are held in registers, read once
-    u32x4 w[32];
+    for (int r = lo + wave; r < hi; r += 4) {
+      const int64_t s = ring_slot(head, seg, r, C);
+      const float g = gate[slot_copy[s]];
+      float da[8], du[8], hh[8], dgp = 0.f;
+      row_values(s, g, v, true, da, du, hh, dgp);
+      u32x4 oa, ou, oh;
 #pragma unroll
-    for (int i = 0; i < 32; ++i)
-      if (lo + i < hi) {
-        const int64_t sl = ring_slot(head, seg, lo + i, C);
-        const int64_t sr = src_map ? (int64_t)(bld_meta(src_map + sl) / kdiv) : sl;
-        w[i] = *(const u32x4*)(src + sr * cols + c);
+      for (int k = 0; k < 4; ++k) {
+        oa[k] = e4m3_round_trip2(da[2 * k], da[2 * k + 1], Xa[2 * k], Xa[2 * k + 1]);
+        ou[k] = e4m3_round_trip2(du[2 * k], du[2 * k + 1], Xu[2 * k], Xu[2 * k + 1]);
+        oh[k] = e4m3_round_trip2(hh[2 * k], hh[2 * k + 1], Xh[2 * k], Xh[2 * k + 1]);
       }
-    float am[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) am[j] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i)
-      if (lo + i < hi)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          am[2 * k] = fmaxf(am[2 * k], fabsf(lo_bf(w[i][k])));
-          am[2 * k + 1] = fmaxf(am[2 * k + 1], fabsf(hi_bf(w[i][k])));
-        }
-    int X[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) X[j] = mx_block_exp(am[j]);
-#pragma unroll
-    for (int i = 0; i < 32; ++i)
-      if (lo + i < hi) {
-        u32x4 out;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          out[k] = e4m3_round_trip2(lo_bf(w[i][k]), hi_bf(w[i][k]), X[2 * k], X[2 * k + 1]);
-        *(u32x4*)(dst + ring_slot(head, seg, lo + i, C) * cols + c) = out;
-      }
-    return;
-  }
-  float am[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) am[j] = 0.f;
-#pragma unroll 8
-  for (int r = lo; r < hi; ++r) {
-    float v[8];
-    load8(ring_slot(head, seg, r, C), v);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) am[j] = fmaxf(am[j], fabsf(v[j]));
-  }
-  int X[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) X[j] = mx_block_exp(am[j]);
-#pragma unroll 8
-  for (int r = lo; r < hi; ++r) {
-    const int64_t slot = ring_slot(head, seg, r, C);
-    float v[8];
-    load8(slot, v);
-    u32x4 out;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      out[k] = e4m3_round_trip2(v[2 * k], v[2 * k + 1], X[2 * k], X[2 * k + 1]);
-    *(u32x4*)(dst + slot * cols + c) = out;
+      ((u32x4*)(dau16 + s * 2 * f))[v] = oa;
+      ((u32x4*)(dau16 + s * 2 * f + f))[v] = ou;
+      ((u32x4*)(gh16 + s * f))[v] = oh;
+    }
   }
 }
 
 struct BwdMxLayout {
-  size_t tiles, blocks, rdy, rq, rqs, dhr, dau, dauq, daus, gh, dau16, gh16, dg, dxc, dl, xr,
+  size_t tiles, blocks, rdy, rq, rqs, dhr, dauq, daus, dau16, gh16, dg, dxc, dl, xr,
       rpart, rfirst, zero, total;
 };
 
@@ -1140,10 +1139,8 @@ static BwdMxLayout bwd_mx_layout(int64_t T, int64_t C, int d, int E, int k, int 
   L.rq = o;     o += al((size_t)C * d);
   L.rqs = o;    o += al((size_t)C * (d / 32));
   L.dhr = o;    o += al((size_t)C * f * 4);
-  L.dau = o;    o += al((size_t)C * 2 * f * 4);
   L.dauq = o;   o += al((size_t)C * 2 * f);
   L.daus = o;   o += al((size_t)C * (2 * f / 32));
-  L.gh = o;     o += al((size_t)C * f * 4);
   L.dau16 = o;  o += al((size_t)C * 2 * f * 2);
   L.gh16 = o;   o += al((size_t)C * f * 2);
   L.dg = o;     o += al((size_t)C * 4);
@@ -1170,7 +1167,7 @@ hipError_t launch_backward_mx(const void* dy, const void* x, const float* w_r,
                               const uint8_t* w_down_t_scale, int64_t T, int d, int E, int k,
                               int f, void* dx, void* dw_gate, void* dw_up, void* dw_down,
                               float* dw_r, void* ws, hipStream_t st) {
-  if (d % BT || f % BT) return hipErrorInvalidValue;
+  if (d % BT || f % BT || 3 * f * 4 > 160 * 1024) return hipErrorInvalidValue;
   const BwdMxLayout L = bwd_mx_layout(T, C, d, E, k, f);
   uint8_t* w = (uint8_t*)ws;
   int32_t* ntiles = (int32_t*)(w + L.tiles);
@@ -1179,8 +1176,6 @@ hipError_t launch_backward_mx(const void* dy, const void* x, const float* w_r,
   int32_t* blocks = nblocks + 64;
   bf16_t* rdy = (bf16_t*)(w + L.rdy);
   float* dhr = (float*)(w + L.dhr);
-  float* dau = (float*)(w + L.dau);
-  float* gh = (float*)(w + L.gh);
   bf16_t* dau16 = (bf16_t*)(w + L.dau16);
   bf16_t* gh16 = (bf16_t*)(w + L.gh16);
   float* dg = (float*)(w + L.dg);
@@ -1214,9 +1209,13 @@ hipError_t launch_backward_mx(const void* dy, const void* x, const float* w_r,
   g.a_rows = C;
   g.b_rows = (int64_t)E * f;
   if ((err = launch_mx_plain_gemm128(g, n, E, true, st)) != hipSuccess) return err;
-  swiglu_bwd_mx_kernel<<<(unsigned)max_tiles, 256, 0, st>>>(
-      tiles, ntiles, expert_offset, head, C, f, dhr, (const bf16_t*)saved_au, slot_copy,
-      topk_gate, dau, w + L.dauq, w + L.daus, gh, dg);
+  // the block's column maxima: 3 f words of dynamic LDS
+  if ((err = hipFuncSetAttribute((const void*)swiglu_bwd_mx_tq_kernel,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, 3 * f * 4)) != hipSuccess)
+    return err;
+  swiglu_bwd_mx_tq_kernel<<<(unsigned)max_blocks, 256, (size_t)3 * f * 4, st>>>(
+      blocks, nblocks, expert_offset, head, C, f, dhr, (const bf16_t*)saved_au, slot_copy,
+      topk_gate, w + L.dauq, w + L.daus, dau16, gh16, dg);
   // gate/up dgrad: dX_c = [Q_f(dA) | Q_f(dU)] [Q_f(W_gate); Q_f(W_up)]
   GemmArgs g2 = g;
   g2.A = w + L.dauq;
@@ -1238,13 +1237,9 @@ hipError_t launch_backward_mx(const void* dy, const void* x, const float* w_r,
                                                                         rpart, d, dw_r);
   // weight gradients on the operands quantised along the token axis; dy and x are read in
   // place, each ring slot's token row through slot_copy (no copy into ring order first)
-  token_quant_kernel<bf16_t><<<dim3(max_blocks, (d + 2047) / 2048), 256, 0, st>>>(
+  token_quant_kernel<<<dim3(max_blocks, (d + 2047) / 2048), 256, 0, st>>>(
       blocks, nblocks, expert_offset, head, C, d, (const bf16_t*)dy, rdy, slot_copy, k);
-  token_quant_kernel<float><<<dim3(max_blocks, (f + 2047) / 2048), 256, 0, st>>>(
-      blocks, nblocks, expert_offset, head, C, f, gh, gh16, nullptr, 1);
-  token_quant_kernel<float><<<dim3(max_blocks, (2 * f + 2047) / 2048), 256, 0, st>>>(
-      blocks, nblocks, expert_offset, head, C, 2 * f, dau, dau16, nullptr, 1);
-  token_quant_kernel<bf16_t><<<dim3(max_blocks, (d + 2047) / 2048), 256, 0, st>>>(
+  token_quant_kernel<<<dim3(max_blocks, (d + 2047) / 2048), 256, 0, st>>>(
       blocks, nblocks, expert_offset, head, C, d, (const bf16_t*)x, xr, slot_copy, k);
   WgradArgs wd{};
   wd.A = rdy;

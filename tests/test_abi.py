@@ -119,6 +119,9 @@ def test_ring_head_range_and_dtype_gates():
         sd = moe.make_shape(4, bad["d"], 16, 4, bad["f"], fs=bad["fs"], dtype="bf16")
         assert L.moe_decode(sd, *([FAKE] * 12), FAKE, 1 << 30, None) == _lib.MOE_ERR_SHAPE, bad
     assert L.moe_quantize_mx(FAKE, 4, 48, FAKE, FAKE, None) == _lib.MOE_ERR_SHAPE
+    # the MX backward keeps 3 f words of column maxima in one workgroup's LDS: f <= 13568
+    sm = moe.make_shape(64, 256, 8, 2, 13696, dtype="mxfp8")
+    assert L.moe_backward_mx(sm, *([FAKE] * 8), 0, *([FAKE] * 11), 1 << 40, None) == _lib.MOE_ERR_SHAPE
 
 
 def test_workspace_sizes_of_the_workloads():
