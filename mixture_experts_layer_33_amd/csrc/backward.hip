@@ -43,7 +43,6 @@ struct Staging {
   static constexpr int SRS = W * 2 + 16;    // staged row stride in bytes
   static constexpr int BYTES = BT * SRS;    // 34,816 for 128 columns
 };
-constexpr int STAGE_BYTES = Staging<BT>::BYTES;
 
 template <int W = BT>
 __device__ __forceinline__ void stage_put(uint8_t* stg, int m, int n, float v) {
