@@ -4,8 +4,8 @@ The grouped GEMMs address ring rows with 32-bit byte offsets and the boundary re
 any ring array of 4 GiB or more.  These cases take the largest accepted capacity and a
 head that wraps the copies' segment around the ring's end, so that the rows the kernels
 read and write sit at the top of a ring just under 4 GiB, and compare the forward (bf16
-and MXFP8, chained and single-launch) and the bf16 backward with the fp64 oracle as the
-medium-size tests do."""
+and MXFP8, chained and single-launch) and the backward (bf16 and MXFP8) with the fp64
+oracle as the medium-size tests do."""
 import numpy as np
 import pytest
 import torch
@@ -122,4 +122,39 @@ def test_fused_forward_at_the_largest_ring():
     print(f"  bitwise equal to the chained calls; y max-abs-rel {err:.3e}", flush=True)
     assert err <= TOL["bf16"]
     del chained, fused, inp
+    torch.cuda.empty_cache()
+
+
+def test_mxfp8_backward_at_the_largest_ring():
+    """The MXFP8 backward at the largest MX ring (codes just under 4 GiB; its bf16 ring-order
+    work arrays are twice that): gradients against the oracle's backward_mx."""
+    cfg = LayerConfig("ring_edge_bwd_mx", T=48, d=D, E=8, k=2, f=256, dtype="mxfp8",
+                      backward=True, cid=89)
+    C = largest_ring(D)
+    head = C - cfg.n // 2
+    print(f"\n[case] MXFP8 backward ring edge T={cfg.T} d={D} E={cfg.E} k={cfg.k} f={cfg.f} C={C} "
+          f"head={head}", flush=True)
+    inp = make_layer(cfg, DEV)
+    x, w_r = to_oracle(inp.x), to_oracle(inp.w_router)
+    b = None if inp.b_router is None else to_oracle(inp.b_router)
+    q = [moe.quantize_mx(w) for w in (inp.w_gate, inp.w_up, inp.w_down)]
+    bw = moe.quantize_mx_t_backward_weights(inp.w_gate, inp.w_up, inp.w_down)
+    layer = moe.Layer.create(cfg.T, D, cfg.E, cfg.k, cfg.f, C, dtype="mxfp8")
+    layer.forward(inp.x, inp.w_router, inp.b_router, *[c for c, _ in q],
+                  scales=tuple(s for _, s in q), head=head, save_au=True)
+    dx, dwg, dwu, dwd, dwr = layer.backward_mx(inp.dy, inp.x, inp.w_router, *bw, head=head)
+    torch.cuda.synchronize()
+    r = oracle.route(x, w_r, b, cfg.k)
+    np.testing.assert_array_equal(layer.bufs["topk_idx"].cpu().numpy(), r.idx)
+    disp = oracle.dispatch(r.idx, cfg.E, C, head)
+    assert disp.copy_slot.max() == C - 1
+    W = oracle.weights_from_arrays(*(to_oracle(w) for w in (inp.w_gate, inp.w_up, inp.w_down)))
+    ref = oracle.backward_mx(x, w_r, r, W, to_oracle(inp.dy), disp)
+    errs = {"dx": rel(to_oracle(dx), ref.dx), "dw_gate": rel(to_oracle(dwg), ref.dw_gate),
+            "dw_up": rel(to_oracle(dwu), ref.dw_up), "dw_down": rel(to_oracle(dwd), ref.dw_down),
+            "dw_router": rel(dwr.cpu().numpy(), ref.dw_router)}
+    print("  backward: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for name, v in errs.items():
+        assert v <= TOL["mxfp8"], name
+    del layer, inp
     torch.cuda.empty_cache()
