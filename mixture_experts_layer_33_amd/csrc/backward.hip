@@ -949,7 +949,7 @@ __device__ __forceinline__ uint32_t e4m3_round_trip2(float a, float b, int Xa, i
 // read once into registers (16-byte pieces, all in flight together) and written in 16-byte
 // pieces; a thread owns its columns in every row of the block, so the round trip may be in
 // place.  (One thread per column with 2-byte accesses: 735 us per launch at 8,192 skewed
-// tokens; two passes over the rows with a bit-level decode: 352 us; now ~300 us.)  The
+// tokens; two passes over the rows with a bit-level decode: 352 us; now ~290 us.)  The
 // decoded values are bf16 values (3 significant bits and a power-of-two scale).
 __global__ __launch_bounds__(256) void token_quant_kernel(
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nblocks,
@@ -958,20 +958,27 @@ __global__ __launch_bounds__(256) void token_quant_kernel(
   const int bi = blockIdx.x;
   if (bi >= *nblocks) return;
   const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
-  if (c >= cols) return;
   // the block's coordinates are uniform over the workgroup: kept in scalar registers
   const int e = __builtin_amdgcn_readfirstlane(blocks[2 * bi]);
   const int q = __builtin_amdgcn_readfirstlane(blocks[2 * bi + 1]) / 32;
   const int32_t seg = __builtin_amdgcn_readfirstlane(offset[e]);
   const int n = __builtin_amdgcn_readfirstlane(offset[e + 1]) - seg;
   const int hi = n - 32 * q, lo = max(0, hi - 32);
+  // lane i of each wavefront holds the source row of block row lo + i (one vector load of
+  // the map, read back per row by readlane: 32 scalar loads held too many registers); every
+  // lane takes part, before the lanes past the last column leave
+  int srow;
+  {
+    const int64_t sl = ring_slot(head, seg, min(lo + (int)(threadIdx.x & 31), hi - 1), C);
+    srow = src_map ? src_map[sl] / kdiv : (int)sl;
+  }
+  if (c >= cols) return;
   // the block's (at most 32) row pieces are held in registers, read once
   u32x4 w[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i)
     if (lo + i < hi) {
-      const int64_t sl = ring_slot(head, seg, lo + i, C);
-      const int64_t sr = src_map ? (int64_t)(bld_meta(src_map + sl) / kdiv) : sl;
+      const int64_t sr = __builtin_amdgcn_readlane(srow, i);
       w[i] = *(const u32x4*)(src + sr * cols + c);
     }
   float am[8];
