@@ -1012,11 +1012,11 @@ __global__ __launch_bounds__(256) void token_quant_kernel(
 // fixed butterfly), dA|dU quantised along f (codes [C, 2f], scales [2f/128][C][4], as the
 // gate/up dgrad reads them), and dA|dU and g·h round-tripped along the token axis into dau16
 // and gh16 (bf16 [C, 2f] and [C, f], the weight gradients' operands).  The block's column
-// maxima are gathered in LDS and the values recomputed from the same inputs (read again,
-// from L2) for the round trip, instead of being stored in fp32 and read back by a separate
-// round-trip pass: skewed MXFP8 backward 8.35 -> 7.74 ms (same GPU, gradients bitwise
-// equal).  Four wavefronts, each the block
-// rows lo + wave + 4 j, one row at a time.
+// maxima are gathered in LDS and the values recomputed from the same inputs for the round
+// trip (read again; at 8,192 skewed tokens the second read mostly misses L2: 1.37 GB
+// fetched for 0.67 GB of inputs), instead of being stored in fp32 and read back by a
+// separate round-trip pass: skewed MXFP8 backward 8.35 -> 7.74 ms (same GPU, gradients
+// bitwise equal).  Four wavefronts, each the block rows lo + wave + 4 j, one at a time.
 __global__ __launch_bounds__(256) void swiglu_bwd_mx_tq_kernel(
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nblocks,
     const int32_t* __restrict__ offset, int64_t head, int64_t C, int f,
